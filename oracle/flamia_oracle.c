@@ -1,0 +1,533 @@
+/*
+ * Reference oracle for MXFP8 causal packed-document attention (forward and
+ * backward, quantization included).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; only the test-suite, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code, header, table or constant with the HIP
+ * library.
+ *
+ * Source of the method: "FLAMIA: FLAsh MIcroscaling Attention for Fast and
+ * Causally Safe Training on Blackwell" (arXiv 2611.03344).  Every step below
+ * names the section it follows.  All arithmetic is IEEE binary64; the only
+ * roundings are the ones the method itself prescribes (E4M3 codes, bf16
+ * outputs, the fp32 log-sum-exp that the forward saves).
+ *
+ * Readings taken where the paper is silent (each also listed in the design
+ * notes of the repository):
+ *   - scale exponent "rounded up" = the smallest e with amax <= 448 * 2^e;
+ *     an all-zero block gets e = -127 (its codes are zero for any e);
+ *   - token blocks are anchored at the document start;
+ *   - key tiles of B_c keys are visited in ascending order, anchored at the
+ *     document start; the running maximum is replaced when the tile maximum
+ *     exceeds it by more than tau (or on the first tile);
+ *   - the forward row sum accumulates the unquantized p (FlashAttention
+ *     convention); rowsum = 1 accumulates the represented value(P-hat)/2^c;
+ *   - the saved row statistic is lse2 = m + log2(l) in fp32, and the backward
+ *     rebuilds P = 2^(x - lse2) with the same scores x;
+ *   - dS is quantized before the 1/sqrt(d) factor, which multiplies dQ and dK
+ *     after accumulation;
+ *   - D_i = dO~_i . O_i uses the bf16 output that the forward returns;
+ *   - GQA: query head h reads key/value head h / (Hq/Hkv); dK and dV sum over
+ *     the heads of the group before rounding.
+ *
+ * Parity: every exported function is pinned by CPU tests against definitions
+ * that do not go through this file (a library FP8 codec, brute-force nearest
+ * search, exact attention written as dense matrix algebra, finite differences,
+ * and the causal and document-isolation invariants).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_ERR_ARG 1
+#define ORC_ERR_BOUND 2
+#define ORC_ERR_NOMEM 3
+
+enum { QUANT_CEIL = 0, QUANT_FLOOR = 1, QUANT_NONE = 2 };
+
+typedef struct {
+    int32_t ttot, ndocs, hq, hkv, d;
+    int32_t c_log2;       /* P-hat is E4M3(2^c p) (Appendix B.1) */
+    int32_t tau;          /* conditional rescale threshold (Appendix B.1) */
+    int32_t key_tile;     /* B_c (Section 3.2, Figure 1: 128) */
+    int32_t quant;        /* QUANT_CEIL / QUANT_FLOOR / QUANT_NONE */
+    int32_t rowsum;       /* 0: unquantized p, 1: represented value(P-hat)/2^c */
+    double softmax_scale; /* <= 0 selects 1/sqrt(d) */
+    int32_t unsafe_bound; /* 1 skips the c + tau <= 8 check (negative tests only) */
+} orc_params;
+
+/* ---------------------------------------------------------------------------
+ * Scalar formats.
+ * E4M3 (OCP "E4M3FN", the 8-bit code of Section 2, "Microscaling
+ * floating-point formats"): 1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 holds subnormals m * 2^-9; S.1111.111 is NaN, so the
+ * largest finite value is 1.75 * 2^8 = 448 (Section 3.2).
+ * ------------------------------------------------------------------------- */
+double orc_e4m3_value(uint8_t code)
+{
+    int s = code >> 7, ef = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (ef == 15 && m == 7) return NAN;
+    if (ef == 0) v = ldexp((double)m, -9);
+    else v = ldexp((double)(8 + m), ef - 10);
+    return s ? -v : v;
+}
+
+/* Round-to-nearest-even into E4M3 (Appendix A.5: every element rounds to
+ * nearest).  Magnitudes that round above 448 saturate to 448: that is the
+ * clamping of the reference microscaling conversion that Section 3.2
+ * describes; the causally safe exponent never lets it happen. */
+uint8_t orc_e4m3_encode(double y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    double a = fabs(y);
+    int ex, ef;
+    double f, n;
+    if (isnan(y)) return 0x7F;
+    if (a < 0x1p-6) {                 /* subnormal range: quantum 2^-9 */
+        n = nearbyint(a * 512.0);     /* 0..8; 8 is the smallest normal */
+        return (uint8_t)(sign | (uint8_t)n);
+    }
+    f = frexp(a, &ex);                /* a = f 2^ex, f in [0.5, 1) */
+    n = nearbyint(f * 16.0);          /* mantissa with the hidden bit, 8..16 */
+    ef = ex - 1;                      /* unbiased exponent of a */
+    if (n == 16.0) { n = 8.0; ef += 1; }
+    if (ef > 8 || (ef == 8 && n > 14.0)) return (uint8_t)(sign | 0x7E);
+    return (uint8_t)(sign | ((ef + 7) << 3) | ((int)n - 8));
+}
+
+/* Shared block exponent for a block whose largest magnitude is amax.
+ * rule 0 (Section 3.2, "round each scale's exponent up"): the smallest e with
+ *   amax <= 448 * 2^e, so the scaled maximum never exceeds the largest code.
+ * rule 1 (the reference conversion quoted in Section 3.2):
+ *   floor(log2 amax) - e_max with e_max = 8; the scaled maximum may exceed 448.
+ * The result is clamped to the UE8M0 range [-127, 127]; amax = 0 gives -127. */
+int orc_scale_exp(double amax, int rule)
+{
+    int ex, e;
+    double f;
+    if (!(amax > 0.0)) return -127;
+    f = frexp(amax, &ex);             /* amax = (2f) 2^(ex-1), 2f in [1, 2) */
+    e = (ex - 1) - 8;
+    if (rule == 0 && 2.0 * f > 1.75) e += 1;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+double orc_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* bf16 round-to-nearest-even directly from binary64 (one rounding). */
+uint16_t orc_double_to_bf16(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x), r;
+    int ex;
+    float fl;
+    uint32_t u;
+    if (isnan(x)) return 0x7FC0;
+    if (a == 0.0) return sign;
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80);
+    if (a >= 0x1p-126) {
+        double f = frexp(a, &ex);             /* a = f 2^ex */
+        r = ldexp(nearbyint(ldexp(f, 8)), ex - 8);
+    } else {
+        r = ldexp(nearbyint(ldexp(a, 133)), -133);
+    }
+    if (r >= 0x1p128) return (uint16_t)(sign | 0x7F80);
+    fl = (float)r;                            /* exact */
+    memcpy(&u, &fl, 4);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* ---------------------------------------------------------------------------
+ * Token-block quantizer (Section 3.1 "token-block scaling"; Section 3.6.1,
+ * blocks and statistics kept inside document boundaries).
+ * One document slice of L tokens, d channels, rows `rstride` elements apart.
+ * Blocks are [32b, min(32b+32, L)) from the document start; one exponent per
+ * block over all d channels; every token of the block stores it.
+ * deq (L x d, dense) receives value(code) * 2^e, or x itself when quant is
+ * QUANT_NONE.  codes/scales may be NULL.
+ * ------------------------------------------------------------------------- */
+static void tbq_slice(const uint16_t *x, long rstride, int L, int d, int quant,
+                      double *deq, uint8_t *codes, long cstride, uint8_t *scales)
+{
+    for (int b0 = 0; b0 < L; b0 += 32) {
+        int b1 = b0 + 32 < L ? b0 + 32 : L;
+        double amax = 0.0;
+        int e = 0;
+        for (int t = b0; t < b1; ++t)
+            for (int k = 0; k < d; ++k) {
+                double v = fabs(orc_bf16_to_double(x[(long)t * rstride + k]));
+                if (v > amax) amax = v;
+            }
+        if (quant != QUANT_NONE) e = orc_scale_exp(amax, quant == QUANT_FLOOR ? 1 : 0);
+        for (int t = b0; t < b1; ++t) {
+            if (scales) scales[t] = (uint8_t)(e + 127);
+            for (int k = 0; k < d; ++k) {
+                double v = orc_bf16_to_double(x[(long)t * rstride + k]);
+                if (quant == QUANT_NONE) {
+                    deq[(long)t * d + k] = v;
+                } else {
+                    uint8_t c = orc_e4m3_encode(ldexp(v, -e));
+                    if (codes) codes[(long)t * cstride + k] = c;
+                    deq[(long)t * d + k] = ldexp(orc_e4m3_value(c), e);
+                }
+            }
+        }
+    }
+}
+
+static int check_cu(const orc_params *p, const int32_t *cu)
+{
+    if (!cu || p->ndocs < 0 || cu[0] != 0 || cu[p->ndocs] != p->ttot) return 0;
+    for (int i = 0; i < p->ndocs; ++i)
+        if (cu[i + 1] < cu[i]) return 0;
+    return 1;
+}
+
+/* codes [ttot][heads][d], scales [heads][ttot] (UE8M0 byte = e + 127). */
+int orc_quantize(const orc_params *p, int heads, const uint16_t *x, const int32_t *cu,
+                 uint8_t *codes, uint8_t *scales)
+{
+    int d = p->d, nd = p->ndocs;
+    long nunits = (long)nd * heads;
+    int err = ORC_OK;
+    if (!x || !codes || !scales || heads <= 0 || d <= 0 || !check_cu(p, cu)) return ORC_ERR_ARG;
+    if (p->quant == QUANT_NONE) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < nunits; ++u) {
+        int doc = (int)(u / heads), h = (int)(u % heads);
+        int base = cu[doc], L = cu[doc + 1] - cu[doc];
+        double *deq;
+        if (L == 0) continue;
+        deq = (double *)malloc(sizeof(double) * (size_t)L * d);
+        if (!deq) { err = ORC_ERR_NOMEM; continue; }
+        tbq_slice(x + ((long)base * heads + h) * d, (long)heads * d, L, d, p->quant, deq,
+                  codes + ((long)base * heads + h) * d, (long)heads * d,
+                  scales + (long)h * p->ttot + base);
+        free(deq);
+    }
+    return err;
+}
+
+/* ---------------------------------------------------------------------------
+ * Attention.  One unit = one document x one key/value head (all G query heads
+ * of the group), so every statistic stays inside the document.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    double *o64; uint16_t *o16; float *lse2; double *dvec;
+    double *dq64, *dk64, *dv64; uint16_t *dq16, *dk16, *dv16;
+    int64_t *stats;   /* [0] P-hat entries that saturated, [1] dS entries
+                         (causal, in-document), [2] nonzero dS quantized to 0 */
+} orc_out;
+
+static double dotd(const double *a, const double *b, int d)
+{
+    double s = 0.0;
+    for (int k = 0; k < d; ++k) s += a[k] * b[k];
+    return s;
+}
+
+/* Forward for one query row (Section 2 equations for S, P, O; Appendix B.1
+ * for the fixed 2^c factor and the conditional running maximum). */
+static void fwd_row(const orc_params *p, int i, const double *qi, const double *Kt,
+                    const double *Vt, double c1, double *acc, double *x,
+                    double *o_out, double *lse_out, int64_t *sat)
+{
+    int d = p->d, B = p->key_tile, quant = p->quant;
+    double m = -INFINITY, l = 0.0;
+    double two_c = ldexp(1.0, p->c_log2);
+    for (int k = 0; k < d; ++k) acc[k] = 0.0;
+    for (int j0 = 0; j0 <= i; j0 += B) {
+        int j1 = j0 + B <= i + 1 ? j0 + B : i + 1;
+        double mu = -INFINITY;
+        for (int j = j0; j < j1; ++j) {
+            x[j - j0] = dotd(qi, Kt + (long)j * d, d) * c1;
+            if (x[j - j0] > mu) mu = x[j - j0];
+        }
+        if (m == -INFINITY || mu - m > (double)p->tau) {
+            double alpha = (m == -INFINITY) ? 0.0 : exp2(m - mu);
+            l *= alpha;
+            for (int k = 0; k < d; ++k) acc[k] *= alpha;
+            m = mu;
+        }
+        for (int j = j0; j < j1; ++j) {
+            double pj = exp2(x[j - j0] - m), w;
+            const double *vj = Vt + (long)j * d;
+            if (quant == QUANT_NONE) {
+                w = pj;
+                l += pj;
+            } else {
+                double y = pj * two_c;
+                uint8_t code;
+                if (y > 448.0) (*sat)++;
+                code = orc_e4m3_encode(y);
+                w = orc_e4m3_value(code);
+                l += (p->rowsum == 1) ? w / two_c : pj;
+            }
+            for (int k = 0; k < d; ++k) acc[k] += w * vj[k];
+        }
+    }
+    {
+        double den = (quant == QUANT_NONE) ? l : l * two_c;
+        for (int k = 0; k < d; ++k) o_out[k] = acc[k] / den;
+        *lse_out = m + log2(l);
+    }
+}
+
+static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
+                     const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     const uint16_t *dout, const orc_out *out, int *err)
+{
+    const int d = p->d, hq = p->hq, hkv = p->hkv, G = hq / hkv, quant = p->quant;
+    const int base = cu[doc], L = cu[doc + 1] - cu[doc];
+    const double s = p->softmax_scale > 0 ? p->softmax_scale : 1.0 / sqrt((double)d);
+    const double c1 = s * (1.0 / log(2.0));     /* s * log2(e) */
+    const int need_bwd = dout != NULL;
+    double *Kt = 0, *Vt = 0, *Qt = 0, *dOt = 0, *O = 0, *lse = 0, *Dv = 0;
+    double *acc = 0, *xbuf = 0, *dS = 0, *dQa = 0, *dKa = 0, *dVa = 0;
+    float *lsef = 0;
+    int64_t sat = 0, nds = 0, nds0 = 0;
+    size_t Ld = (size_t)L * d;
+
+    if (L == 0) return;
+    Kt = malloc(sizeof(double) * Ld);
+    Vt = malloc(sizeof(double) * Ld);
+    Qt = malloc(sizeof(double) * Ld);
+    O = malloc(sizeof(double) * Ld);
+    lse = malloc(sizeof(double) * L);
+    lsef = malloc(sizeof(float) * L);
+    acc = malloc(sizeof(double) * d);
+    xbuf = malloc(sizeof(double) * (p->key_tile > 32 ? p->key_tile : 32));
+    if (need_bwd) {
+        dOt = malloc(sizeof(double) * Ld);
+        Dv = malloc(sizeof(double) * L);
+        dS = malloc(sizeof(double) * 32 * (size_t)L);
+        dQa = malloc(sizeof(double) * Ld);
+        dKa = calloc(Ld, sizeof(double));
+        dVa = calloc(Ld, sizeof(double));
+    }
+    if (!Kt || !Vt || !Qt || !O || !lse || !lsef || !acc || !xbuf ||
+        (need_bwd && (!dOt || !Dv || !dS || !dQa || !dKa || !dVa))) {
+        *err = ORC_ERR_NOMEM;
+        goto done;
+    }
+    /* K~ and V~: token blocks of this document and this key/value head. */
+    tbq_slice(k + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, Kt, 0, 0, 0);
+    tbq_slice(v + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, Vt, 0, 0, 0);
+
+    for (int hh = 0; hh < G; ++hh) {
+        const int h = g * G + hh;
+        tbq_slice(q + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, Qt, 0, 0, 0);
+        /* ---- forward, row by row ---- */
+        for (int i = 0; i < L; ++i) {
+            fwd_row(p, i, Qt + (long)i * d, Kt, Vt, c1, acc, xbuf, O + (long)i * d, &lse[i], &sat);
+            lsef[i] = (float)lse[i];
+            /* MX modes return a bf16 O and the backward reads it back
+             * (Section 3.4: returned outputs are BF16); the exact mode keeps
+             * binary64 throughout. */
+            for (int c = 0; c < d; ++c) {
+                long gi = ((long)(base + i) * hq + h) * d + c;
+                uint16_t b = orc_double_to_bf16(O[(long)i * d + c]);
+                if (out->o64) out->o64[gi] = O[(long)i * d + c];
+                if (out->o16) out->o16[gi] = b;
+                if (quant != QUANT_NONE) O[(long)i * d + c] = orc_bf16_to_double(b);
+            }
+            if (out->lse2) out->lse2[(long)h * p->ttot + base + i] = lsef[i];
+        }
+        if (!need_bwd) continue;
+
+        /* ---- backward (Section 2 equations; Section 3.3 consistency) ---- */
+        tbq_slice(dout + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, dOt, 0, 0, 0);
+        for (int i = 0; i < L; ++i) {
+            Dv[i] = dotd(dOt + (long)i * d, O + (long)i * d, d);
+            if (out->dvec) out->dvec[(long)h * p->ttot + base + i] = Dv[i];
+        }
+        memset(dQa, 0, sizeof(double) * Ld);
+        for (int i0 = 0; i0 < L; i0 += 32) {
+            int i1 = i0 + 32 < L ? i0 + 32 : L;
+            /* dS for the 32 query rows of this block, every visible key. */
+            for (int i = i0; i < i1; ++i) {
+                double li = (quant == QUANT_NONE) ? lse[i] : (double)lsef[i];
+                const double *qi = Qt + (long)i * d, *doi = dOt + (long)i * d;
+                double *row = dS + (size_t)(i - i0) * L;
+                for (int j = 0; j < L; ++j) row[j] = 0.0;
+                for (int j = 0; j <= i; ++j) {
+                    double xij = dotd(qi, Kt + (long)j * d, d) * c1;
+                    double P = exp2(xij - li), wb;
+                    double dP = dotd(doi, Vt + (long)j * d, d);
+                    if (quant == QUANT_NONE) {
+                        wb = P;
+                    } else {
+                        /* Appendix B.1: the dV operand is E4M3(2^8 P), no scale. */
+                        wb = ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(P, 8))), -8);
+                    }
+                    for (int c = 0; c < d; ++c) dVa[(long)j * d + c] += wb * doi[c];
+                    row[j] = P * (dP - Dv[i]);
+                }
+            }
+            /* dS~: one exponent per 32x32 document-local block (Section 3.3),
+             * then dQ += dS~ K~ and dK += dS~^T Q~. */
+            for (int j0 = 0; j0 <= i1 - 1; j0 += 32) {
+                int j1 = j0 + 32 < L ? j0 + 32 : L;
+                int e = 0;
+                if (quant != QUANT_NONE) {
+                    double amax = 0.0;
+                    for (int i = i0; i < i1; ++i)
+                        for (int j = j0; j < j1 && j <= i; ++j) {
+                            double a = fabs(dS[(size_t)(i - i0) * L + j]);
+                            if (a > amax) amax = a;
+                        }
+                    e = orc_scale_exp(amax, quant == QUANT_FLOOR ? 1 : 0);
+                }
+                for (int i = i0; i < i1; ++i)
+                    for (int j = j0; j < j1 && j <= i; ++j) {
+                        double ds = dS[(size_t)(i - i0) * L + j], dq;
+                        if (quant == QUANT_NONE) {
+                            dq = ds;
+                        } else {
+                            dq = ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(ds, -e))), e);
+                            nds++;
+                            if (ds != 0.0 && dq == 0.0) nds0++;
+                        }
+                        if (dq == 0.0) continue;
+                        for (int c = 0; c < d; ++c) {
+                            dQa[(long)i * d + c] += dq * Kt[(long)j * d + c];
+                            dKa[(long)j * d + c] += dq * Qt[(long)i * d + c];
+                        }
+                    }
+            }
+        }
+        for (int i = 0; i < L; ++i)
+            for (int c = 0; c < d; ++c) {
+                long gi = ((long)(base + i) * hq + h) * d + c;
+                double val = s * dQa[(long)i * d + c];
+                if (out->dq64) out->dq64[gi] = val;
+                if (out->dq16) out->dq16[gi] = orc_double_to_bf16(val);
+            }
+    }
+    if (need_bwd) {
+        for (int j = 0; j < L; ++j)
+            for (int c = 0; c < d; ++c) {
+                long gj = ((long)(base + j) * hkv + g) * d + c;
+                double kv = s * dKa[(long)j * d + c], vv = dVa[(long)j * d + c];
+                if (out->dk64) out->dk64[gj] = kv;
+                if (out->dv64) out->dv64[gj] = vv;
+                if (out->dk16) out->dk16[gj] = orc_double_to_bf16(kv);
+                if (out->dv16) out->dv16[gj] = orc_double_to_bf16(vv);
+            }
+    }
+    if (out->stats) {
+#pragma omp atomic
+        out->stats[0] += sat;
+#pragma omp atomic
+        out->stats[1] += nds;
+#pragma omp atomic
+        out->stats[2] += nds0;
+    }
+done:
+    free(Kt); free(Vt); free(Qt); free(O); free(lse); free(lsef); free(acc); free(xbuf);
+    free(dOt); free(Dv); free(dS); free(dQa); free(dKa); free(dVa);
+}
+
+typedef struct { long len; int doc, g; } unit_t;
+
+static int cmp_unit(const void *a, const void *b)
+{
+    const unit_t *x = a, *y = b;
+    if (x->len != y->len) return x->len < y->len ? 1 : -1;
+    if (x->doc != y->doc) return x->doc - y->doc;
+    return x->g - y->g;
+}
+
+/*
+ * Forward (and, when dout != NULL, backward) for the units selected by
+ * kv_mask[g] and doc_mask[doc] (NULL = all).  Layouts: q/dout/o/dq
+ * [ttot][hq][d]; k/v/dk/dv [ttot][hkv][d]; lse2/dvec [hq][ttot].  Any output
+ * pointer may be NULL.  Outputs of units that are not selected are left as
+ * the caller initialised them.
+ */
+int orc_attention(const orc_params *p, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  const uint16_t *dout, const int32_t *cu, const uint8_t *kv_mask,
+                  const uint8_t *doc_mask,
+                  double *o64, uint16_t *o16, float *lse2, double *dvec,
+                  double *dq64, double *dk64, double *dv64,
+                  uint16_t *dq16, uint16_t *dk16, uint16_t *dv16, int64_t *stats)
+{
+    orc_out out = {o64, o16, lse2, dvec, dq64, dk64, dv64, dq16, dk16, dv16, stats};
+    unit_t *units;
+    long nu = 0;
+    int err = ORC_OK;
+    if (!p || !q || !k || !v || p->d <= 0 || p->hq <= 0 || p->hkv <= 0 || p->hq % p->hkv)
+        return ORC_ERR_ARG;
+    if (p->key_tile <= 0 || p->quant < 0 || p->quant > 2 || !check_cu(p, cu)) return ORC_ERR_ARG;
+    /* Section 3.4 / Appendix B.1: c + tau <= log2(448) keeps 2^c p below the
+     * largest E4M3 value; anything else is rejected. */
+    if (p->c_log2 < 0 || p->tau < 0) return ORC_ERR_ARG;
+    if (p->quant != QUANT_NONE && p->c_log2 + p->tau > 8 && !p->unsafe_bound)
+        return ORC_ERR_BOUND;
+    if (stats) stats[0] = stats[1] = stats[2] = 0;
+    units = malloc(sizeof(unit_t) * ((size_t)p->ndocs * p->hkv + 1));
+    if (!units) return ORC_ERR_NOMEM;
+    for (int doc = 0; doc < p->ndocs; ++doc) {
+        if (doc_mask && !doc_mask[doc]) continue;
+        for (int g = 0; g < p->hkv; ++g) {
+            if (kv_mask && !kv_mask[g]) continue;
+            units[nu].len = cu[doc + 1] - cu[doc];
+            units[nu].doc = doc;
+            units[nu].g = g;
+            nu++;
+        }
+    }
+    qsort(units, (size_t)nu, sizeof(unit_t), cmp_unit);   /* longest first */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < nu; ++u) {
+        int e = ORC_OK;
+        unit_run(p, units[u].doc, units[u].g, cu, q, k, v, dout, &out, &e);
+        if (e) err = e;
+    }
+    free(units);
+    return err;
+}
+
+void orc_e4m3_encode_array(const double *y, long n, uint8_t *codes)
+{
+    for (long i = 0; i < n; ++i) codes[i] = orc_e4m3_encode(y[i]);
+}
+
+void orc_e4m3_value_array(const uint8_t *codes, long n, double *v)
+{
+    for (long i = 0; i < n; ++i) v[i] = orc_e4m3_value(codes[i]);
+}
+
+void orc_scale_exp_array(const double *a, long n, int rule, int32_t *e)
+{
+    for (long i = 0; i < n; ++i) e[i] = orc_scale_exp(a[i], rule);
+}
+
+void orc_double_to_bf16_array(const double *x, long n, uint16_t *b)
+{
+    for (long i = 0; i < n; ++i) b[i] = orc_double_to_bf16(x[i]);
+}
+
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
