@@ -1,0 +1,194 @@
+"""Benchmark of the MXFP8 causal packed-document training call on one MI355X.
+
+One step = flamia_fwd (quantize Q/K/V, work list, forward kernel) followed by
+flamia_bwd (quantize dO with D and the dQ clear, work list, backward kernel,
+dQ finalize) on one seeded synthetic batch already resident in HBM.
+
+Prints ONE JSON line:
+  value     whole-call throughput, FLOP = 7 * Hq * d * sum(L^2) (forward 2
+            products x 2d x L^2/2 causal pairs, backward 2.5x the forward)
+  roofline  the dominant kernel's algorithmic FLOP per launch divided by its
+            average duration, measured with HIP events recorded by the library
+            on the launch stream around each internal launch
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd causal attention TFLOP/s incl. quant (MXFP8, packed docs), % of roofline"
+MXFP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8/MXFP8 MFMA peak (AMD specification)
+FWD_PHASES = ["quantize_q", "quantize_k", "quantize_v", "worklist_fwd", "fwd_kernel"]
+BWD_PHASES = ["quantize_do", "worklist_bwd", "bwd_kernel", "dq_finalize"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """hipEvent plumbing through the HIP runtime (no compute)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.lib.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        self.lib.hipEventSynchronize(ctypes.c_void_p(b))
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+
+def cpu_baseline(inst, hkv):
+    """The oracle as it stands, on key/value head 0 and its query heads (all
+    documents), scaled to TFLOP/s of that sample."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    km = np.zeros(hkv, np.uint8)
+    km[0] = 1
+    t0 = time.perf_counter()
+    oracle.attention(inst["q"], inst["k"], inst["v"], inst["do"], inst["cu_seqlens"], kv_mask=km,
+                     want_f64=False)
+    dt = time.perf_counter() - t0
+    hq, d = inst["q"].shape[1], inst["q"].shape[2]
+    G = hq // hkv
+    flop = 7.0 * G * d * inst["sum_L2"]
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"key/value head 0 of {hkv} ({G} of {hq} query heads), all {len(inst['lengths'])} "
+                      f"documents, forward + backward incl. quantization; {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa-4x8k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build runs the attention call on a single "
+              f"MI355X); --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from precision_causal_attention_amd import flamia as F
+    from precision_causal_attention_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    log(f"[bench] generating {wl.name} seed {args.seed}")
+    inst = W.generate(wl, args.seed)
+    T, hq, d = inst["q"].shape
+    hkv = inst["k"].shape[1]
+    ndocs = len(inst["lengths"])
+    dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, do = (dev(inst[n]) for n in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(inst["cu_seqlens"]).cuda()
+    call = F.TrainingCall(T, hq, hkv, d, ndocs_cap=ndocs)
+    hip = Hip()
+    nf, nb = len(FWD_PHASES) + 1, len(BWD_PHASES) + 1
+    ev = hip.events((nf + nb) * args.steps)
+    stream = torch.cuda.current_stream()
+
+    def step(i=None):
+        if i is None:
+            call.opts.phase_events, call.opts.n_events = None, 0
+            call.forward(q, k, v, cu, stream)
+            call.backward(do, cu, stream)
+            return
+        base = i * (nf + nb)
+        fe = (ctypes.c_void_p * nf)(*ev[base:base + nf])
+        be = (ctypes.c_void_p * nb)(*ev[base + nf:base + nf + nb])
+        call.opts.phase_events, call.opts.n_events = ctypes.cast(fe, ctypes.POINTER(ctypes.c_void_p)), nf
+        call.forward(q, k, v, cu, stream)
+        call.opts.phase_events, call.opts.n_events = ctypes.cast(be, ctypes.POINTER(ctypes.c_void_p)), nb
+        call.backward(do, cu, stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+
+    phases = {p: 0.0 for p in FWD_PHASES + BWD_PHASES}
+    for i in range(args.steps):
+        base = i * (nf + nb)
+        for j, p in enumerate(FWD_PHASES):
+            phases[p] += hip.elapsed_ms(ev[base + j], ev[base + j + 1]) / args.steps
+        for j, p in enumerate(BWD_PHASES):
+            phases[p] += hip.elapsed_ms(ev[base + nf + j], ev[base + nf + j + 1]) / args.steps
+
+    sum_l2 = inst["sum_L2"]
+    flop = 7.0 * hq * d * sum_l2
+    tflops = flop / (ms_step * 1e-3) / 1e12
+    kflop = {"fwd_kernel": 2.0 * hq * d * sum_l2, "bwd_kernel": 5.0 * hq * d * sum_l2}
+    dom = max(kflop, key=lambda n: phases[n])
+    achieved = kflop[dom] / (phases[dom] * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "frac_of_mxfp8_peak": round(tflops / MXFP8_PEAK_TFLOPS, 4),
+        "config": {"workload": wl.name, "rows": wl.rows, "row_len": wl.row_len, "tokens": T, "hq": hq,
+                   "hkv": hkv, "d": d, "docs": ndocs, "sum_L2": sum_l2, "seed": args.seed,
+                   "doc_law": wl.docs, "parallelism": "single-gpu"},
+        "phases_ms": {p: round(t, 4) for p, t in phases.items()},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MXFP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MXFP8_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle sample)")
+        result["cpu_baseline"] = cpu_baseline(inst, hkv)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * flamia.h -- C ABI of an MI355X (gfx950) library for microscaled (MXFP8)
+ * causal flash attention over packed variable-length documents: the
+ * training call (forward and backward) with the operand quantization fused in.
+ *
+ * Method: "FLAMIA: FLAsh MIcroscaling Attention for Fast and Causally Safe
+ * Training on Blackwell".  Section numbers below refer to that paper.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are packed (Section 3.6.1): T = dims->ttot tokens, documents
+ *    contiguous, document d occupies tokens [cu_seqlens[d], cu_seqlens[d+1]).
+ *    cu_seqlens is an int32 device array of ndocs+1 entries, non-decreasing,
+ *    cu_seqlens[0] = 0, cu_seqlens[ndocs] = ttot.  Empty documents are allowed
+ *    (pad a list with trailing empty documents to reuse one captured graph for
+ *    different document counts).  The library reads it only on the device and
+ *    never synchronizes with the host.
+ *  - Activations are bf16 (passed as uint16_t bit patterns), layout
+ *    [T][heads][d], row-major, d contiguous.  Q, dO, O and dQ have hq heads;
+ *    K, V, dK and dV have hkv heads; query head h reads key/value head
+ *    h / (hq / hkv) (grouped-query attention).
+ *  - Quantized operands (flamia_mx_t): E4M3 codes [T][heads][d] (uint8) and a
+ *    dense per-token UE8M0 scale table [heads][T] (uint8, value 2^(byte-127)).
+ *    Every token of a 32-token block, counted from its document's start,
+ *    stores the block's exponent (Section 3.1 token-block scaling, Section
+ *    3.6.1 dense per-token metadata).  The exponent is the smallest e with
+ *    max|x| <= 448 * 2^e (Section 3.2), so no code saturates.
+ *  - lse2 is the saved row statistic, [hq][T] fp32, base 2, in the domain of
+ *    the scaled scores x = (q.k) * softmax_scale * log2(e):
+ *    lse2_i = log2(sum_j 2^(x_ij)).  Natural-log LSE = lse2 * ln 2.
+ *  - All pointers are device pointers unless stated otherwise, 16-byte
+ *    aligned.  The caller owns every buffer; the library allocates nothing.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *    Calls on one stream are ordered.  Concurrent calls on different streams
+ *    need separate workspaces and outputs.
+ *  - Errors: arguments are validated on the host before anything is enqueued;
+ *    on any error nothing is enqueued and a status code is returned.
+ *    FLAMIA_ERR_HIP reports a failed launch (the HIP error text is kept per
+ *    thread, see flamia_last_error()).  Contents of cu_seqlens are not
+ *    checked (a device array); a malformed array is undefined behaviour.
+ */
+#ifndef FLAMIA_H
+#define FLAMIA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLAMIA_ABI_VERSION 1
+
+typedef enum {
+    FLAMIA_OK = 0,
+    FLAMIA_ERR_NULL = 1,      /* a required pointer is NULL */
+    FLAMIA_ERR_SHAPE = 2,     /* d not 64/128, hq % hkv != 0, ttot > ttot_cap, ... */
+    FLAMIA_ERR_ALIGN = 3,     /* a tensor pointer is not 16-byte aligned */
+    FLAMIA_ERR_OPTS = 4,      /* c_log2 + tau > 8 (Section 3.4), key_tile != 128, ... */
+    FLAMIA_ERR_WORKSPACE = 5, /* workspace NULL or smaller than flamia_workspace_bytes() */
+    FLAMIA_ERR_HIP = 6        /* a kernel launch failed */
+} flamia_status_t;
+
+/* Host struct.  ttot_cap / ndocs_cap are the capacities the workspace is sized
+ * for (Section 3.6.1: buffer capacities depend on T only); ttot <= ttot_cap,
+ * ndocs <= ndocs_cap. */
+typedef struct {
+    int32_t ttot, ttot_cap, ndocs, ndocs_cap, hq, hkv, d;
+} flamia_dims_t;
+
+/* Host struct of numerical options.  A NULL opts pointer means the defaults
+ * of flamia_default_opts(). */
+typedef struct {
+    int32_t c_log2;        /* P-hat = E4M3(2^c p) in the forward (Appendix B.1); default 4 */
+    int32_t tau;           /* conditional rescale threshold (Appendix B.1); default 4;
+                              c_log2 + tau <= 8 is enforced (2^(c+tau) <= 448) */
+    int32_t key_tile;      /* B_c; only 128 is supported (Section 3.2, Figure 1) */
+    int32_t rowsum;        /* 0: the forward row sum accumulates the unquantized p;
+                              1: it accumulates the represented value(P-hat)/2^c */
+    float softmax_scale;   /* <= 0 selects 1/sqrt(d) */
+    /* Optional phase timing: when phase_events is non-NULL it points to
+     * n_events hipEvent_t handles (created by the caller); the call records
+     * event i on `stream` before its i-th internal launch and the next one
+     * after its last launch, as far as n_events allows.  flamia_fwd has 5
+     * phases (quantize Q, K, V; work list; forward kernel), flamia_bwd 4
+     * (quantize dO with D and the dQ clear; work list; backward kernel; dQ
+     * finalize).  NULL disables it. */
+    void **phase_events;
+    int32_t n_events;
+} flamia_opts_t;
+
+typedef struct {
+    uint8_t *codes;        /* [T][heads][d] E4M3 */
+    uint8_t *scales;       /* [heads][T] UE8M0 */
+} flamia_mx_t;
+
+flamia_opts_t flamia_default_opts(void);
+int flamia_abi_version(void);
+const char *flamia_status_str(flamia_status_t s);
+/* Text of the last HIP error seen by a call on this host thread ("" if none). */
+const char *flamia_last_error(void);
+
+/* Bytes of device workspace that flamia_fwd / flamia_bwd need for these
+ * capacities; depends on ttot_cap, ndocs_cap and the head counts only.
+ * ttot and ndocs are ignored.  Returns 0 if dims is NULL or the head layout
+ * or a capacity is invalid. */
+size_t flamia_workspace_bytes(const flamia_dims_t *dims, const flamia_opts_t *opts);
+
+/*
+ * flamia_quantize -- token-block quantization of one packed tensor
+ * (Section 3.1, Section 3.2 rounded-up exponent, Section 3.6.1 document-local
+ * blocks).
+ *   x      : bf16 [ttot][heads][d] (input)
+ *   out    : codes [ttot][heads][d] and scales [heads][ttot] (outputs)
+ * No workspace.  heads must be >= 1; only dims->ttot, ndocs and d are read.
+ */
+flamia_status_t flamia_quantize(const flamia_dims_t *dims, int32_t heads, const uint16_t *x,
+                                const int32_t *cu_seqlens, flamia_mx_t out, void *stream);
+
+/*
+ * flamia_fwd -- forward of the training call (Section 2 equations for S, P, O;
+ * Section 3.5.1 fused quantization; Appendix B.1 P-hat with the fixed 2^c
+ * factor and the conditional running maximum; Section 3.6.2 GPU-built,
+ * cost-sorted work list).
+ *   q, k, v            : bf16 inputs
+ *   q_mx, k_mx, v_mx   : outputs -- the quantized operands, which the caller
+ *                        keeps for flamia_bwd (the backward rebuilds the scores
+ *                        from exactly these codes, Section 3.3)
+ *   o                  : bf16 output [ttot][hq][d]
+ *   lse2               : fp32 output [hq][ttot]
+ *   ws / ws_bytes      : workspace of at least flamia_workspace_bytes()
+ * Deterministic: the same inputs give bitwise-identical outputs (Appendix B.5).
+ */
+flamia_status_t flamia_fwd(const flamia_dims_t *dims, const flamia_opts_t *opts,
+                           const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const int32_t *cu_seqlens,
+                           flamia_mx_t q_mx, flamia_mx_t k_mx, flamia_mx_t v_mx,
+                           uint16_t *o, float *lse2, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * flamia_bwd -- backward of the training call (Section 2 equations for dV,
+ * dP, dS, dQ, dK; Section 3.3: scores rebuilt from the forward's quantized
+ * Q/K, the same tiling, diagonal handling, exponential and saved row
+ * statistic; D_i = dO~_i . O_i from the quantized dO and the bf16 output;
+ * dS quantized on 32x32 document-local blocks; Appendix B.1: the dV operand
+ * is E4M3(2^8 P) with no stored scale).
+ *   d_o                : bf16 [ttot][hq][d] (input)
+ *   o, lse2            : the forward's outputs (inputs here)
+ *   q_mx, k_mx, v_mx   : the forward's quantized operands (inputs here)
+ *   dq                 : bf16 output [ttot][hq][d]
+ *   dk, dv             : bf16 outputs [ttot][hkv][d] (summed over the query
+ *                        heads of each group)
+ *   ws / ws_bytes      : workspace (holds the dO codes, D and the fp32 dQ
+ *                        accumulator)
+ * dQ is accumulated with fp32 atomics, so its last bits may vary run to run;
+ * dK and dV are deterministic.
+ */
+flamia_status_t flamia_bwd(const flamia_dims_t *dims, const flamia_opts_t *opts,
+                           const uint16_t *d_o, const uint16_t *o, const float *lse2,
+                           const int32_t *cu_seqlens,
+                           flamia_mx_t q_mx, flamia_mx_t k_mx, flamia_mx_t v_mx,
+                           uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                           void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLAMIA_H */

@@ -60,6 +60,14 @@ typedef struct {
     int32_t rowsum;       /* 0: unquantized p, 1: represented value(P-hat)/2^c */
     double softmax_scale; /* <= 0 selects 1/sqrt(d) */
     int32_t unsafe_bound; /* 1 skips the c + tau <= 8 check (negative tests only) */
+    /* Tolerance bookkeeping (test infrastructure, not part of the method):
+     * relative error bound of an implementation's score dot products, as a
+     * fraction of the largest single product |q_k k_k|.  When > 0 and the
+     * tol_* outputs are requested, the oracle reports for every output element
+     * how far it can move when a quantization decision (a P-hat or P-hat_b
+     * code, a running-maximum replacement) lies within that error band of its
+     * rounding or comparison threshold. */
+    double score_rel_err;
 } orc_params;
 
 /* ---------------------------------------------------------------------------
@@ -232,7 +240,52 @@ typedef struct {
     double *dq64, *dk64, *dv64; uint16_t *dq16, *dk16, *dv16;
     int64_t *stats;   /* [0] P-hat entries that saturated, [1] dS entries
                          (causal, in-document), [2] nonzero dS quantized to 0 */
+    double *tol_o, *tol_lse, *tol_dv, *tol_dq, *tol_dk;   /* decision-sensitivity bounds */
 } orc_out;
+
+/* ---------------------------------------------------------------------------
+ * Decision-sensitivity helpers (test infrastructure).
+ * ------------------------------------------------------------------------- */
+static double e4m3_spacing(double y)
+{
+    /* distance from value(code(y)) to the next larger code value */
+    uint8_t c = orc_e4m3_encode(fabs(y));
+    if (c >= 0x7E) return 32.0;
+    return orc_e4m3_value((uint8_t)(c + 1)) - orc_e4m3_value(c);
+}
+
+/* Largest change of the represented value of E4M3(y) when log2(y) moves by
+ * at most r; `loose` widens it to one code step regardless. */
+static double code_swing(double y, double r, int loose)
+{
+    double lo = orc_e4m3_value(orc_e4m3_encode(y * exp2(-r)));
+    double hi = orc_e4m3_value(orc_e4m3_encode(y * exp2(r)));
+    double sw = hi - lo;
+    if (loose) {
+        double sp = e4m3_spacing(y);
+        if (sp > sw) sw = sp;
+    }
+    return sw;
+}
+
+/* E4M3 value of v scaled by 2^-e, scaled back */
+static double deq_at(double v, int e)
+{
+    return ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(v, -e))), e);
+}
+
+/* score error bound (log2 units) of one pair: the implementation's dot
+ * product error plus fp32 roundings of the score pipeline */
+static double score_delta(const orc_params *p, const double *a, const double *b, int d,
+                          double c1, double x, double m)
+{
+    double mp = 0.0;
+    for (int k = 0; k < d; ++k) {
+        double t = fabs(a[k] * b[k]);
+        if (t > mp) mp = t;
+    }
+    return p->score_rel_err * mp * c1 + 0x1p-20 * (1.0 + fabs(x) + (isfinite(m) ? fabs(m) : 0.0));
+}
 
 static double dotd(const double *a, const double *b, int d)
 {
@@ -243,26 +296,51 @@ static double dotd(const double *a, const double *b, int d)
 
 /* Forward for one query row (Section 2 equations for S, P, O; Appendix B.1
  * for the fixed 2^c factor and the conditional running maximum). */
+typedef struct {
+    double *tacc;   /* [d] like acc: sum of code swings x |V| (NULL: no bookkeeping) */
+    double *delta;  /* [key_tile] per-entry score error bounds of the current tile */
+    double tol_lse; /* out: bound on |lse2 change| */
+    double *tol_o;  /* out: [d] */
+} row_tol;
+
 static void fwd_row(const orc_params *p, int i, const double *qi, const double *Kt,
                     const double *Vt, double c1, double *acc, double *x,
-                    double *o_out, double *lse_out, int64_t *sat)
+                    double *o_out, double *lse_out, int64_t *sat, row_tol *rt)
 {
     int d = p->d, B = p->key_tile, quant = p->quant;
     double m = -INFINITY, l = 0.0;
     double two_c = ldexp(1.0, p->c_log2);
+    /* tolerance bookkeeping (not part of the method) */
+    const int track = rt != NULL && quant != QUANT_NONE;
+    double dm = 0.0, dmax = 0.0, tl = 0.0;
+    int loose = 0;
     for (int k = 0; k < d; ++k) acc[k] = 0.0;
+    if (track) for (int k = 0; k < d; ++k) rt->tacc[k] = 0.0;
     for (int j0 = 0; j0 <= i; j0 += B) {
         int j1 = j0 + B <= i + 1 ? j0 + B : i + 1;
-        double mu = -INFINITY;
+        double mu = -INFINITY, dmu = 0.0;
         for (int j = j0; j < j1; ++j) {
             x[j - j0] = dotd(qi, Kt + (long)j * d, d) * c1;
             if (x[j - j0] > mu) mu = x[j - j0];
+        }
+        if (track) {
+            for (int j = j0; j < j1; ++j) {
+                rt->delta[j - j0] = score_delta(p, qi, Kt + (long)j * d, d, c1, x[j - j0], m);
+                if (rt->delta[j - j0] > dmu) dmu = rt->delta[j - j0];
+            }
+            if (m != -INFINITY && fabs(mu - m - (double)p->tau) <= dmu + dm) loose = 1;
+            if (dmu > dmax) dmax = dmu;
         }
         if (m == -INFINITY || mu - m > (double)p->tau) {
             double alpha = (m == -INFINITY) ? 0.0 : exp2(m - mu);
             l *= alpha;
             for (int k = 0; k < d; ++k) acc[k] *= alpha;
             m = mu;
+            if (track) {
+                for (int k = 0; k < d; ++k) rt->tacc[k] *= alpha;
+                tl *= alpha;
+                dm = dmu;
+            }
         }
         for (int j = j0; j < j1; ++j) {
             double pj = exp2(x[j - j0] - m), w;
@@ -277,6 +355,13 @@ static void fwd_row(const orc_params *p, int i, const double *qi, const double *
                 code = orc_e4m3_encode(y);
                 w = orc_e4m3_value(code);
                 l += (p->rowsum == 1) ? w / two_c : pj;
+                if (track) {
+                    double sw = code_swing(y, rt->delta[j - j0] + dm, loose);
+                    if (sw > 0.0) {
+                        for (int k = 0; k < d; ++k) rt->tacc[k] += sw * fabs(vj[k]);
+                        if (p->rowsum == 1) tl += sw / two_c;
+                    }
+                }
             }
             for (int k = 0; k < d; ++k) acc[k] += w * vj[k];
         }
@@ -285,6 +370,13 @@ static void fwd_row(const orc_params *p, int i, const double *qi, const double *
         double den = (quant == QUANT_NONE) ? l : l * two_c;
         for (int k = 0; k < d; ++k) o_out[k] = acc[k] / den;
         *lse_out = m + log2(l);
+        if (track) {
+            /* codes that may move, plus the smooth movement of the row sum */
+            double rel_l = log(2.0) * (dmax + dm);
+            for (int k = 0; k < d; ++k)
+                rt->tol_o[k] = rt->tacc[k] / den + fabs(o_out[k]) * (tl / l + rel_l);
+            rt->tol_lse = dmax + dm + log2(1.0 + tl / l) + 0x1p-20 * (1.0 + fabs(*lse_out));
+        }
     }
 }
 
@@ -302,6 +394,12 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
     float *lsef = 0;
     int64_t sat = 0, nds = 0, nds0 = 0;
     size_t Ld = (size_t)L * d;
+    /* tolerance bookkeeping (test infrastructure) */
+    const int track = p->score_rel_err > 0 && quant != QUANT_NONE &&
+                      (out->tol_o || out->tol_lse || out->tol_dv || out->tol_dq || out->tol_dk);
+    double *tacc = 0, *tdel = 0, *tolo = 0, *tlse = 0, *tdv = 0;
+    double *tOall = 0, *dSd = 0, *tdq = 0, *tdk = 0;
+    row_tol rt_store, *rt = 0;
 
     if (L == 0) return;
     Kt = malloc(sizeof(double) * Ld);
@@ -320,8 +418,27 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         dKa = calloc(Ld, sizeof(double));
         dVa = calloc(Ld, sizeof(double));
     }
+    if (track) {
+        tacc = malloc(sizeof(double) * d);
+        tdel = malloc(sizeof(double) * (p->key_tile > 32 ? p->key_tile : 32));
+        tolo = malloc(sizeof(double) * d);
+        tlse = malloc(sizeof(double) * L);
+        if (need_bwd) {
+            tdv = calloc(Ld, sizeof(double));
+            tOall = malloc(sizeof(double) * Ld);
+            dSd = malloc(sizeof(double) * 32 * (size_t)L);
+            tdq = malloc(sizeof(double) * Ld);
+            tdk = calloc(Ld, sizeof(double));
+        }
+        rt_store.tacc = tacc;
+        rt_store.delta = tdel;
+        rt_store.tol_o = tolo;
+        rt = &rt_store;
+    }
     if (!Kt || !Vt || !Qt || !O || !lse || !lsef || !acc || !xbuf ||
-        (need_bwd && (!dOt || !Dv || !dS || !dQa || !dKa || !dVa))) {
+        (need_bwd && (!dOt || !Dv || !dS || !dQa || !dKa || !dVa)) ||
+        (track && (!tacc || !tdel || !tolo || !tlse ||
+                   (need_bwd && (!tdv || !tOall || !dSd || !tdq || !tdk))))) {
         *err = ORC_ERR_NOMEM;
         goto done;
     }
@@ -334,8 +451,15 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         tbq_slice(q + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, Qt, 0, 0, 0);
         /* ---- forward, row by row ---- */
         for (int i = 0; i < L; ++i) {
-            fwd_row(p, i, Qt + (long)i * d, Kt, Vt, c1, acc, xbuf, O + (long)i * d, &lse[i], &sat);
+            fwd_row(p, i, Qt + (long)i * d, Kt, Vt, c1, acc, xbuf, O + (long)i * d, &lse[i], &sat, rt);
             lsef[i] = (float)lse[i];
+            if (track) {
+                tlse[i] = rt->tol_lse;
+                if (out->tol_lse) out->tol_lse[(long)h * p->ttot + base + i] = rt->tol_lse;
+                if (out->tol_o)
+                    for (int c = 0; c < d; ++c) out->tol_o[((long)(base + i) * hq + h) * d + c] = tolo[c];
+                if (tOall) memcpy(tOall + (long)i * d, tolo, sizeof(double) * d);
+            }
             /* MX modes return a bf16 O and the backward reads it back
              * (Section 3.4: returned outputs are BF16); the exact mode keeps
              * binary64 throughout. */
@@ -357,6 +481,7 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
             if (out->dvec) out->dvec[(long)h * p->ttot + base + i] = Dv[i];
         }
         memset(dQa, 0, sizeof(double) * Ld);
+        if (tdq) memset(tdq, 0, sizeof(double) * Ld);
         for (int i0 = 0; i0 < L; i0 += 32) {
             int i1 = i0 + 32 < L ? i0 + 32 : L;
             /* dS for the 32 query rows of this block, every visible key. */
@@ -374,24 +499,45 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                     } else {
                         /* Appendix B.1: the dV operand is E4M3(2^8 P), no scale. */
                         wb = ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(P, 8))), -8);
+                        if (track && tdv) {   /* tolerance bookkeeping */
+                            double r = score_delta(p, qi, Kt + (long)j * d, d, c1, xij, li) + tlse[i];
+                            double sw = ldexp(code_swing(ldexp(P, 8), r, 0), -8);
+                            if (sw > 0.0)
+                                for (int c = 0; c < d; ++c) tdv[(long)j * d + c] += sw * fabs(doi[c]);
+                        }
                     }
                     for (int c = 0; c < d; ++c) dVa[(long)j * d + c] += wb * doi[c];
                     row[j] = P * (dP - Dv[i]);
+                    if (dSd) {   /* tolerance bookkeeping: error band of dS */
+                        double dx = score_delta(p, qi, Kt + (long)j * d, d, c1, xij, li) + tlse[i];
+                        double ddp = score_delta(p, doi, Vt + (long)j * d, d, 1.0, dP, 0.0);
+                        double dD = 0x1p-20 * fabs(Dv[i]);
+                        for (int c = 0; c < d; ++c) dD += fabs(doi[c]) * tOall[(long)i * d + c];
+                        dSd[(size_t)(i - i0) * L + j] =
+                            fabs(row[j]) * (exp2(dx) - 1.0) + P * (ddp + dD);
+                    }
                 }
             }
             /* dS~: one exponent per 32x32 document-local block (Section 3.3),
              * then dQ += dS~ K~ and dK += dS~^T Q~. */
             for (int j0 = 0; j0 <= i1 - 1; j0 += 32) {
                 int j1 = j0 + 32 < L ? j0 + 32 : L;
-                int e = 0;
+                int e = 0, elo = 0, ehi = 0;
                 if (quant != QUANT_NONE) {
-                    double amax = 0.0;
+                    double amax = 0.0, alo = 0.0, ahi = 0.0;
                     for (int i = i0; i < i1; ++i)
                         for (int j = j0; j < j1 && j <= i; ++j) {
                             double a = fabs(dS[(size_t)(i - i0) * L + j]);
                             if (a > amax) amax = a;
+                            if (dSd) {   /* tolerance bookkeeping: exponent band */
+                                double b = dSd[(size_t)(i - i0) * L + j];
+                                if (a - b > alo) alo = a - b;
+                                if (a + b > ahi) ahi = a + b;
+                            }
                         }
                     e = orc_scale_exp(amax, quant == QUANT_FLOOR ? 1 : 0);
+                    elo = dSd ? orc_scale_exp(alo, quant == QUANT_FLOOR ? 1 : 0) : e;
+                    ehi = dSd ? orc_scale_exp(ahi, quant == QUANT_FLOOR ? 1 : 0) : e;
                 }
                 for (int i = i0; i < i1; ++i)
                     for (int j = j0; j < j1 && j <= i; ++j) {
@@ -402,6 +548,21 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                             dq = ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(ds, -e))), e);
                             nds++;
                             if (ds != 0.0 && dq == 0.0) nds0++;
+                            if (dSd) {   /* tolerance bookkeeping: how far dS~ can move */
+                                double band = dSd[(size_t)(i - i0) * L + j], sw = 0.0;
+                                const int es[3] = {elo, e, ehi};
+                                for (int a = 0; a < 3; ++a) {
+                                    double t1 = fabs(deq_at(ds + band, es[a]) - dq);
+                                    double t2 = fabs(deq_at(ds - band, es[a]) - dq);
+                                    if (t1 > sw) sw = t1;
+                                    if (t2 > sw) sw = t2;
+                                }
+                                if (sw > 0.0)
+                                    for (int c = 0; c < d; ++c) {
+                                        tdq[(long)i * d + c] += sw * fabs(Kt[(long)j * d + c]);
+                                        tdk[(long)j * d + c] += sw * fabs(Qt[(long)i * d + c]);
+                                    }
+                            }
                         }
                         if (dq == 0.0) continue;
                         for (int c = 0; c < d; ++c) {
@@ -416,6 +577,7 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                 long gi = ((long)(base + i) * hq + h) * d + c;
                 double val = s * dQa[(long)i * d + c];
                 if (out->dq64) out->dq64[gi] = val;
+                if (tdq && out->tol_dq) out->tol_dq[gi] = s * tdq[(long)i * d + c];
                 if (out->dq16) out->dq16[gi] = orc_double_to_bf16(val);
             }
     }
@@ -428,6 +590,8 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                 if (out->dv64) out->dv64[gj] = vv;
                 if (out->dk16) out->dk16[gj] = orc_double_to_bf16(kv);
                 if (out->dv16) out->dv16[gj] = orc_double_to_bf16(vv);
+                if (tdv && out->tol_dv) out->tol_dv[gj] = tdv[(long)j * d + c];
+                if (tdk && out->tol_dk) out->tol_dk[gj] = s * tdk[(long)j * d + c];
             }
     }
     if (out->stats) {
@@ -441,6 +605,8 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
 done:
     free(Kt); free(Vt); free(Qt); free(O); free(lse); free(lsef); free(acc); free(xbuf);
     free(dOt); free(Dv); free(dS); free(dQa); free(dKa); free(dVa);
+    free(tacc); free(tdel); free(tolo); free(tlse); free(tdv);
+    free(tOall); free(dSd); free(tdq); free(tdk);
 }
 
 typedef struct { long len; int doc, g; } unit_t;
@@ -465,9 +631,11 @@ int orc_attention(const orc_params *p, const uint16_t *q, const uint16_t *k, con
                   const uint8_t *doc_mask,
                   double *o64, uint16_t *o16, float *lse2, double *dvec,
                   double *dq64, double *dk64, double *dv64,
-                  uint16_t *dq16, uint16_t *dk16, uint16_t *dv16, int64_t *stats)
+                  uint16_t *dq16, uint16_t *dk16, uint16_t *dv16, int64_t *stats,
+                  double *tol_o, double *tol_lse, double *tol_dv, double *tol_dq, double *tol_dk)
 {
-    orc_out out = {o64, o16, lse2, dvec, dq64, dk64, dv64, dq16, dk16, dv16, stats};
+    orc_out out = {o64, o16, lse2, dvec, dq64, dk64, dv64, dq16, dk16, dv16, stats,
+                   tol_o, tol_lse, tol_dv, tol_dq, tol_dk};
     unit_t *units;
     long nu = 0;
     int err = ORC_OK;

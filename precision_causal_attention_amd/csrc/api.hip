@@ -1,0 +1,265 @@
+// C-ABI host layer: argument validation, workspace layout and the launch
+// sequence of the training call.  Nothing here synchronizes with the device
+// or allocates memory; every launch goes to the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "flamia.h"
+#include "kernels.h"
+
+using namespace flamia;
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+flamia_status_t hip_fail(hipError_t e) {
+    strncpy(g_last_error, hipGetErrorString(e), sizeof g_last_error - 1);
+    g_last_error[sizeof g_last_error - 1] = 0;
+    return FLAMIA_ERR_HIP;
+}
+
+constexpr long kMaxTokens = 1L << 20;        // ttot_cap limit (1M tokens; bounds the plan kernel's LDS histogram)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Capacities and head layout (all the workspace size depends on).
+flamia_status_t check_caps(const flamia_dims_t* d) {
+    if (!d) return FLAMIA_ERR_NULL;
+    if (d->d != 64 && d->d != 128) return FLAMIA_ERR_SHAPE;
+    if (d->hq <= 0 || d->hkv <= 0 || d->hq % d->hkv) return FLAMIA_ERR_SHAPE;
+    if (d->ttot_cap < 0 || d->ttot_cap > kMaxTokens) return FLAMIA_ERR_SHAPE;
+    if (d->ndocs_cap < 0 || d->ndocs_cap > kMaxTokens) return FLAMIA_ERR_SHAPE;
+    return FLAMIA_OK;
+}
+
+// Everything a call needs: capacities plus the current sizes within them.
+flamia_status_t check_dims(const flamia_dims_t* d) {
+    const flamia_status_t s = check_caps(d);
+    if (s != FLAMIA_OK) return s;
+    if (d->ttot < 0 || d->ttot > d->ttot_cap) return FLAMIA_ERR_SHAPE;
+    if (d->ndocs < 0 || d->ndocs > d->ndocs_cap) return FLAMIA_ERR_SHAPE;
+    if (d->ttot > 0 && d->ndocs == 0) return FLAMIA_ERR_SHAPE;
+    return FLAMIA_OK;
+}
+
+flamia_status_t check_opts(const flamia_opts_t* o) {
+    // Section 3.4 / Appendix B.1: 2^(c + tau) must stay within 448.
+    if (o->c_log2 < 0 || o->tau < 0 || o->c_log2 + o->tau > 8) return FLAMIA_ERR_OPTS;
+    if (o->key_tile != kTile) return FLAMIA_ERR_OPTS;
+    if (o->rowsum != 0 && o->rowsum != 1) return FLAMIA_ERR_OPTS;
+    if (!(o->softmax_scale <= 0.f || isfinite(o->softmax_scale))) return FLAMIA_ERR_OPTS;
+    if (o->n_events < 0 || (o->n_events > 0 && !o->phase_events)) return FLAMIA_ERR_OPTS;
+    return FLAMIA_OK;
+}
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+    long max_tiles, max_items;
+    int max_cost;
+    size_t ctrl, prefix, items, ocodes, oscales, dvec, dqacc, total;
+};
+
+Layout layout(const flamia_dims_t* d) {
+    Layout w;
+    const long tc = d->ttot_cap;
+    w.max_cost = (int)((tc + kTile - 1) / kTile) + 1;
+    w.max_tiles = tc / kTile + d->ndocs_cap + 1;
+    w.max_items = w.max_tiles * (d->hq > d->hkv ? d->hq : d->hkv);
+    size_t off = 0;
+    w.ctrl = off;    off += up256(sizeof(int32_t) * (16 + 2 * (size_t)(w.max_cost + 1)));
+    w.prefix = off;  off += up256(sizeof(int32_t) * ((size_t)d->ndocs_cap + 1));
+    w.items = off;   off += up256(sizeof(int4) * (size_t)w.max_items);
+    w.ocodes = off;  off += up256((size_t)tc * d->hq * d->d);
+    w.oscales = off; off += up256((size_t)tc * d->hq);
+    w.dvec = off;    off += up256(sizeof(float) * (size_t)tc * d->hq);
+    w.dqacc = off;   off += up256(sizeof(float) * (size_t)tc * d->hq * d->d);
+    w.total = off;
+    return w;
+}
+
+flamia_opts_t resolve(const flamia_opts_t* o) { return o ? *o : flamia_default_opts(); }
+
+// Records the caller's phase event i (if provided) on the stream.
+struct PhaseMarks {
+    const flamia_opts_t& o;
+    hipStream_t st;
+    int next = 0;
+    hipError_t mark() {
+        if (!o.phase_events || next >= o.n_events) { ++next; return hipSuccess; }
+        return hipEventRecord((hipEvent_t)o.phase_events[next++], st);
+    }
+};
+
+float scale_of(const flamia_opts_t& o, int d) {
+    return o.softmax_scale > 0.f ? o.softmax_scale : 1.0f / sqrtf((float)d);
+}
+
+bool mx_ok(flamia_mx_t m) { return m.codes && m.scales && aligned16(m.codes); }
+
+}  // namespace
+
+extern "C" {
+
+flamia_opts_t flamia_default_opts(void) {
+    flamia_opts_t o;
+    o.c_log2 = 4;
+    o.tau = 4;
+    o.key_tile = kTile;
+    o.rowsum = 0;
+    o.softmax_scale = 0.f;
+    o.phase_events = nullptr;
+    o.n_events = 0;
+    return o;
+}
+
+int flamia_abi_version(void) { return FLAMIA_ABI_VERSION; }
+
+const char* flamia_status_str(flamia_status_t s) {
+    switch (s) {
+        case FLAMIA_OK: return "ok";
+        case FLAMIA_ERR_NULL: return "null pointer argument";
+        case FLAMIA_ERR_SHAPE: return "unsupported or inconsistent shape";
+        case FLAMIA_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case FLAMIA_ERR_OPTS: return "invalid options (c_log2 + tau must be <= 8, key_tile 128)";
+        case FLAMIA_ERR_WORKSPACE: return "workspace missing or too small";
+        case FLAMIA_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+const char* flamia_last_error(void) { return g_last_error; }
+
+size_t flamia_workspace_bytes(const flamia_dims_t* dims, const flamia_opts_t* opts) {
+    if (check_caps(dims) != FLAMIA_OK) return 0;
+    (void)opts;
+    return layout(dims).total;
+}
+
+flamia_status_t flamia_quantize(const flamia_dims_t* dims, int32_t heads, const uint16_t* x,
+                                const int32_t* cu_seqlens, flamia_mx_t out, void* stream) {
+    flamia_status_t s = check_dims(dims);
+    if (s != FLAMIA_OK) return s;
+    if (heads <= 0) return FLAMIA_ERR_SHAPE;
+    if (!x || !cu_seqlens || !out.codes || !out.scales) return FLAMIA_ERR_NULL;
+    if (!aligned16(x) || !aligned16(out.codes)) return FLAMIA_ERR_ALIGN;
+    QuantArgs a{x, cu_seqlens, dims->ndocs, dims->ttot, heads, dims->d, out.codes, out.scales, nullptr, nullptr, nullptr};
+    hipError_t e = launch_quantize(a, (hipStream_t)stream);
+    return e == hipSuccess ? FLAMIA_OK : hip_fail(e);
+}
+
+flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_in,
+                           const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const int32_t* cu_seqlens,
+                           flamia_mx_t q_mx, flamia_mx_t k_mx, flamia_mx_t v_mx,
+                           uint16_t* o, float* lse2, void* ws, size_t ws_bytes, void* stream) {
+    flamia_status_t s = check_dims(dims);
+    if (s != FLAMIA_OK) return s;
+    const flamia_opts_t opts = resolve(opts_in);
+    if ((s = check_opts(&opts)) != FLAMIA_OK) return s;
+    if (!q || !k || !v || !cu_seqlens || !o || !lse2 || !q_mx.codes || !q_mx.scales ||
+        !k_mx.codes || !k_mx.scales || !v_mx.codes || !v_mx.scales)
+        return FLAMIA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !mx_ok(q_mx) ||
+        !mx_ok(k_mx) || !mx_ok(v_mx))
+        return FLAMIA_ERR_ALIGN;
+    const Layout w = layout(dims);
+    if (!ws || ws_bytes < w.total) return FLAMIA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return FLAMIA_ERR_ALIGN;
+    if (dims->ttot == 0) return FLAMIA_OK;
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* base = (uint8_t*)ws;
+    const int d = dims->d;
+
+    // fused quantization of the three operands (Section 3.5.1)
+    const QuantArgs qa[3] = {
+        {q, cu_seqlens, dims->ndocs, dims->ttot, dims->hq, d, q_mx.codes, q_mx.scales, nullptr, nullptr, nullptr},
+        {k, cu_seqlens, dims->ndocs, dims->ttot, dims->hkv, d, k_mx.codes, k_mx.scales, nullptr, nullptr, nullptr},
+        {v, cu_seqlens, dims->ndocs, dims->ttot, dims->hkv, d, v_mx.codes, v_mx.scales, nullptr, nullptr, nullptr}};
+    PhaseMarks pm{opts, st};
+    hipError_t e;
+    for (const QuantArgs& a : qa) {
+        if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(a, st)) != hipSuccess) return hip_fail(e);
+    }
+    int32_t* ctrl = (int32_t*)(base + w.ctrl);
+    int4* items = (int4*)(base + w.items);
+    PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, dims->hq, 0,
+                items, w.max_tiles * dims->hq};
+    if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
+    FwdArgs fa;
+    fa.qc = q_mx.codes; fa.qs = q_mx.scales;
+    fa.kc = k_mx.codes; fa.ks = k_mx.scales;
+    fa.vc = v_mx.codes; fa.vs = v_mx.scales;
+    fa.o = o; fa.lse2 = lse2;
+    fa.items = items; fa.nitems = ctrl;
+    fa.ttot = dims->ttot; fa.hq = dims->hq; fa.hkv = dims->hkv;
+    fa.c1 = scale_of(opts, d) * 1.4426950408889634f;
+    fa.c_log2 = (float)opts.c_log2;
+    fa.tau = (float)opts.tau;
+    fa.rowsum = opts.rowsum;
+    if ((e = pm.mark()) != hipSuccess || (e = launch_fwd(fa, d, w.max_tiles * dims->hq, st)) != hipSuccess)
+        return hip_fail(e);
+    e = pm.mark();
+    return e == hipSuccess ? FLAMIA_OK : hip_fail(e);
+}
+
+flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_in,
+                           const uint16_t* d_o, const uint16_t* o, const float* lse2,
+                           const int32_t* cu_seqlens,
+                           flamia_mx_t q_mx, flamia_mx_t k_mx, flamia_mx_t v_mx,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                           void* ws, size_t ws_bytes, void* stream) {
+    flamia_status_t s = check_dims(dims);
+    if (s != FLAMIA_OK) return s;
+    const flamia_opts_t opts = resolve(opts_in);
+    if ((s = check_opts(&opts)) != FLAMIA_OK) return s;
+    if (!d_o || !o || !lse2 || !cu_seqlens || !dq || !dk || !dv || !q_mx.codes || !q_mx.scales ||
+        !k_mx.codes || !k_mx.scales || !v_mx.codes || !v_mx.scales)
+        return FLAMIA_ERR_NULL;
+    if (!aligned16(d_o) || !aligned16(o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        !mx_ok(q_mx) || !mx_ok(k_mx) || !mx_ok(v_mx))
+        return FLAMIA_ERR_ALIGN;
+    const Layout w = layout(dims);
+    if (!ws || ws_bytes < w.total) return FLAMIA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return FLAMIA_ERR_ALIGN;
+    if (dims->ttot == 0) return FLAMIA_OK;
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* base = (uint8_t*)ws;
+    const int d = dims->d;
+    uint8_t* oc = base + w.ocodes;
+    uint8_t* os = base + w.oscales;
+    float* dvec = (float*)(base + w.dvec);
+    float* dqacc = (float*)(base + w.dqacc);
+
+    // dO launch: codes + scales, D = dO~ . O, dQ accumulator cleared (Section 3.5.1)
+    QuantArgs qa{d_o, cu_seqlens, dims->ndocs, dims->ttot, dims->hq, d, oc, os, o, dvec, dqacc};
+    PhaseMarks pm{opts, st};
+    hipError_t e;
+    if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(qa, st)) != hipSuccess) return hip_fail(e);
+    int32_t* ctrl = (int32_t*)(base + w.ctrl);
+    int4* items = (int4*)(base + w.items);
+    PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, dims->hkv, 1,
+                items, w.max_tiles * dims->hkv};
+    if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
+    BwdArgs ba;
+    ba.qc = q_mx.codes; ba.qs = q_mx.scales;
+    ba.kc = k_mx.codes; ba.ks = k_mx.scales;
+    ba.vc = v_mx.codes; ba.vs = v_mx.scales;
+    ba.oc = oc; ba.os = os;
+    ba.lse2 = lse2; ba.dvec = dvec; ba.dqacc = dqacc;
+    ba.dk = dk; ba.dv = dv;
+    ba.items = items; ba.nitems = ctrl;
+    ba.ttot = dims->ttot; ba.hq = dims->hq; ba.hkv = dims->hkv;
+    ba.scale = scale_of(opts, d);
+    ba.c1 = ba.scale * 1.4426950408889634f;
+    if ((e = pm.mark()) != hipSuccess || (e = launch_bwd(ba, d, w.max_tiles * dims->hkv, st)) != hipSuccess)
+        return hip_fail(e);
+    if ((e = pm.mark()) != hipSuccess ||
+        (e = launch_dq_finalize(dqacc, dq, (long)dims->ttot * dims->hq * d, ba.scale, st)) != hipSuccess)
+        return hip_fail(e);
+    e = pm.mark();
+    return e == hipSuccess ? FLAMIA_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,262 @@
+// MXFP8 causal backward over packed documents (FLAMIA paper: Section 2
+// equations dV = P^T dO, dP = dO V^T, dS = P o (dP - D), dQ = dS K,
+// dK = dS^T Q; Section 3.3: scores rebuilt from the forward's quantized Q/K
+// with the same tiling, masking and exponential, P from the saved row
+// statistic, dS quantized on 32x32 document-local blocks from the block
+// maximum; Appendix B.1: the dV operand is E4M3(2^8 P) with no stored scale).
+//
+// One workgroup = one work item (document, key/value head, 128-key tile
+// anchored at the document start); wave w owns keys 32w..32w+31 of the tile.
+// For every query head of the group and every 64-query step from the
+// diagonal to the end of the document:
+//   S  [query][key] = Q^ K^T    A = query rows (LDS), B = the wave's key rows (registers)
+//   dP [query][key] = dO^ V^T   same structure; both bitwise equal to the
+//                               forward's S^T (role-swapped operands give identical
+//                               accumulator bits on this hardware)
+//   P = 2^(x - lse2), P-hat_b = E4M3(2^8 P), dS = P (dP - D)
+//   dS-hat: one exponent per 32x32 block = one accumulator tile (block max via
+//   a wave reduction), codes written once and read in both orientations:
+//   dV^T += dO^T P-hat_b   (A = dO^T by transposed LDS read, B = accumulator bytes)
+//   dK^T += Q^T dS-hat     (A = Q^T by transposed LDS read, B = accumulator bytes)
+//   dQ   += dS-hat K^      (A = dS-hat by transposed read of its key-major LDS
+//                           copy, B = K^ by transposed read), fp32 atomics into
+//                           the accumulator, scaled and rounded by dq_finalize.
+// dK and dV accumulate in registers across the query heads of the group
+// (GQA sum in fp32) and are written once.
+#include "device.h"
+#include "kernels.h"
+
+namespace flamia {
+
+constexpr int kQStep = 64;
+
+template <int D>
+struct BwdSmem {
+    static constexpr int kStride = D + 16;       // row pitch of code tiles
+    static constexpr int kSStride = kQStep + 16; // row pitch of the key-major dS-hat tile
+    uint8_t q[kQStep * kStride];
+    uint8_t o[kQStep * kStride];                 // quantized dO
+    uint8_t k[kTile * kStride];
+    uint8_t st[kTile * kSStride];                // dS-hat, [key][query]
+    float lse[kQStep];
+    float dv[kQStep];                            // D
+    uint8_t eq[kQStep];
+    uint8_t eo[kQStep];
+    uint8_t ek[kTile];
+    int es[2][4];                                // dS block exponent + 127 [query block][key block]
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdArgs a) {
+    constexpr int KC = D / 64;
+    constexpr int DT = D / 32;
+    constexpr int STR = BwdSmem<D>::kStride;
+    constexpr int SSTR = BwdSmem<D>::kSStride;
+    constexpr int QCH = kQStep * D / 16;          // 16-byte chunks of a 64-row code tile
+    constexpr int KCH = kTile * D / 16;
+    __shared__ BwdSmem<D> sm;
+
+    if ((int)blockIdx.x >= *a.nitems) return;
+    const int4 it = a.items[blockIdx.x];
+    const int k0 = it.x, ds = it.y, de = it.z, g = it.w;
+    const int G = a.hq / a.hkv;
+    const int L = de - ds;
+    const int kt0 = k0 - ds;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lg = lane >> 5, lr = lane & 31;
+    const int key_loc = kt0 + 32 * wave + lr;
+    const bool key_valid = key_loc < L;
+    const int key_row = ds + min(key_loc, L - 1);
+
+    // The wave's key rows as B operands of S and dP (column = key, k = channel).
+    v8i kb[KC], vb[KC];
+    {
+        const uint8_t* kp = a.kc + ((long)key_row * a.hkv + g) * D;
+        const uint8_t* vp = a.vc + ((long)key_row * a.hkv + g) * D;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            uint4 lo = *reinterpret_cast<const uint4*>(kp + 64 * kc + 16 * lg);
+            uint4 hi = *reinterpret_cast<const uint4*>(kp + 64 * kc + 32 + 16 * lg);
+            kb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            lo = *reinterpret_cast<const uint4*>(vp + 64 * kc + 16 * lg);
+            hi = *reinterpret_cast<const uint4*>(vp + 64 * kc + 32 + 16 * lg);
+            vb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+    }
+    const int ek = a.ks[(long)g * a.ttot + key_row];
+    const int ev = a.vs[(long)g * a.ttot + key_row];
+
+    // K^ tile of the work item in LDS (B operand of dQ, read transposed)
+    for (int c = tid; c < KCH; c += 256) {
+        const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+        const long kr = min(k0 + row, a.ttot - 1);
+        *reinterpret_cast<uint4*>(&sm.k[row * STR + col]) = *reinterpret_cast<const uint4*>(a.kc + (kr * a.hkv + g) * D + col);
+    }
+    if (tid < kTile) sm.ek[tid] = a.ks[(long)g * a.ttot + min(k0 + tid, a.ttot - 1)];
+
+    v16f dvt[DT], dkt[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) { dvt[dt] = v16f{0}; dkt[dt] = v16f{0}; }
+
+    const int s16 = lane & 15, grp = (lane >> 4) & 1;
+    const int tr_key = 8 * ((s16 >> 1) >> 2) + 4 * lg + ((s16 >> 1) & 3);
+    const int tr_col = 16 * grp + 8 * (s16 & 1);
+    const float inv256 = 1.f / 256.f;
+
+    for (int hh = 0; hh < G; ++hh) {
+        const int h = g * G + hh;
+        for (int q0 = kt0; q0 < L; q0 += kQStep) {
+            // ---- stage the 64-query step: codes, scales, lse2 (+inf past the document), D
+            __syncthreads();
+            for (int c = tid; c < QCH; c += 256) {
+                const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+                const long qr = ds + min(q0 + row, L - 1);
+                *reinterpret_cast<uint4*>(&sm.q[row * STR + col]) = *reinterpret_cast<const uint4*>(a.qc + (qr * a.hq + h) * D + col);
+                *reinterpret_cast<uint4*>(&sm.o[row * STR + col]) = *reinterpret_cast<const uint4*>(a.oc + (qr * a.hq + h) * D + col);
+            }
+            if (tid < kQStep) {
+                const int ql = q0 + tid;
+                const long qr = ds + min(ql, L - 1);
+                sm.eq[tid] = a.qs[(long)h * a.ttot + qr];
+                sm.eo[tid] = a.os[(long)h * a.ttot + qr];
+                sm.lse[tid] = ql < L ? a.lse2[(long)h * a.ttot + qr] : INFINITY;
+                sm.dv[tid] = a.dvec[(long)h * a.ttot + qr];
+            }
+            __syncthreads();
+
+            // ---- S and dP for the wave's 32 keys x 64 queries
+            v16f sacc[2], pacc[2];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int row = 32 * st + lr;
+                sacc[st] = v16f{0};
+                pacc[st] = v16f{0};
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    uint4 lo = *reinterpret_cast<const uint4*>(&sm.q[row * STR + 64 * kc + 16 * lg]);
+                    uint4 hi = *reinterpret_cast<const uint4*>(&sm.q[row * STR + 64 * kc + 32 + 16 * lg]);
+                    const v8i qa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    sacc[st] = mfma_mx(qa, kb[kc], sacc[st], sm.eq[row], ek);
+                    lo = *reinterpret_cast<const uint4*>(&sm.o[row * STR + 64 * kc + 16 * lg]);
+                    hi = *reinterpret_cast<const uint4*>(&sm.o[row * STR + 64 * kc + 32 + 16 * lg]);
+                    const v8i oa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    pacc[st] = mfma_mx(oa, vb[kc], pacc[st], sm.eo[row], ev);
+                }
+            }
+            // ---- P, P-hat_b, dS, dS-hat (one 32x32 block per accumulator tile)
+            const bool overlap = q0 < kt0 + kTile;    // step meets the causal boundary
+            int pbc[2][4], dsc[2][4], es[2];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                float dsv[16];
+                float amax = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int qi = 32 * st + 8 * (i >> 2) + 4 * lg + (i & 3);
+                    const float x = sacc[st][i] * a.c1;
+                    float p = exp2_fast(x - sm.lse[qi]);
+                    if (overlap && key_loc > q0 + qi) p = 0.f;
+                    sacc[st][i] = p;
+                    const float d = p * (pacc[st][i] - sm.dv[qi]);
+                    dsv[i] = d;
+                    amax = fmaxf(amax, fabsf(d));
+                }
+                amax = wave_max(amax);
+                const int e = block_exponent(amax, -126);
+                es[st] = e + 127;
+                const float sc = __uint_as_float((uint32_t)(e + 127) << 23);   // 2^e
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pbc[st][j] = pack_fp8x4_div(sacc[st][4 * j], sacc[st][4 * j + 1], sacc[st][4 * j + 2],
+                                                sacc[st][4 * j + 3], inv256);
+                    dsc[st][j] = pack_fp8x4_div(dsv[4 * j], dsv[4 * j + 1], dsv[4 * j + 2], dsv[4 * j + 3], sc);
+                }
+            }
+            // ---- key-major copy of dS-hat for dQ, and the block exponents
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<int*>(&sm.st[(32 * wave + lr) * SSTR + 32 * st + 8 * j + 4 * lg]) = dsc[st][j];
+            if (lane == 0) { sm.es[0][wave] = es[0]; sm.es[1][wave] = es[1]; }
+
+            // ---- dV^T += dO^T P-hat_b and dK^T += Q^T dS-hat (contraction over the 64 queries)
+            {
+                const v8i pb = v8i{pbc[0][0], pbc[0][1], pbc[0][2], pbc[0][3], pbc[1][0], pbc[1][1], pbc[1][2], pbc[1][3]};
+                const v8i db = v8i{dsc[0][0], dsc[0][1], dsc[0][2], dsc[0][3], dsc[1][0], dsc[1][1], dsc[1][2], dsc[1][3]};
+                const int so = sm.eo[32 * lg], sq = sm.eq[32 * lg];
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    v2i r[4];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        r[rr] = lds_read_tr8(&sm.o[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                    const v8i oa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+                    dvt[dt] = mfma_mx(oa, pb, dvt[dt], so, 127 - 8);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        r[rr] = lds_read_tr8(&sm.q[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                    const v8i qa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+                    dkt[dt] = mfma_mx(qa, db, dkt[dt], sq, es[lg]);
+                }
+            }
+            __syncthreads();
+
+            // ---- dQ[query][d] = dS-hat K^ over the 128 keys; wave w -> query half w>>1
+            {
+                const int qsub = wave >> 1;
+                constexpr int DPW = DT / 2;                 // channel tiles per wave
+#pragma unroll
+                for (int u = 0; u < DPW; ++u) {
+                    const int dt = (wave & 1) * DPW + u;
+                    v16f acc = v16f{0};
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        v2i r[4];
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            r[rr] = lds_read_tr8(&sm.st[(64 * c + 16 * rr + tr_key) * SSTR + 32 * qsub + tr_col]);
+                        const v8i sa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            r[rr] = lds_read_tr8(&sm.k[(64 * c + 16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                        const v8i kbt = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+                        acc = mfma_mx(sa, kbt, acc, sm.es[qsub][2 * c + lg], sm.ek[64 * c + 32 * lg]);
+                    }
+                    float* dqp = a.dqacc + (long)h * D + 32 * dt + lr;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int ql = q0 + 32 * qsub + 8 * (i >> 2) + 4 * lg + (i & 3);
+                        if (ql < L) atomicAdd(dqp + (long)(ds + ql) * a.hq * D, acc[i]);
+                    }
+                }
+            }
+        }
+    }
+    // ---- epilogue: dK = softmax_scale * sum, dV; summed over the group's heads
+    if (key_valid) {
+        uint16_t* kp = a.dk + ((long)(ds + key_loc) * a.hkv + g) * D;
+        uint16_t* vp = a.dv + ((long)(ds + key_loc) * a.hkv + g) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int dd = 32 * dt + 8 * j + 4 * lg;
+                *reinterpret_cast<uint2*>(kp + dd) = make_uint2(
+                    f32_to_bf16(dkt[dt][4 * j] * a.scale) | (f32_to_bf16(dkt[dt][4 * j + 1] * a.scale) << 16),
+                    f32_to_bf16(dkt[dt][4 * j + 2] * a.scale) | (f32_to_bf16(dkt[dt][4 * j + 3] * a.scale) << 16));
+                *reinterpret_cast<uint2*>(vp + dd) = make_uint2(
+                    f32_to_bf16(dvt[dt][4 * j]) | (f32_to_bf16(dvt[dt][4 * j + 1]) << 16),
+                    f32_to_bf16(dvt[dt][4 * j + 2]) | (f32_to_bf16(dvt[dt][4 * j + 3]) << 16));
+            }
+    }
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int d, long grid, hipStream_t st) {
+    if (grid <= 0) return hipSuccess;
+    if (d == 64) hipLaunchKernelGGL(bwd_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(bwd_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace flamia

@@ -1,0 +1,109 @@
+// Internal device helpers of the HIP library (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+namespace flamia {
+
+// ---------------------------------------------------------------------------
+// Block-scaled FP8 MFMA, 32x32x64, E4M3 x E4M3 -> fp32.
+// Operand layout (measured on gfx950): lane l carries row (A) / column (B)
+// l % 32; bytes 0..15 of lanes l and l+32 form the first 32-element
+// contraction block, scaled by the UE8M0 byte of lane l % 32; bytes 16..31
+// form the second block, scaled by the byte of lane l % 32 + 32.  A and B use
+// the same (lane / 32, byte) -> k assignment.  Accumulator: lane l holds
+// column l % 32, rows 8*(i/4) + 4*(l/32) + i%4 for i = 0..15.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ v16f mfma_mx(v8i a, v8i b, v16f c, int scale_a, int scale_b) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
+// Transposed LDS read of 8-bit elements (ds_read_b64_tr_b8).  Within each
+// group of 16 lanes, lane s supplies the address of an 8-byte row R_s; lane j
+// receives byte i = R_{2i + (j%16)/8}[j % 8] for i = 0..7.
+__device__ __forceinline__ v2i lds_read_tr8(const uint8_t* lds_addr) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(v2i, const_cast<uint8_t*>(lds_addr)));
+}
+
+// Four fp32 -> four E4M3 bytes (byte i = element i), round to nearest even;
+// bit-identical to the format's definition for |x| <= 448.
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+// Same with an exact power-of-two divisor: byte i = E4M3(x_i / scale).
+__device__ __forceinline__ int pack_fp8x4_div(float a, float b, float c, float d, float scale) {
+    v2s w = v2s{0, 0};
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, scale, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, scale, true);
+    int out;
+    __builtin_memcpy(&out, &w, 4);
+    return out;
+}
+
+__device__ __forceinline__ float fp8_to_f32(uint32_t code) {
+    // E4M3 byte -> float, exact (subnormals 2^-9 m, normals 2^(E-7) (1 + m/8)).
+    const uint32_t s = code & 0x80u, e = (code >> 3) & 15u, m = code & 7u;
+    float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return s ? -v : v;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Shared exponent of a block with largest magnitude `amax` (fp32, >= 0):
+// the smallest e with amax <= 448 * 2^e ("rounded up", so no element of the
+// block saturates), clamped to [lo, 127]; amax == 0 gives lo.
+__device__ __forceinline__ int block_exponent(float amax, int lo) {
+    const uint32_t u = __float_as_uint(amax);
+    int E;
+    uint32_t frac;             // 23-bit fraction of amax normalised to [1, 2)
+    if (u == 0u) return lo;
+    const uint32_t ef = u >> 23;
+    if (ef != 0u) {
+        E = (int)ef - 127;
+        frac = u & 0x7FFFFFu;
+    } else {                   // fp32 subnormal: normalise the fraction
+        const int lz = __clz(u) - 8;          // leading zeros inside the 23-bit field + 1
+        E = -126 - lz;
+        frac = (u << lz) & 0x7FFFFFu;
+    }
+    // mantissa 1.f > 1.75  <=>  frac > 0.75 * 2^23
+    int e = E - 8 + (frac > 0x600000u ? 1 : 0);
+    e = e < lo ? lo : e;
+    return e > 127 ? 127 : e;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// Position of document `doc`'s boundaries; binary search of the largest
+// d with cu[d] <= t among [0, ndocs).
+__device__ __forceinline__ int find_doc(const int32_t* cu, int ndocs, int t) {
+    int lo = 0, hi = ndocs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace flamia

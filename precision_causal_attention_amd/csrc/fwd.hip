@@ -1,0 +1,215 @@
+// MXFP8 causal forward over packed documents (FLAMIA paper: Section 2
+// equations S = QK^T/sqrt(d), P = softmax(S), O = PV; Section 3.1 token-block
+// scales applied by the block-scaled product; Appendix B.1 P-hat = E4M3(2^c p)
+// with a conditional running maximum; Section 3.6.1 masking of keys outside
+// the document and of the causal boundary on the diagonal tile only).
+//
+// One workgroup = one work item (document, query head, 128-query tile
+// anchored at the document start); four waves, each owning 32 queries.
+// Per 128-key tile (ascending, anchored at the document start):
+//   S^T[key][query] = K^ Q^T      4 block-scaled MFMAs 32x32x64 per 64 channels
+//                                 (A = key rows from LDS, B = the wave's query rows
+//                                 kept in registers; the MFMA applies 2^(e_K + e_Q))
+//   x = S * softmax_scale * log2(e);  tile max -> conditional rescale (tau)
+//   p' = 2^(x - (m - c)) = 2^c p;  P-hat = E4M3(p')
+//   O^T[d][query] += V^T P-hat^T   A = V^T read from LDS with the transposing
+//                                 ds_read_b64_tr_b8, B = P-hat straight from the
+//                                 S^T accumulators (their layout is the operand
+//                                 layout), scale of each 32-key block of V.
+// The accumulator layout puts one query per lane column, so the online-softmax
+// statistics are per-lane scalars (plus one exchange between lane halves).
+#include "device.h"
+#include "kernels.h"
+
+namespace flamia {
+
+template <int D>
+struct FwdSmem {
+    static constexpr int kStride = D + 16;        // row pitch of a code tile in LDS (bank spread)
+    uint8_t k[kTile * kStride];
+    uint8_t v[kTile * kStride];
+    uint8_t ek[kTile];
+    uint8_t ev[kTile];
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
+    constexpr int KC = D / 64;                    // 64-channel contraction steps of S
+    constexpr int DT = D / 32;                    // 32-row channel tiles of O^T
+    constexpr int STR = FwdSmem<D>::kStride;
+    constexpr int CHUNKS = kTile * D / 16;        // 16-byte chunks of one code tile
+    __shared__ FwdSmem<D> sm;
+
+    if ((int)blockIdx.x >= *a.nitems) return;
+    const int4 it = a.items[blockIdx.x];
+    const int q0 = it.x, ds = it.y, de = it.z, h = it.w;
+    const int g = h / (a.hq / a.hkv);
+    const int L = de - ds;
+    const int lq0 = q0 - ds;
+    const int ntiles = lq0 / kTile + 1;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lg = lane >> 5, lr = lane & 31;
+    const int q_loc = lq0 + 32 * wave + lr;       // document-local query of this lane
+    const bool q_valid = q_loc < L;
+    const int q_row = ds + min(q_loc, L - 1);     // clamped row inside the document for loads
+
+    // The wave's 32 query rows as the B operand (column = query, k = channel):
+    // bytes 0..15 = channels 64kc + 16lg .. +16, bytes 16..31 = 64kc + 32 + 16lg .. +16.
+    v8i qb[KC];
+    {
+        const uint8_t* qp = a.qc + ((long)q_row * a.hq + h) * D;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * kc + 16 * lg);
+            const uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * kc + 32 + 16 * lg);
+            qb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+    }
+    const int eq = a.qs[(long)h * a.ttot + q_row];
+
+    v16f acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = v16f{0};
+    float m = -INFINITY;       // running maximum of x (retained until exceeded by > tau)
+    float l = 0.f;             // running sum of p' = 2^c p over this lane's keys
+
+    // transposed-read source address pattern (see lds_read_tr8): within the
+    // 16-lane group, source lane s points at key (s/2)-pattern, channel half s%2
+    const int s16 = lane & 15, grp = (lane >> 4) & 1;
+    const int tr_key = 8 * ((s16 >> 1) >> 2) + 4 * lg + ((s16 >> 1) & 3);
+    const int tr_col = 16 * grp + 8 * (s16 & 1);
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int k0 = ds + kTile * t;
+        // ---- cooperative load of the K^ and V^ code tiles and their scales
+        uint4 kr[CHUNKS / 256], vr[CHUNKS / 256];
+#pragma unroll
+        for (int r = 0; r < CHUNKS / 256; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+            const long krow = min(k0 + row, a.ttot - 1);
+            kr[r] = *reinterpret_cast<const uint4*>(a.kc + (krow * a.hkv + g) * D + col);
+            vr[r] = *reinterpret_cast<const uint4*>(a.vc + (krow * a.hkv + g) * D + col);
+        }
+        uint8_t ekr = 0, evr = 0;
+        if (tid < kTile) {
+            const long kt = min(k0 + tid, a.ttot - 1);
+            ekr = a.ks[(long)g * a.ttot + kt];
+            evr = a.vs[(long)g * a.ttot + kt];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < CHUNKS / 256; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+            *reinterpret_cast<uint4*>(&sm.k[row * STR + col]) = kr[r];
+            *reinterpret_cast<uint4*>(&sm.v[row * STR + col]) = vr[r];
+        }
+        if (tid < kTile) {
+            sm.ek[tid] = ekr;
+            sm.ev[tid] = evr;
+        }
+        __syncthreads();
+
+        // ---- S^T = K^ Q^T for the 4 sub-tiles of 32 keys
+        v16f s[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int row = 32 * kk + lr;
+            s[kk] = v16f{0};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const uint4 lo = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 16 * lg]);
+                const uint4 hi = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 32 + 16 * lg]);
+                const v8i ka = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                s[kk] = mfma_mx(ka, qb[kc], s[kk], sm.ek[row], eq);
+            }
+        }
+        // ---- scores in the base-2 domain; causal mask on the diagonal tile only
+        const bool diag = (t == ntiles - 1);
+        float mu = -INFINITY;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float x = s[kk][i] * a.c1;
+                if (diag) {
+                    const int key = kTile * t + 32 * kk + 8 * (i >> 2) + 4 * lg + (i & 3);
+                    if (key > q_loc) x = -INFINITY;
+                }
+                s[kk][i] = x;
+                mu = fmaxf(mu, x);
+            }
+        mu = fmaxf(mu, __shfl_xor(mu, 32, 64));
+        // ---- conditional running maximum (replace when exceeded by more than tau)
+        const float m_new = (m == -INFINITY || mu - m > a.tau) ? mu : m;
+        if (__any(m_new != m)) {
+            const float alpha = (m == -INFINITY) ? 0.f : exp2_fast(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+        }
+        m = m_new;
+        const float mc = m - a.c_log2;
+        // ---- p' = 2^c p and P-hat codes in operand byte order (byte i of a
+        // sub-tile = accumulator register i)
+        int pc[4][4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float p0 = exp2_fast(s[kk][4 * j] - mc), p1 = exp2_fast(s[kk][4 * j + 1] - mc);
+                const float p2 = exp2_fast(s[kk][4 * j + 2] - mc), p3 = exp2_fast(s[kk][4 * j + 3] - mc);
+                const int w = pack_fp8x4(p0, p1, p2, p3);
+                pc[kk][j] = w;
+                if (a.rowsum == 0) {
+                    l += (p0 + p1) + (p2 + p3);
+                } else {
+                    l += (fp8_to_f32(w & 0xFF) + fp8_to_f32((w >> 8) & 0xFF)) +
+                         (fp8_to_f32((w >> 16) & 0xFF) + fp8_to_f32((uint32_t)w >> 24));
+                }
+            }
+        // ---- O^T += V^T P-hat^T, two 64-key chunks
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const v8i pb = v8i{pc[2 * c][0], pc[2 * c][1], pc[2 * c][2], pc[2 * c][3],
+                               pc[2 * c + 1][0], pc[2 * c + 1][1], pc[2 * c + 1][2], pc[2 * c + 1][3]};
+            const int sv = sm.ev[64 * c + 32 * lg];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                v2i r[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    r[rr] = lds_read_tr8(&sm.v[(64 * c + 16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                const v8i va = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+                acc[dt] = mfma_mx(va, pb, acc[dt], sv, 127);
+            }
+        }
+    }
+    // ---- epilogue: O = acc / l (both carry the 2^c factor), lse2 = m + log2(l/2^c)
+    const float lt = l + __shfl_xor(l, 32, 64);
+    if (q_valid) {
+        const float inv = 1.f / lt;
+        uint16_t* op = a.o + ((long)(ds + q_loc) * a.hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t b0 = f32_to_bf16(acc[dt][4 * j] * inv), b1 = f32_to_bf16(acc[dt][4 * j + 1] * inv);
+                const uint32_t b2 = f32_to_bf16(acc[dt][4 * j + 2] * inv), b3 = f32_to_bf16(acc[dt][4 * j + 3] * inv);
+                *reinterpret_cast<uint2*>(op + 32 * dt + 8 * j + 4 * lg) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            }
+        if (lg == 0) a.lse2[(long)h * a.ttot + ds + q_loc] = m + (log2_fast(lt) - a.c_log2);
+    }
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int d, long grid, hipStream_t st) {
+    if (grid <= 0) return hipSuccess;
+    if (d == 64) hipLaunchKernelGGL(fwd_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(fwd_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace flamia

@@ -95,8 +95,16 @@ def cu_from_lengths(lens) -> np.ndarray:
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (nearest-even); return the uint16 patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.size >= (1 << 20):
+        import torch   # multi-threaded conversion of large inputs, same rounding
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)   # finite: no uint32 overflow below
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    u += r
+    u >>= 16
     return u.astype(np.uint16)
 
 

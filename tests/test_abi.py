@@ -1,0 +1,94 @@
+"""The C-ABI library loads, exports every function include/flamia.h declares,
+and rejects invalid arguments on the host before anything is launched (these
+calls never reach the GPU, so they run without one)."""
+import ctypes
+import subprocess
+
+import pytest
+
+from precision_causal_attention_amd import flamia as F
+
+
+@pytest.fixture(scope="module")
+def L():
+    return F.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = F.header_functions()
+    assert {"flamia_fwd", "flamia_bwd", "flamia_quantize", "flamia_workspace_bytes"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", F.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_version_and_defaults(L):
+    assert F.flamia_abi_version() == 1
+    o = F.flamia_default_opts()
+    assert (o.c_log2, o.tau, o.key_tile, o.rowsum) == (4, 4, 128, 0)
+    assert F.flamia_status_str(0) == "ok"
+
+
+def dims(**kw):
+    base = dict(ttot=1024, ttot_cap=1024, ndocs=3, ndocs_cap=8, hq=8, hkv=2, d=64)
+    base.update(kw)
+    return F.Dims(*[base[k] for k in ("ttot", "ttot_cap", "ndocs", "ndocs_cap", "hq", "hkv", "d")])
+
+
+def test_workspace_depends_on_capacity_only():
+    a = F.flamia_workspace_bytes(dims(ttot=100, ndocs=1))
+    b = F.flamia_workspace_bytes(dims(ttot=1000, ndocs=7))
+    assert a == b > 0
+    assert F.flamia_workspace_bytes(dims(ttot_cap=2048)) > a
+    assert F.flamia_workspace_bytes(dims(d=96)) == 0
+
+
+FAKE = 1 << 20   # aligned non-null host integer, never dereferenced: validation fails first
+
+
+def call_fwd(dm, opts=None, ws_bytes=None, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, o=FAKE, lse=FAKE, ws=FAKE)
+    args.update(over)
+    mx = (FAKE, FAKE)
+    wsb = F.flamia_workspace_bytes(dims()) if ws_bytes is None else ws_bytes
+    return F.flamia_fwd(dm, opts, args["q"], args["k"], args["v"], args["cu"], mx, mx, mx,
+                        args["o"], args["lse"], args["ws"], wsb, stream=0, check=False)
+
+
+def call_bwd(dm, opts=None, ws_bytes=None, **over):
+    args = dict(do=FAKE, o=FAKE, lse=FAKE, cu=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE)
+    args.update(over)
+    mx = (FAKE, FAKE)
+    wsb = F.flamia_workspace_bytes(dims()) if ws_bytes is None else ws_bytes
+    return F.flamia_bwd(dm, opts, args["do"], args["o"], args["lse"], args["cu"], mx, mx, mx,
+                        args["dq"], args["dk"], args["dv"], args["ws"], wsb, stream=0, check=False)
+
+
+@pytest.mark.parametrize("call", [call_fwd, call_bwd])
+def test_invalid_arguments_return_status(call):
+    bad_opts = F.flamia_default_opts()
+    bad_opts.c_log2, bad_opts.tau = 8, 2          # 2^(c+tau) = 1024 > 448
+    tile_opts = F.flamia_default_opts()
+    tile_opts.key_tile = 64
+    assert call(dims(d=96)) == 2                  # FLAMIA_ERR_SHAPE
+    assert call(dims(hq=6, hkv=4)) == 2
+    assert call(dims(ttot=4096)) == 2             # beyond capacity
+    assert call(dims(ndocs=0)) == 2
+    assert call(dims(), opts=bad_opts) == 4       # FLAMIA_ERR_OPTS
+    assert call(dims(), opts=tile_opts) == 4
+    assert call(dims(), ws_bytes=100) == 5        # FLAMIA_ERR_WORKSPACE
+    assert call(dims(), ws=0) == 5                # NULL workspace is a workspace error (flamia.h)
+    assert call(dims(), cu=0) == 1                # FLAMIA_ERR_NULL
+    assert call(dims(), o=FAKE + 4) == 3          # FLAMIA_ERR_ALIGN
+
+
+def test_quantize_validation():
+    dm = dims()
+    mx = (FAKE, FAKE)
+    assert F.flamia_quantize(dm, 0, FAKE, FAKE, mx, stream=0, check=False) == 2
+    assert F.flamia_quantize(dm, 2, 0, FAKE, mx, stream=0, check=False) == 1
+    assert F.flamia_quantize(dm, 2, FAKE + 2, FAKE, mx, stream=0, check=False) == 3
+    assert F.flamia_quantize(dims(d=32), 2, FAKE, FAKE, mx, stream=0, check=False) == 2
