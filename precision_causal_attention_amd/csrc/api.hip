@@ -74,7 +74,9 @@ Layout layout(const flamia_dims_t* d) {
     w.ocodes = off;  off += up256((size_t)tc * d->hq * d->d);
     w.oscales = off; off += up256((size_t)tc * d->hq);
     w.dvec = off;    off += up256(sizeof(float) * (size_t)tc * d->hq);
-    w.dqacc = off;   off += up256(sizeof(float) * (size_t)tc * d->hq * d->d);
+    // fp32 dQ accumulator plus 64 rows of slack that absorb the zero
+    // contributions of query rows past the last document's end
+    w.dqacc = off;   off += up256(sizeof(float) * ((size_t)tc + 64) * d->hq * d->d);
     w.total = off;
     return w;
 }

@@ -38,8 +38,8 @@ struct BwdSmem {
     uint8_t o[kQStep * kStride];                 // quantized dO
     uint8_t k[kTile * kStride];
     uint8_t st[kTile * kSStride];                // dS-hat, [key][query]
-    float lse[kQStep];
-    float dv[kQStep];                            // D
+    alignas(16) float lse[kQStep];
+    alignas(16) float dv[kQStep];                // D
     uint8_t eq[kQStep];
     uint8_t eo[kQStep];
     uint8_t ek[kTile];
@@ -47,12 +47,12 @@ struct BwdSmem {
 };
 
 template <int D>
-__global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs a) {
     constexpr int KC = D / 64;
     constexpr int DT = D / 32;
     constexpr int STR = BwdSmem<D>::kStride;
     constexpr int SSTR = BwdSmem<D>::kSStride;
-    constexpr int QCH = kQStep * D / 16;          // 16-byte chunks of a 64-row code tile
+    constexpr int NQ = kQStep * D / 16 / 256;     // 16-byte chunks per thread of a 64-row code tile
     constexpr int KCH = kTile * D / 16;
     __shared__ BwdSmem<D> sm;
 
@@ -67,6 +67,50 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdArgs a) {
     const int key_loc = kt0 + 32 * wave + lr;
     const bool key_valid = key_loc < L;
     const int key_row = ds + min(key_loc, L - 1);
+
+    // ---- staging of one 64-query step (prefetched into registers one step ahead)
+    uint4 pq[NQ], po[NQ];
+    uint32_t p_eq = 0, p_eo = 0;
+    float p_lse = 0.f, p_dv = 0.f;
+    bool p_in = true;
+    auto load_step = [&](int h, int q0) {
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+            const long qr = ds + min(q0 + row, L - 1);
+            pq[r] = *reinterpret_cast<const uint4*>(a.qc + (qr * a.hq + h) * D + col);
+            po[r] = *reinterpret_cast<const uint4*>(a.oc + (qr * a.hq + h) * D + col);
+        }
+        // Every thread issues the same loads (rows clamped into the document),
+        // so the number of outstanding memory operations is static and the
+        // wait for this prefetch never has to drain the dQ atomics issued after it.
+        {
+            const int ql = q0 + (tid & (kQStep - 1));
+            const long qr = ds + min(ql, L - 1);
+            p_eq = a.qs[(long)h * a.ttot + qr];
+            p_eo = a.os[(long)h * a.ttot + qr];
+            p_lse = a.lse2[(long)h * a.ttot + qr];
+            p_in = ql < L;
+            p_dv = a.dvec[(long)h * a.ttot + qr];
+        }
+    };
+    auto store_step = [&]() {
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+            *reinterpret_cast<uint4*>(&sm.q[row * STR + col]) = pq[r];
+            *reinterpret_cast<uint4*>(&sm.o[row * STR + col]) = po[r];
+        }
+        if (tid < kQStep) {
+            sm.eq[tid] = (uint8_t)p_eq;
+            sm.eo[tid] = (uint8_t)p_eo;
+            sm.lse[tid] = p_in ? p_lse : INFINITY;   // +inf: row outside the document
+            sm.dv[tid] = p_dv;
+        }
+    };
+    load_step(g * G, kt0);
 
     // The wave's key rows as B operands of S and dP (column = key, k = channel).
     v8i kb[KC], vb[KC];
@@ -103,135 +147,138 @@ __global__ void __launch_bounds__(256, 1) bwd_kernel(const BwdArgs a) {
     const int tr_col = 16 * grp + 8 * (s16 & 1);
     const float inv256 = 1.f / 256.f;
 
-    for (int hh = 0; hh < G; ++hh) {
+    int hh = 0, q0 = kt0;
+    for (;;) {
+        // ---- publish the prefetched step in LDS, start fetching the next one
+        __syncthreads();
+        store_step();
+        __syncthreads();
         const int h = g * G + hh;
-        for (int q0 = kt0; q0 < L; q0 += kQStep) {
-            // ---- stage the 64-query step: codes, scales, lse2 (+inf past the document), D
-            __syncthreads();
-            for (int c = tid; c < QCH; c += 256) {
-                const int row = c / (D / 16), col = (c % (D / 16)) * 16;
-                const long qr = ds + min(q0 + row, L - 1);
-                *reinterpret_cast<uint4*>(&sm.q[row * STR + col]) = *reinterpret_cast<const uint4*>(a.qc + (qr * a.hq + h) * D + col);
-                *reinterpret_cast<uint4*>(&sm.o[row * STR + col]) = *reinterpret_cast<const uint4*>(a.oc + (qr * a.hq + h) * D + col);
-            }
-            if (tid < kQStep) {
-                const int ql = q0 + tid;
-                const long qr = ds + min(ql, L - 1);
-                sm.eq[tid] = a.qs[(long)h * a.ttot + qr];
-                sm.eo[tid] = a.os[(long)h * a.ttot + qr];
-                sm.lse[tid] = ql < L ? a.lse2[(long)h * a.ttot + qr] : INFINITY;
-                sm.dv[tid] = a.dvec[(long)h * a.ttot + qr];
-            }
-            __syncthreads();
+        const int qs0 = q0;
+        q0 += kQStep;
+        if (q0 >= L) { q0 = kt0; ++hh; }
+        const bool more = hh < G;
+        if (more) load_step(g * G + hh, q0);
 
-            // ---- S and dP for the wave's 32 keys x 64 queries
-            v16f sacc[2], pacc[2];
+        // ---- S and dP for the wave's 32 keys x 64 queries
+        v16f sacc[2], pacc[2];
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const int row = 32 * st + lr;
-                sacc[st] = v16f{0};
-                pacc[st] = v16f{0};
+        for (int st = 0; st < 2; ++st) {
+            const int row = 32 * st + lr;
+            sacc[st] = v16f{0};
+            pacc[st] = v16f{0};
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    uint4 lo = *reinterpret_cast<const uint4*>(&sm.q[row * STR + 64 * kc + 16 * lg]);
-                    uint4 hi = *reinterpret_cast<const uint4*>(&sm.q[row * STR + 64 * kc + 32 + 16 * lg]);
-                    const v8i qa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    sacc[st] = mfma_mx(qa, kb[kc], sacc[st], sm.eq[row], ek);
-                    lo = *reinterpret_cast<const uint4*>(&sm.o[row * STR + 64 * kc + 16 * lg]);
-                    hi = *reinterpret_cast<const uint4*>(&sm.o[row * STR + 64 * kc + 32 + 16 * lg]);
-                    const v8i oa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    pacc[st] = mfma_mx(oa, vb[kc], pacc[st], sm.eo[row], ev);
-                }
+            for (int kc = 0; kc < KC; ++kc) {
+                uint4 lo = *reinterpret_cast<const uint4*>(&sm.q[row * STR + 64 * kc + 16 * lg]);
+                uint4 hi = *reinterpret_cast<const uint4*>(&sm.q[row * STR + 64 * kc + 32 + 16 * lg]);
+                const v8i qa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                sacc[st] = mfma_mx(qa, kb[kc], sacc[st], sm.eq[row], ek);
+                lo = *reinterpret_cast<const uint4*>(&sm.o[row * STR + 64 * kc + 16 * lg]);
+                hi = *reinterpret_cast<const uint4*>(&sm.o[row * STR + 64 * kc + 32 + 16 * lg]);
+                const v8i oa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                pacc[st] = mfma_mx(oa, vb[kc], pacc[st], sm.eo[row], ev);
             }
-            // ---- P, P-hat_b, dS, dS-hat (one 32x32 block per accumulator tile)
-            const bool overlap = q0 < kt0 + kTile;    // step meets the causal boundary
-            int pbc[2][4], dsc[2][4], es[2];
+        }
+        // ---- P, P-hat_b, dS, dS-hat (one 32x32 block per accumulator tile)
+        const bool overlap = qs0 < kt0 + kTile;    // step meets the causal boundary
+        int pbc[2][4], dsc[2][4], es[2];
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                float dsv[16];
-                float amax = 0.f;
+        for (int st = 0; st < 2; ++st) {
+            float dsv[16];
+            float amax = 0.f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int qi = 32 * st + 8 * (i >> 2) + 4 * lg + (i & 3);
-                    const float x = sacc[st][i] * a.c1;
-                    float p = exp2_fast(x - sm.lse[qi]);
-                    if (overlap && key_loc > q0 + qi) p = 0.f;
+            for (int j = 0; j < 4; ++j) {
+                const int q4 = 32 * st + 8 * j + 4 * lg;            // 4 consecutive query rows
+                const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse[q4]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&sm.dv[q4]);
+                const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * j + r;
+                    float p = exp2_fast(fmaf(sacc[st][i], a.c1, -lq[r]));
+                    if (overlap && key_loc > qs0 + q4 + r) p = 0.f;
                     sacc[st][i] = p;
-                    const float d = p * (pacc[st][i] - sm.dv[qi]);
-                    dsv[i] = d;
-                    amax = fmaxf(amax, fabsf(d));
-                }
-                amax = wave_max(amax);
-                const int e = block_exponent(amax, -126);
-                es[st] = e + 127;
-                const float sc = __uint_as_float((uint32_t)(e + 127) << 23);   // 2^e
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pbc[st][j] = pack_fp8x4_div(sacc[st][4 * j], sacc[st][4 * j + 1], sacc[st][4 * j + 2],
-                                                sacc[st][4 * j + 3], inv256);
-                    dsc[st][j] = pack_fp8x4_div(dsv[4 * j], dsv[4 * j + 1], dsv[4 * j + 2], dsv[4 * j + 3], sc);
+                    const float dsi = p * (pacc[st][i] - dq[r]);
+                    dsv[i] = dsi;
+                    amax = fmaxf(amax, fabsf(dsi));
                 }
             }
-            // ---- key-major copy of dS-hat for dQ, and the block exponents
+            amax = wave_max(amax);
+            const int e = block_exponent(amax, -126);
+            es[st] = e + 127;
+            const float sc = __uint_as_float((uint32_t)(e + 127) << 23);   // 2^e
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int j = 0; j < 4; ++j) {
+                pbc[st][j] = pack_fp8x4_div(sacc[st][4 * j], sacc[st][4 * j + 1], sacc[st][4 * j + 2],
+                                            sacc[st][4 * j + 3], inv256);
+                dsc[st][j] = pack_fp8x4_div(dsv[4 * j], dsv[4 * j + 1], dsv[4 * j + 2], dsv[4 * j + 3], sc);
+            }
+        }
+        // ---- key-major copy of dS-hat for dQ, and the block exponents
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<int*>(&sm.st[(32 * wave + lr) * SSTR + 32 * st + 8 * j + 4 * lg]) = dsc[st][j];
-            if (lane == 0) { sm.es[0][wave] = es[0]; sm.es[1][wave] = es[1]; }
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<int*>(&sm.st[(32 * wave + lr) * SSTR + 32 * st + 8 * j + 4 * lg]) = dsc[st][j];
+        if (lane == 0) { sm.es[0][wave] = es[0]; sm.es[1][wave] = es[1]; }
 
-            // ---- dV^T += dO^T P-hat_b and dK^T += Q^T dS-hat (contraction over the 64 queries)
-            {
-                const v8i pb = v8i{pbc[0][0], pbc[0][1], pbc[0][2], pbc[0][3], pbc[1][0], pbc[1][1], pbc[1][2], pbc[1][3]};
-                const v8i db = v8i{dsc[0][0], dsc[0][1], dsc[0][2], dsc[0][3], dsc[1][0], dsc[1][1], dsc[1][2], dsc[1][3]};
-                const int so = sm.eo[32 * lg], sq = sm.eq[32 * lg];
+        // ---- dV^T += dO^T P-hat_b and dK^T += Q^T dS-hat (contraction over the 64 queries)
+        {
+            const v8i pb = v8i{pbc[0][0], pbc[0][1], pbc[0][2], pbc[0][3], pbc[1][0], pbc[1][1], pbc[1][2], pbc[1][3]};
+            const v8i db = v8i{dsc[0][0], dsc[0][1], dsc[0][2], dsc[0][3], dsc[1][0], dsc[1][1], dsc[1][2], dsc[1][3]};
+            const int so = sm.eo[32 * lg], sq = sm.eq[32 * lg];
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
+            for (int dt = 0; dt < DT; ++dt) {
+                v2i r[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    r[rr] = lds_read_tr8(&sm.o[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                const v8i oa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+                dvt[dt] = mfma_mx(oa, pb, dvt[dt], so, 127 - 8);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    r[rr] = lds_read_tr8(&sm.q[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                const v8i qa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+                dkt[dt] = mfma_mx(qa, db, dkt[dt], sq, es[lg]);
+            }
+        }
+        __syncthreads();
+
+        // ---- dQ[query][d] = dS-hat K^ over the 128 keys; wave w -> query half w>>1
+        {
+            const int qsub = wave >> 1;
+            constexpr int DPW = DT / 2;                 // channel tiles per wave
+#pragma unroll
+            for (int u = 0; u < DPW; ++u) {
+                const int dt = (wave & 1) * DPW + u;
+                v16f acc = v16f{0};
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
                     v2i r[4];
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        r[rr] = lds_read_tr8(&sm.o[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
-                    const v8i oa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
-                    dvt[dt] = mfma_mx(oa, pb, dvt[dt], so, 127 - 8);
+                        r[rr] = lds_read_tr8(&sm.st[(64 * c + 16 * rr + tr_key) * SSTR + 32 * qsub + tr_col]);
+                    const v8i sa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        r[rr] = lds_read_tr8(&sm.q[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
-                    const v8i qa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
-                    dkt[dt] = mfma_mx(qa, db, dkt[dt], sq, es[lg]);
+                        r[rr] = lds_read_tr8(&sm.k[(64 * c + 16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                    const v8i kbt = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+                    acc = mfma_mx(sa, kbt, acc, sm.es[qsub][2 * c + lg], sm.ek[64 * c + 32 * lg]);
                 }
-            }
-            __syncthreads();
-
-            // ---- dQ[query][d] = dS-hat K^ over the 128 keys; wave w -> query half w>>1
-            {
-                const int qsub = wave >> 1;
-                constexpr int DPW = DT / 2;                 // channel tiles per wave
+                // Rows past the document end hold exact zeros (P = 0 there):
+                // they are added, as zeros, to the rows that follow (the next
+                // document's, or the accumulator's 64-row slack past the last
+                // token), so all 16 atomics are issued unconditionally and no
+                // address is shared by the padding of different items.
+                float* dqp = a.dqacc + (long)h * D + 32 * dt + lr;
 #pragma unroll
-                for (int u = 0; u < DPW; ++u) {
-                    const int dt = (wave & 1) * DPW + u;
-                    v16f acc = v16f{0};
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        v2i r[4];
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr)
-                            r[rr] = lds_read_tr8(&sm.st[(64 * c + 16 * rr + tr_key) * SSTR + 32 * qsub + tr_col]);
-                        const v8i sa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr)
-                            r[rr] = lds_read_tr8(&sm.k[(64 * c + 16 * rr + tr_key) * STR + 32 * dt + tr_col]);
-                        const v8i kbt = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
-                        acc = mfma_mx(sa, kbt, acc, sm.es[qsub][2 * c + lg], sm.ek[64 * c + 32 * lg]);
-                    }
-                    float* dqp = a.dqacc + (long)h * D + 32 * dt + lr;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int ql = q0 + 32 * qsub + 8 * (i >> 2) + 4 * lg + (i & 3);
-                        if (ql < L) atomicAdd(dqp + (long)(ds + ql) * a.hq * D, acc[i]);
-                    }
+                for (int i = 0; i < 16; ++i) {
+                    const int ql = qs0 + 32 * qsub + 8 * (i >> 2) + 4 * lg + (i & 3);
+                    atomicAdd(dqp + (long)(ds + ql) * a.hq * D, ql < L ? acc[i] : 0.f);
                 }
             }
         }
+        if (!more) break;
     }
     // ---- epilogue: dK = softmax_scale * sum, dV; summed over the group's heads
     if (key_valid) {

@@ -90,9 +90,34 @@ __device__ __forceinline__ int block_exponent(float amax, int lo) {
     return e > 127 ? 127 : e;
 }
 
+// Lane exchange without the LDS crossbar: DPP within 16-lane rows, then
+// v_permlane16_swap / v_permlane32_swap across rows.  Each swap returns the
+// pair {own value, partner value} (order depends on the lane), so a
+// commutative combine of the two halves gives the same result in both lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max_xor16(float v) {      // rows 0<->1, 2<->3
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {      // lanes l <-> l ^ 32
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Maximum over all 64 lanes, returned in every lane.
 __device__ __forceinline__ float wave_max(float v) {
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    v = fmaxf(v, dpp<0xB1>(v));     // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp<0x4E>(v));     // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp<0x141>(v));    // row_half_mirror: the two quads of each 8
+    v = fmaxf(v, dpp<0x140>(v));    // row_mirror: the two halves of each 16
+    v = max_xor16(v);
+    return max_xor32(v);
 }
 
 // Position of document `doc`'s boundaries; binary search of the largest

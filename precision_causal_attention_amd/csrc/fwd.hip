@@ -79,10 +79,11 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
     const int tr_key = 8 * ((s16 >> 1) >> 2) + 4 * lg + ((s16 >> 1) & 3);
     const int tr_col = 16 * grp + 8 * (s16 & 1);
 
-    for (int t = 0; t < ntiles; ++t) {
+    // ---- K^/V^ code tiles and scales, prefetched into registers one tile ahead
+    uint4 kr[CHUNKS / 256], vr[CHUNKS / 256];
+    uint32_t ekr = 0, evr = 0;
+    auto load_tile = [&](int t) {
         const int k0 = ds + kTile * t;
-        // ---- cooperative load of the K^ and V^ code tiles and their scales
-        uint4 kr[CHUNKS / 256], vr[CHUNKS / 256];
 #pragma unroll
         for (int r = 0; r < CHUNKS / 256; ++r) {
             const int c = tid + 256 * r;
@@ -91,12 +92,15 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
             kr[r] = *reinterpret_cast<const uint4*>(a.kc + (krow * a.hkv + g) * D + col);
             vr[r] = *reinterpret_cast<const uint4*>(a.vc + (krow * a.hkv + g) * D + col);
         }
-        uint8_t ekr = 0, evr = 0;
         if (tid < kTile) {
             const long kt = min(k0 + tid, a.ttot - 1);
             ekr = a.ks[(long)g * a.ttot + kt];
             evr = a.vs[(long)g * a.ttot + kt];
         }
+    };
+    load_tile(0);
+
+    for (int t = 0; t < ntiles; ++t) {
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < CHUNKS / 256; ++r) {
@@ -106,10 +110,11 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
             *reinterpret_cast<uint4*>(&sm.v[row * STR + col]) = vr[r];
         }
         if (tid < kTile) {
-            sm.ek[tid] = ekr;
-            sm.ev[tid] = evr;
+            sm.ek[tid] = (uint8_t)ekr;
+            sm.ev[tid] = (uint8_t)evr;
         }
         __syncthreads();
+        if (t + 1 < ntiles) load_tile(t + 1);
 
         // ---- S^T = K^ Q^T for the 4 sub-tiles of 32 keys
         v16f s[4];
@@ -125,22 +130,21 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
                 s[kk] = mfma_mx(ka, qb[kc], s[kk], sm.ek[row], eq);
             }
         }
-        // ---- scores in the base-2 domain; causal mask on the diagonal tile only
+        // ---- causal mask on the diagonal tile only; tile maximum on the raw
+        // scores (rounding is monotonic, so max(S) * c1 = max(S * c1) exactly)
         const bool diag = (t == ntiles - 1);
-        float mu = -INFINITY;
+        float smax = -INFINITY;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float x = s[kk][i] * a.c1;
                 if (diag) {
                     const int key = kTile * t + 32 * kk + 8 * (i >> 2) + 4 * lg + (i & 3);
-                    if (key > q_loc) x = -INFINITY;
+                    if (key > q_loc) s[kk][i] = -INFINITY;
                 }
-                s[kk][i] = x;
-                mu = fmaxf(mu, x);
+                smax = fmaxf(smax, s[kk][i]);
             }
-        mu = fmaxf(mu, __shfl_xor(mu, 32, 64));
+        const float mu = max_xor32(smax) * a.c1;
         // ---- conditional running maximum (replace when exceeded by more than tau)
         const float m_new = (m == -INFINITY || mu - m > a.tau) ? mu : m;
         if (__any(m_new != m)) {
@@ -152,7 +156,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
                 for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
         }
         m = m_new;
-        const float mc = m - a.c_log2;
+        const float nmc = a.c_log2 - m;                 // p' = 2^(x - m + c)
         // ---- p' = 2^c p and P-hat codes in operand byte order (byte i of a
         // sub-tile = accumulator register i)
         int pc[4][4];
@@ -160,8 +164,10 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float p0 = exp2_fast(s[kk][4 * j] - mc), p1 = exp2_fast(s[kk][4 * j + 1] - mc);
-                const float p2 = exp2_fast(s[kk][4 * j + 2] - mc), p3 = exp2_fast(s[kk][4 * j + 3] - mc);
+                const float p0 = exp2_fast(fmaf(s[kk][4 * j], a.c1, nmc));
+                const float p1 = exp2_fast(fmaf(s[kk][4 * j + 1], a.c1, nmc));
+                const float p2 = exp2_fast(fmaf(s[kk][4 * j + 2], a.c1, nmc));
+                const float p3 = exp2_fast(fmaf(s[kk][4 * j + 3], a.c1, nmc));
                 const int w = pack_fp8x4(p0, p1, p2, p3);
                 pc[kk][j] = w;
                 if (a.rowsum == 0) {
@@ -189,7 +195,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
         }
     }
     // ---- epilogue: O = acc / l (both carry the 2^c factor), lse2 = m + log2(l/2^c)
-    const float lt = l + __shfl_xor(l, 32, 64);
+    const float lt = add_xor32(l);
     if (q_valid) {
         const float inv = 1.f / lt;
         uint16_t* op = a.o + ((long)(ds + q_loc) * a.hq + h) * D;
