@@ -1,12 +1,13 @@
 """Benchmark of the MXFP8 causal packed-document training call on one MI355X.
 
 One step = flamia_fwd (quantize Q/K/V, work list, forward kernel) followed by
-flamia_bwd (quantize dO with D and the dQ clear, work list, backward kernel,
-dQ finalize) on one seeded synthetic batch already resident in HBM.
+flamia_bwd (quantize dO with D, work lists, key-major dK/dV kernel,
+query-major dQ kernel) on one seeded synthetic batch already resident in HBM.
 
 Prints ONE JSON line:
   value     whole-call throughput, FLOP = 7 * Hq * d * sum(L^2) (forward 2
-            products x 2d x L^2/2 causal pairs, backward 2.5x the forward)
+            products x 2d x L^2/2 causal pairs, backward 2.5x the forward;
+            the recomputed score products of the dQ pass earn no credit)
   roofline  the dominant kernel's algorithmic FLOP per launch divided by its
             average duration, measured with HIP events recorded by the library
             on the launch stream around each internal launch
@@ -26,7 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd+bwd causal attention TFLOP/s incl. quant (MXFP8, packed docs), % of roofline"
 MXFP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8/MXFP8 MFMA peak (AMD specification)
 FWD_PHASES = ["quantize_q", "quantize_k", "quantize_v", "worklist_fwd", "fwd_kernel"]
-BWD_PHASES = ["quantize_do", "worklist_bwd", "bwd_kernel", "dq_finalize"]
+BWD_PHASES = ["quantize_do", "worklist_bwd", "dkv_kernel", "dq_kernel"]
 
 
 def log(*a):
@@ -159,7 +160,10 @@ def main():
     sum_l2 = inst["sum_L2"]
     flop = 7.0 * hq * d * sum_l2
     tflops = flop / (ms_step * 1e-3) / 1e12
-    kflop = {"fwd_kernel": 2.0 * hq * d * sum_l2, "bwd_kernel": 5.0 * hq * d * sum_l2}
+    # algorithmic FLOP of each kernel (products x 2d x L^2/2 causal pairs per head):
+    # forward S and PV; dK/dV pass S, dP, dV, dK; dQ pass S, dP, dQ
+    kflop = {"fwd_kernel": 2.0 * hq * d * sum_l2, "dkv_kernel": 4.0 * hq * d * sum_l2,
+             "dq_kernel": 3.0 * hq * d * sum_l2}
     dom = max(kflop, key=lambda n: phases[n])
     achieved = kflop[dom] / (phases[dom] * 1e-3) / 1e12
     result = {

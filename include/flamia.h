@@ -83,8 +83,8 @@ typedef struct {
      * event i on `stream` before its i-th internal launch and the next one
      * after its last launch, as far as n_events allows.  flamia_fwd has 5
      * phases (quantize Q, K, V; work list; forward kernel), flamia_bwd 4
-     * (quantize dO with D and the dQ clear; work list; backward kernel; dQ
-     * finalize).  NULL disables it. */
+     * (quantize dO with D; work lists; key-major dK/dV kernel; query-major dQ
+     * kernel).  NULL disables it. */
     void **phase_events;
     int32_t n_events;
 } flamia_opts_t;
@@ -150,10 +150,11 @@ flamia_status_t flamia_fwd(const flamia_dims_t *dims, const flamia_opts_t *opts,
  *   dq                 : bf16 output [ttot][hq][d]
  *   dk, dv             : bf16 outputs [ttot][hkv][d] (summed over the query
  *                        heads of each group)
- *   ws / ws_bytes      : workspace (holds the dO codes, D and the fp32 dQ
- *                        accumulator)
- * dQ is accumulated with fp32 atomics, so its last bits may vary run to run;
- * dK and dV are deterministic.
+ *   ws / ws_bytes      : workspace (holds the dO codes and scales, D and the
+ *                        work lists)
+ * Two passes rebuild the same dS-hat payload: a key-major pass accumulates dK
+ * and dV, a query-major pass accumulates dQ; each output element is owned by
+ * one workgroup, so the backward is deterministic (no atomics).
  */
 flamia_status_t flamia_bwd(const flamia_dims_t *dims, const flamia_opts_t *opts,
                            const uint16_t *d_o, const uint16_t *o, const float *lse2,

@@ -58,7 +58,7 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Layout {
     long max_tiles, max_items;
     int max_cost;
-    size_t ctrl, prefix, items, ocodes, oscales, dvec, dqacc, total;
+    size_t ctrl, prefix, items_q, items_k, ocodes, oscales, dvec, total;
 };
 
 Layout layout(const flamia_dims_t* d) {
@@ -66,17 +66,15 @@ Layout layout(const flamia_dims_t* d) {
     const long tc = d->ttot_cap;
     w.max_cost = (int)((tc + kTile - 1) / kTile) + 1;
     w.max_tiles = tc / kTile + d->ndocs_cap + 1;
-    w.max_items = w.max_tiles * (d->hq > d->hkv ? d->hq : d->hkv);
+    w.max_items = w.max_tiles * (d->hq + d->hkv);
     size_t off = 0;
-    w.ctrl = off;    off += up256(sizeof(int32_t) * (16 + 2 * (size_t)(w.max_cost + 1)));
+    w.ctrl = off;    off += up256(sizeof(int32_t) * (16 + 3 * (size_t)(w.max_cost + 1)));
     w.prefix = off;  off += up256(sizeof(int32_t) * ((size_t)d->ndocs_cap + 1));
-    w.items = off;   off += up256(sizeof(int4) * (size_t)w.max_items);
+    w.items_q = off; off += up256(sizeof(int4) * (size_t)w.max_tiles * d->hq);
+    w.items_k = off; off += up256(sizeof(int4) * (size_t)w.max_tiles * d->hkv);
     w.ocodes = off;  off += up256((size_t)tc * d->hq * d->d);
     w.oscales = off; off += up256((size_t)tc * d->hq);
     w.dvec = off;    off += up256(sizeof(float) * (size_t)tc * d->hq);
-    // fp32 dQ accumulator plus 64 rows of slack that absorb the zero
-    // contributions of query rows past the last document's end
-    w.dqacc = off;   off += up256(sizeof(float) * ((size_t)tc + 64) * d->hq * d->d);
     w.total = off;
     return w;
 }
@@ -146,7 +144,7 @@ flamia_status_t flamia_quantize(const flamia_dims_t* dims, int32_t heads, const 
     if (heads <= 0) return FLAMIA_ERR_SHAPE;
     if (!x || !cu_seqlens || !out.codes || !out.scales) return FLAMIA_ERR_NULL;
     if (!aligned16(x) || !aligned16(out.codes)) return FLAMIA_ERR_ALIGN;
-    QuantArgs a{x, cu_seqlens, dims->ndocs, dims->ttot, heads, dims->d, out.codes, out.scales, nullptr, nullptr, nullptr};
+    QuantArgs a{x, cu_seqlens, dims->ndocs, dims->ttot, heads, dims->d, out.codes, out.scales, nullptr, nullptr};
     hipError_t e = launch_quantize(a, (hipStream_t)stream);
     return e == hipSuccess ? FLAMIA_OK : hip_fail(e);
 }
@@ -176,18 +174,18 @@ flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
 
     // fused quantization of the three operands (Section 3.5.1)
     const QuantArgs qa[3] = {
-        {q, cu_seqlens, dims->ndocs, dims->ttot, dims->hq, d, q_mx.codes, q_mx.scales, nullptr, nullptr, nullptr},
-        {k, cu_seqlens, dims->ndocs, dims->ttot, dims->hkv, d, k_mx.codes, k_mx.scales, nullptr, nullptr, nullptr},
-        {v, cu_seqlens, dims->ndocs, dims->ttot, dims->hkv, d, v_mx.codes, v_mx.scales, nullptr, nullptr, nullptr}};
+        {q, cu_seqlens, dims->ndocs, dims->ttot, dims->hq, d, q_mx.codes, q_mx.scales, nullptr, nullptr},
+        {k, cu_seqlens, dims->ndocs, dims->ttot, dims->hkv, d, k_mx.codes, k_mx.scales, nullptr, nullptr},
+        {v, cu_seqlens, dims->ndocs, dims->ttot, dims->hkv, d, v_mx.codes, v_mx.scales, nullptr, nullptr}};
     PhaseMarks pm{opts, st};
     hipError_t e;
     for (const QuantArgs& a : qa) {
         if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(a, st)) != hipSuccess) return hip_fail(e);
     }
     int32_t* ctrl = (int32_t*)(base + w.ctrl);
-    int4* items = (int4*)(base + w.items);
-    PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, dims->hq, 0,
-                items, w.max_tiles * dims->hq};
+    int4* items = (int4*)(base + w.items_q);
+    PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
+                dims->hq, items, 0, nullptr};
     if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
     FwdArgs fa;
     fa.qc = q_mx.codes; fa.qs = q_mx.scales;
@@ -232,33 +230,44 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     uint8_t* oc = base + w.ocodes;
     uint8_t* os = base + w.oscales;
     float* dvec = (float*)(base + w.dvec);
-    float* dqacc = (float*)(base + w.dqacc);
 
-    // dO launch: codes + scales, D = dO~ . O, dQ accumulator cleared (Section 3.5.1)
-    QuantArgs qa{d_o, cu_seqlens, dims->ndocs, dims->ttot, dims->hq, d, oc, os, o, dvec, dqacc};
+    // dO launch: codes + scales and D = dO~ . O (Section 3.5.1)
+    QuantArgs qa{d_o, cu_seqlens, dims->ndocs, dims->ttot, dims->hq, d, oc, os, o, dvec};
     PhaseMarks pm{opts, st};
     hipError_t e;
     if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(qa, st)) != hipSuccess) return hip_fail(e);
     int32_t* ctrl = (int32_t*)(base + w.ctrl);
-    int4* items = (int4*)(base + w.items);
-    PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, dims->hkv, 1,
-                items, w.max_tiles * dims->hkv};
+    int4* items_q = (int4*)(base + w.items_q);
+    int4* items_k = (int4*)(base + w.items_k);
+    PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
+                dims->hq, items_q, dims->hkv, items_k};
     if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
+    const float scale = scale_of(opts, d);
     BwdArgs ba;
     ba.qc = q_mx.codes; ba.qs = q_mx.scales;
     ba.kc = k_mx.codes; ba.ks = k_mx.scales;
     ba.vc = v_mx.codes; ba.vs = v_mx.scales;
     ba.oc = oc; ba.os = os;
-    ba.lse2 = lse2; ba.dvec = dvec; ba.dqacc = dqacc;
+    ba.lse2 = lse2; ba.dvec = dvec;
     ba.dk = dk; ba.dv = dv;
-    ba.items = items; ba.nitems = ctrl;
+    ba.items = items_k; ba.nitems = ctrl + 2;
     ba.ttot = dims->ttot; ba.hq = dims->hq; ba.hkv = dims->hkv;
-    ba.scale = scale_of(opts, d);
-    ba.c1 = ba.scale * 1.4426950408889634f;
+    ba.scale = scale;
+    ba.c1 = scale * 1.4426950408889634f;
     if ((e = pm.mark()) != hipSuccess || (e = launch_bwd(ba, d, w.max_tiles * dims->hkv, st)) != hipSuccess)
         return hip_fail(e);
-    if ((e = pm.mark()) != hipSuccess ||
-        (e = launch_dq_finalize(dqacc, dq, (long)dims->ttot * dims->hq * d, ba.scale, st)) != hipSuccess)
+    DqArgs qd;
+    qd.qc = q_mx.codes; qd.qs = q_mx.scales;
+    qd.kc = k_mx.codes; qd.ks = k_mx.scales;
+    qd.vc = v_mx.codes; qd.vs = v_mx.scales;
+    qd.oc = oc; qd.os = os;
+    qd.lse2 = lse2; qd.dvec = dvec;
+    qd.dq = dq;
+    qd.items = items_q; qd.nitems = ctrl;
+    qd.ttot = dims->ttot; qd.hq = dims->hq; qd.hkv = dims->hkv;
+    qd.scale = scale;
+    qd.c1 = ba.c1;
+    if ((e = pm.mark()) != hipSuccess || (e = launch_dq(qd, d, w.max_tiles * dims->hq, st)) != hipSuccess)
         return hip_fail(e);
     e = pm.mark();
     return e == hipSuccess ? FLAMIA_OK : hip_fail(e);

@@ -5,24 +5,22 @@
 // statistic, dS quantized on 32x32 document-local blocks from the block
 // maximum; Appendix B.1: the dV operand is E4M3(2^8 P) with no stored scale).
 //
-// One workgroup = one work item (document, key/value head, 128-key tile
-// anchored at the document start); wave w owns keys 32w..32w+31 of the tile.
-// For every query head of the group and every 64-query step from the
-// diagonal to the end of the document:
+// Key-major dK/dV pass.  One workgroup = one work item (document,
+// key/value head, 128-key tile anchored at the document start); wave w owns
+// keys 32w..32w+31 of the tile.  For every query head of the group and every
+// 64-query step from the diagonal to the end of the document:
 //   S  [query][key] = Q^ K^T    A = query rows (LDS), B = the wave's key rows (registers)
 //   dP [query][key] = dO^ V^T   same structure; both bitwise equal to the
 //                               forward's S^T (role-swapped operands give identical
 //                               accumulator bits on this hardware)
 //   P = 2^(x - lse2), P-hat_b = E4M3(2^8 P), dS = P (dP - D)
 //   dS-hat: one exponent per 32x32 block = one accumulator tile (block max via
-//   a wave reduction), codes written once and read in both orientations:
+//   a wave reduction):
 //   dV^T += dO^T P-hat_b   (A = dO^T by transposed LDS read, B = accumulator bytes)
 //   dK^T += Q^T dS-hat     (A = Q^T by transposed LDS read, B = accumulator bytes)
-//   dQ   += dS-hat K^      (A = dS-hat by transposed read of its key-major LDS
-//                           copy, B = K^ by transposed read), fp32 atomics into
-//                           the accumulator, scaled and rounded by dq_finalize.
 // dK and dV accumulate in registers across the query heads of the group
-// (GQA sum in fp32) and are written once.
+// (GQA sum in fp32) and are written once.  dQ is the query-major pass
+// (dq.hip), which rebuilds the same dS-hat bit for bit.
 #include "device.h"
 #include "kernels.h"
 
@@ -33,17 +31,12 @@ constexpr int kQStep = 64;
 template <int D>
 struct BwdSmem {
     static constexpr int kStride = D + 16;       // row pitch of code tiles
-    static constexpr int kSStride = kQStep + 16; // row pitch of the key-major dS-hat tile
     uint8_t q[kQStep * kStride];
     uint8_t o[kQStep * kStride];                 // quantized dO
-    uint8_t k[kTile * kStride];
-    uint8_t st[kTile * kSStride];                // dS-hat, [key][query]
     alignas(16) float lse[kQStep];
     alignas(16) float dv[kQStep];                // D
     uint8_t eq[kQStep];
     uint8_t eo[kQStep];
-    uint8_t ek[kTile];
-    int es[2][4];                                // dS block exponent + 127 [query block][key block]
 };
 
 template <int D>
@@ -51,9 +44,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     constexpr int KC = D / 64;
     constexpr int DT = D / 32;
     constexpr int STR = BwdSmem<D>::kStride;
-    constexpr int SSTR = BwdSmem<D>::kSStride;
     constexpr int NQ = kQStep * D / 16 / 256;     // 16-byte chunks per thread of a 64-row code tile
-    constexpr int KCH = kTile * D / 16;
     __shared__ BwdSmem<D> sm;
 
     if ((int)blockIdx.x >= *a.nitems) return;
@@ -83,8 +74,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             po[r] = *reinterpret_cast<const uint4*>(a.oc + (qr * a.hq + h) * D + col);
         }
         // Every thread issues the same loads (rows clamped into the document),
-        // so the number of outstanding memory operations is static and the
-        // wait for this prefetch never has to drain the dQ atomics issued after it.
+        // so the number of outstanding memory operations is static.
         {
             const int ql = q0 + (tid & (kQStep - 1));
             const long qr = ds + min(ql, L - 1);
@@ -130,14 +120,6 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     const int ek = a.ks[(long)g * a.ttot + key_row];
     const int ev = a.vs[(long)g * a.ttot + key_row];
 
-    // K^ tile of the work item in LDS (B operand of dQ, read transposed)
-    for (int c = tid; c < KCH; c += 256) {
-        const int row = c / (D / 16), col = (c % (D / 16)) * 16;
-        const long kr = min(k0 + row, a.ttot - 1);
-        *reinterpret_cast<uint4*>(&sm.k[row * STR + col]) = *reinterpret_cast<const uint4*>(a.kc + (kr * a.hkv + g) * D + col);
-    }
-    if (tid < kTile) sm.ek[tid] = a.ks[(long)g * a.ttot + min(k0 + tid, a.ttot - 1)];
-
     v16f dvt[DT], dkt[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) { dvt[dt] = v16f{0}; dkt[dt] = v16f{0}; }
@@ -181,7 +163,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
         }
         // ---- P, P-hat_b, dS, dS-hat (one 32x32 block per accumulator tile)
         const bool overlap = qs0 < kt0 + kTile;    // step meets the causal boundary
-        int pbc[2][4], dsc[2][4], es[2];
+        int pbc[2][4], dsc[2][4], es[2];   // es: dS block exponent + 127 per query block
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             float dsv[16];
@@ -214,14 +196,6 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
                 dsc[st][j] = pack_fp8x4_div(dsv[4 * j], dsv[4 * j + 1], dsv[4 * j + 2], dsv[4 * j + 3], sc);
             }
         }
-        // ---- key-major copy of dS-hat for dQ, and the block exponents
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<int*>(&sm.st[(32 * wave + lr) * SSTR + 32 * st + 8 * j + 4 * lg]) = dsc[st][j];
-        if (lane == 0) { sm.es[0][wave] = es[0]; sm.es[1][wave] = es[1]; }
-
         // ---- dV^T += dO^T P-hat_b and dK^T += Q^T dS-hat (contraction over the 64 queries)
         {
             const v8i pb = v8i{pbc[0][0], pbc[0][1], pbc[0][2], pbc[0][3], pbc[1][0], pbc[1][1], pbc[1][2], pbc[1][3]};
@@ -240,42 +214,6 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
                     r[rr] = lds_read_tr8(&sm.q[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
                 const v8i qa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
                 dkt[dt] = mfma_mx(qa, db, dkt[dt], sq, es[lg]);
-            }
-        }
-        __syncthreads();
-
-        // ---- dQ[query][d] = dS-hat K^ over the 128 keys; wave w -> query half w>>1
-        {
-            const int qsub = wave >> 1;
-            constexpr int DPW = DT / 2;                 // channel tiles per wave
-#pragma unroll
-            for (int u = 0; u < DPW; ++u) {
-                const int dt = (wave & 1) * DPW + u;
-                v16f acc = v16f{0};
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    v2i r[4];
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        r[rr] = lds_read_tr8(&sm.st[(64 * c + 16 * rr + tr_key) * SSTR + 32 * qsub + tr_col]);
-                    const v8i sa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        r[rr] = lds_read_tr8(&sm.k[(64 * c + 16 * rr + tr_key) * STR + 32 * dt + tr_col]);
-                    const v8i kbt = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
-                    acc = mfma_mx(sa, kbt, acc, sm.es[qsub][2 * c + lg], sm.ek[64 * c + 32 * lg]);
-                }
-                // Rows past the document end hold exact zeros (P = 0 there):
-                // they are added, as zeros, to the rows that follow (the next
-                // document's, or the accumulator's 64-row slack past the last
-                // token), so all 16 atomics are issued unconditionally and no
-                // address is shared by the padding of different items.
-                float* dqp = a.dqacc + (long)h * D + 32 * dt + lr;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int ql = qs0 + 32 * qsub + 8 * (i >> 2) + 4 * lg + (i & 3);
-                    atomicAdd(dqp + (long)(ds + ql) * a.hq * D, ql < L ? acc[i] : 0.f);
-                }
             }
         }
         if (!more) break;

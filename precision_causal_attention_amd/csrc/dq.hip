@@ -1,0 +1,197 @@
+// Query-major dQ pass of the MXFP8 causal backward (FLAMIA paper: Section 2
+// equation dQ = dS K; Section 3.3: dS rebuilt from the forward's quantized
+// Q/K and the saved row statistic, one E4M3 exponent per 32x32
+// document-local block).
+//
+// One workgroup = one work item (document, query head, 128-query tile
+// anchored at the document start); wave w owns queries 32w..32w+31; key
+// tiles are visited in ascending order up to the diagonal, as in the forward.
+// Per 128-key tile:
+//   S^T [key][query] = K^ Q^T     (A = key rows from LDS, B = query rows in registers)
+//   dP^T[key][query] = V^ dO^T    (A = value rows from LDS, B = dO rows in registers)
+//   P = 2^(x - lse2), dS = P (dP - D); each 32x32 accumulator tile is one dS
+//   block: its maximum gives the exponent, the convert divides by 2^e
+//   dQ^T[d][query] += K^T dS-hat^T   (A = K^T by the transposing LDS read,
+//                                     B = dS-hat straight from the accumulators)
+// The score and dP products use the same operands, instructions and order as
+// the key-major pass (role-swapped MFMA operands give identical bits), so
+// dS-hat here is bitwise the payload the key-major pass feeds to dK.  dQ is
+// owned by one workgroup: no atomics, deterministic, written once as bf16.
+#include "device.h"
+#include "kernels.h"
+
+namespace flamia {
+
+template <int D>
+struct DqSmem {
+    static constexpr int kStride = D + 16;
+    uint8_t k[kTile * kStride];
+    uint8_t v[kTile * kStride];
+    uint8_t ek[kTile];
+    uint8_t ev[kTile];
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a) {
+    constexpr int KC = D / 64;
+    constexpr int DT = D / 32;
+    constexpr int STR = DqSmem<D>::kStride;
+    constexpr int CHUNKS = kTile * D / 16;
+    __shared__ DqSmem<D> sm;
+
+    if ((int)blockIdx.x >= *a.nitems) return;
+    const int4 it = a.items[blockIdx.x];
+    const int q0 = it.x, ds = it.y, de = it.z, h = it.w;
+    const int g = h / (a.hq / a.hkv);
+    const int L = de - ds;
+    const int lq0 = q0 - ds;
+    const int ntiles = lq0 / kTile + 1;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lg = lane >> 5, lr = lane & 31;
+    const int q_loc = lq0 + 32 * wave + lr;
+    const bool q_valid = q_loc < L;
+    const int q_row = ds + min(q_loc, L - 1);
+
+    // query rows of Q^ and dO^ as B operands (column = query, k = channel)
+    v8i qb[KC], ob[KC];
+    {
+        const uint8_t* qp = a.qc + ((long)q_row * a.hq + h) * D;
+        const uint8_t* op = a.oc + ((long)q_row * a.hq + h) * D;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * kc + 16 * lg);
+            uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * kc + 32 + 16 * lg);
+            qb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            lo = *reinterpret_cast<const uint4*>(op + 64 * kc + 16 * lg);
+            hi = *reinterpret_cast<const uint4*>(op + 64 * kc + 32 + 16 * lg);
+            ob[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+    }
+    const int eq = a.qs[(long)h * a.ttot + q_row];
+    const int eo = a.os[(long)h * a.ttot + q_row];
+    const float lse_raw = a.lse2[(long)h * a.ttot + q_row];
+    const float lse = q_valid ? lse_raw : INFINITY;      // P = 0 on rows outside the document
+    const float Dq = a.dvec[(long)h * a.ttot + q_row];
+
+    v16f acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = v16f{0};
+
+    const int s16 = lane & 15, grp = (lane >> 4) & 1;
+    const int tr_key = 8 * ((s16 >> 1) >> 2) + 4 * lg + ((s16 >> 1) & 3);
+    const int tr_col = 16 * grp + 8 * (s16 & 1);
+
+    uint4 kr[CHUNKS / 256], vr[CHUNKS / 256];
+    uint32_t ekr = 0, evr = 0;
+    auto load_tile = [&](int t) {
+        const int k0 = ds + kTile * t;
+#pragma unroll
+        for (int r = 0; r < CHUNKS / 256; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+            const long krow = min(k0 + row, a.ttot - 1);
+            kr[r] = *reinterpret_cast<const uint4*>(a.kc + (krow * a.hkv + g) * D + col);
+            vr[r] = *reinterpret_cast<const uint4*>(a.vc + (krow * a.hkv + g) * D + col);
+        }
+        {
+            const long kt = min(k0 + (tid & (kTile - 1)), a.ttot - 1);
+            ekr = a.ks[(long)g * a.ttot + kt];
+            evr = a.vs[(long)g * a.ttot + kt];
+        }
+    };
+    load_tile(0);
+
+    for (int t = 0; t < ntiles; ++t) {
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < CHUNKS / 256; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+            *reinterpret_cast<uint4*>(&sm.k[row * STR + col]) = kr[r];
+            *reinterpret_cast<uint4*>(&sm.v[row * STR + col]) = vr[r];
+        }
+        if (tid < kTile) {
+            sm.ek[tid] = (uint8_t)ekr;
+            sm.ev[tid] = (uint8_t)evr;
+        }
+        __syncthreads();
+        if (t + 1 < ntiles) load_tile(t + 1);
+
+        const bool diag = (t == ntiles - 1);
+        int dsc[4][4], es[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int row = 32 * kk + lr;
+            v16f s = v16f{0}, dp = v16f{0};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                uint4 lo = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 16 * lg]);
+                uint4 hi = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 32 + 16 * lg]);
+                const v8i ka = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                s = mfma_mx(ka, qb[kc], s, sm.ek[row], eq);
+                lo = *reinterpret_cast<const uint4*>(&sm.v[row * STR + 64 * kc + 16 * lg]);
+                hi = *reinterpret_cast<const uint4*>(&sm.v[row * STR + 64 * kc + 32 + 16 * lg]);
+                const v8i va = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                dp = mfma_mx(va, ob[kc], dp, sm.ev[row], eo);
+            }
+            float dsv[16];
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float p = exp2_fast(fmaf(s[i], a.c1, -lse));
+                if (diag) {
+                    const int key = kTile * t + 32 * kk + 8 * (i >> 2) + 4 * lg + (i & 3);
+                    if (key > q_loc) p = 0.f;
+                }
+                const float d = p * (dp[i] - Dq);
+                dsv[i] = d;
+                amax = fmaxf(amax, fabsf(d));
+            }
+            amax = wave_max(amax);
+            const int e = block_exponent(amax, -126);
+            es[kk] = e + 127;
+            const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dsc[kk][j] = pack_fp8x4_div(dsv[4 * j], dsv[4 * j + 1], dsv[4 * j + 2], dsv[4 * j + 3], sc);
+        }
+        // ---- dQ^T += K^T dS-hat^T, two 64-key chunks
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const v8i db = v8i{dsc[2 * c][0], dsc[2 * c][1], dsc[2 * c][2], dsc[2 * c][3],
+                               dsc[2 * c + 1][0], dsc[2 * c + 1][1], dsc[2 * c + 1][2], dsc[2 * c + 1][3]};
+            const int sk = sm.ek[64 * c + 32 * lg];
+            const int sd = lg ? es[2 * c + 1] : es[2 * c];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                v2i r[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    r[rr] = lds_read_tr8(&sm.k[(64 * c + 16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                const v8i ka = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+                acc[dt] = mfma_mx(ka, db, acc[dt], sk, sd);
+            }
+        }
+    }
+    // ---- epilogue: dQ = softmax_scale * sum, bf16
+    if (q_valid) {
+        uint16_t* qp = a.dq + ((long)(ds + q_loc) * a.hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t b0 = f32_to_bf16(acc[dt][4 * j] * a.scale), b1 = f32_to_bf16(acc[dt][4 * j + 1] * a.scale);
+                const uint32_t b2 = f32_to_bf16(acc[dt][4 * j + 2] * a.scale), b3 = f32_to_bf16(acc[dt][4 * j + 3] * a.scale);
+                *reinterpret_cast<uint2*>(qp + 32 * dt + 8 * j + 4 * lg) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            }
+    }
+}
+
+hipError_t launch_dq(const DqArgs& a, int d, long grid, hipStream_t st) {
+    if (grid <= 0) return hipSuccess;
+    if (d == 64) hipLaunchKernelGGL(dq_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(dq_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace flamia

@@ -14,10 +14,9 @@ struct QuantArgs {
     int ndocs, ttot, heads, d;
     uint8_t* codes;
     uint8_t* scales;
-    // dO variant only (nullptr otherwise)
+    // dO variant only (nullptr otherwise): D = dO~ . O
     const uint16_t* o;
     float* dvec;
-    float* dqacc;
 };
 
 // Work items: int4 {first token of the tile (global), document start,
@@ -28,10 +27,11 @@ struct PlanArgs {
     int max_cost;          // >= max tiles of one document
     int32_t* tiles_prefix; // [ndocs + 1]
     int32_t* ctrl;         // control block, see plan.hip
-    int heads;             // heads per tile item (hq for forward, hkv for backward)
-    int backward;          // 0: cost = tile index + 1; 1: cost = tiles from the diagonal to the end
-    int4* items;
-    long max_items;
+    long max_tiles;
+    int heads_q;           // query-major list: cost = tile index + 1 (forward, dQ)
+    int4* items_q;
+    int heads_k;           // key-major list: cost = tiles from the diagonal to the end (dK/dV);
+    int4* items_k;         // nullptr: not built
 };
 
 struct FwdArgs {
@@ -50,7 +50,6 @@ struct BwdArgs {
     const uint8_t *qc, *qs, *kc, *ks, *vc, *vs, *oc, *os;   // oc/os: quantized dO
     const float* lse2;
     const float* dvec;
-    float* dqacc;
     uint16_t *dk, *dv;
     const int4* items;
     const int32_t* nitems;
@@ -58,10 +57,21 @@ struct BwdArgs {
     float c1, scale;
 };
 
+struct DqArgs {
+    const uint8_t *qc, *qs, *kc, *ks, *vc, *vs, *oc, *os;
+    const float* lse2;
+    const float* dvec;
+    uint16_t* dq;
+    const int4* items;
+    const int32_t* nitems;
+    int ttot, hq, hkv;
+    float c1, scale;
+};
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
-hipError_t launch_dq_finalize(const float* acc, uint16_t* dq, long n, float scale, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, int d, long grid, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, int d, long grid, hipStream_t st);
+hipError_t launch_dq(const DqArgs& a, int d, long grid, hipStream_t st);
 
 }  // namespace flamia

@@ -13,8 +13,10 @@
 // integer cost instead of a comparison sort.  Within one cost class the order
 // is whatever the atomics give; it does not change any result.
 //
-// ctrl layout (int32): [0] item count, [1] tile count,
-//   [16, 16+C+1) offset of each cost class, [16+C+1, 16+2(C+1)) cursors.
+// ctrl layout (int32): [0] query-major item count, [1] tile count,
+//   [2] key-major item count, [16, 16+C1) offset of each cost class,
+//   [16+C1, 16+2 C1) query-major cursors, [16+2 C1, 16+3 C1) key-major cursors
+//   (C1 = max_cost + 1).
 #include "device.h"
 #include "kernels.h"
 
@@ -49,7 +51,7 @@ __device__ void block_scan(int* buf, int n, bool reverse, int* partial) {
 
 __global__ void __launch_bounds__(kPlanThreads)
 plan_count_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost,
-                  int32_t* __restrict__ tiles_prefix, int32_t* __restrict__ ctrl, int heads) {
+                  int32_t* __restrict__ tiles_prefix, int32_t* __restrict__ ctrl, int heads_q, int heads_k) {
     extern __shared__ int smem[];
     int* partial = smem;                       // kPlanThreads
     int* hist = smem + kPlanThreads;           // max_cost + 1
@@ -76,11 +78,13 @@ plan_count_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost,
         const int incl = hist[c];
         const int own = c >= 1 ? ctrl[16 + c] : 0;
         ctrl[16 + c] = incl - own;             // exclusive: sum over c' > c
-        ctrl[16 + C1 + c] = 0;                 // cursor
+        ctrl[16 + C1 + c] = 0;                 // cursors
+        ctrl[16 + 2 * C1 + c] = 0;
     }
     if (tid == 0) {
         ctrl[1] = hist[1];                     // all tiles
-        ctrl[0] = hist[1] * heads;
+        ctrl[0] = hist[1] * heads_q;
+        ctrl[2] = hist[1] * heads_k;
     }
     __syncthreads();
     // exclusive prefix of tile counts over documents
@@ -109,31 +113,37 @@ plan_count_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost,
 
 __global__ void __launch_bounds__(256)
 plan_fill_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost,
-                 const int32_t* __restrict__ tiles_prefix, int32_t* __restrict__ ctrl, int heads,
-                 int backward, int4* __restrict__ items, long max_tiles) {
+                 const int32_t* __restrict__ tiles_prefix, int32_t* __restrict__ ctrl, long max_tiles,
+                 int heads_q, int4* __restrict__ items_q, int heads_k, int4* __restrict__ items_k) {
     const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const int total = ctrl[1];
     if (p >= total || p >= max_tiles) return;
     const int doc = find_doc(tiles_prefix, ndocs, (int)p);
     const int t = (int)p - tiles_prefix[doc];
     const int n = tiles_prefix[doc + 1] - tiles_prefix[doc];
-    const int cost = backward ? n - t : t + 1;
     const int C1 = max_cost + 1;
-    const int slot = ctrl[16 + cost] + atomicAdd(&ctrl[16 + C1 + cost], 1);
     const int ds = cu[doc], de = cu[doc + 1];
-    for (int h = 0; h < heads; ++h) items[(long)slot * heads + h] = make_int4(ds + kTile * t, ds, de, h);
+    {
+        const int cost = t + 1;
+        const int slot = ctrl[16 + cost] + atomicAdd(&ctrl[16 + C1 + cost], 1);
+        for (int h = 0; h < heads_q; ++h) items_q[(long)slot * heads_q + h] = make_int4(ds + kTile * t, ds, de, h);
+    }
+    if (items_k) {
+        const int cost = n - t;
+        const int slot = ctrl[16 + cost] + atomicAdd(&ctrl[16 + 2 * C1 + cost], 1);
+        for (int h = 0; h < heads_k; ++h) items_k[(long)slot * heads_k + h] = make_int4(ds + kTile * t, ds, de, h);
+    }
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
     const size_t smem = sizeof(int) * (kPlanThreads + a.max_cost + 1);
     hipLaunchKernelGGL(plan_count_kernel, dim3(1), dim3(kPlanThreads), smem, st, a.cu, a.ndocs, a.max_cost,
-                       a.tiles_prefix, a.ctrl, a.heads);
+                       a.tiles_prefix, a.ctrl, a.heads_q, a.items_k ? a.heads_k : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long max_tiles = a.max_items / a.heads;
-    const unsigned blocks = (unsigned)((max_tiles + 255) / 256);
+    const unsigned blocks = (unsigned)((a.max_tiles + 255) / 256);
     hipLaunchKernelGGL(plan_fill_kernel, dim3(blocks), dim3(256), 0, st, a.cu, a.ndocs, a.max_cost,
-                       a.tiles_prefix, a.ctrl, a.heads, a.backward, a.items, max_tiles);
+                       a.tiles_prefix, a.ctrl, a.max_tiles, a.heads_q, a.items_q, a.heads_k, a.items_k);
     return hipGetLastError();
 }
 

@@ -19,8 +19,7 @@ template <int D, bool kDO>
 __global__ void __launch_bounds__(256)
 quantize_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int ndocs,
                 int ttot, int heads, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                const uint16_t* __restrict__ o, float* __restrict__ dvec,
-                float* __restrict__ dqacc) {
+                const uint16_t* __restrict__ o, float* __restrict__ dvec) {
     constexpr int HALF = D / 2;              // channels per lane
     constexpr int NV = HALF / 8;             // 16-byte bf16 vectors per lane
     const int w0 = blockIdx.x * kBlock;
@@ -74,8 +73,7 @@ quantize_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, 
             }
             if constexpr (kDO) {
                 // D_i = dO~_i . O_i with the dequantized dO and the bf16 output
-                // (paper, Section 3.3), fp32 accumulation; and zero the fp32 dQ
-                // accumulator rows of this token and head.
+                // (paper, Section 3.3), fp32 accumulation.
                 float dot = 0.f;
 #pragma unroll
                 for (int j = 0; j < NV; ++j) {
@@ -91,30 +89,10 @@ quantize_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, 
                     }
                 }
                 dot += __shfl_xor(dot, 1, 64);
-                if (active) {
-                    if (half == 0) dvec[(long)h * ttot + t] = dot;
-                    float4* z = reinterpret_cast<float4*>(dqacc + base);
-#pragma unroll
-                    for (int j = 0; j < HALF / 4; ++j) z[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-                }
+                if (active && half == 0) dvec[(long)h * ttot + t] = dot;
             }
         }
     }
-}
-
-// dQ = bf16(softmax_scale * dQacc), 8 elements per thread.
-__global__ void __launch_bounds__(256)
-dq_finalize_kernel(const float* __restrict__ acc, uint16_t* __restrict__ dq, long n8, float scale) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n8) return;
-    const float4 a = reinterpret_cast<const float4*>(acc)[2 * i];
-    const float4 b = reinterpret_cast<const float4*>(acc)[2 * i + 1];
-    uint4 r;
-    r.x = f32_to_bf16(a.x * scale) | (f32_to_bf16(a.y * scale) << 16);
-    r.y = f32_to_bf16(a.z * scale) | (f32_to_bf16(a.w * scale) << 16);
-    r.z = f32_to_bf16(b.x * scale) | (f32_to_bf16(b.y * scale) << 16);
-    r.w = f32_to_bf16(b.z * scale) | (f32_to_bf16(b.w * scale) << 16);
-    reinterpret_cast<uint4*>(dq)[i] = r;
 }
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
@@ -122,19 +100,12 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
     const dim3 grid((a.ttot + kBlock - 1) / kBlock), block(256);
     const bool dO = a.o != nullptr;
     if (a.d == 64) {
-        if (dO) hipLaunchKernelGGL((quantize_kernel<64, true>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec, a.dqacc);
-        else hipLaunchKernelGGL((quantize_kernel<64, false>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec, a.dqacc);
+        if (dO) hipLaunchKernelGGL((quantize_kernel<64, true>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec);
+        else hipLaunchKernelGGL((quantize_kernel<64, false>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec);
     } else {
-        if (dO) hipLaunchKernelGGL((quantize_kernel<128, true>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec, a.dqacc);
-        else hipLaunchKernelGGL((quantize_kernel<128, false>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec, a.dqacc);
+        if (dO) hipLaunchKernelGGL((quantize_kernel<128, true>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec);
+        else hipLaunchKernelGGL((quantize_kernel<128, false>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec);
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_dq_finalize(const float* acc, uint16_t* dq, long n, float scale, hipStream_t st) {
-    const long n8 = n / 8;
-    if (n8 <= 0) return hipSuccess;
-    hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, acc, dq, n8, scale);
     return hipGetLastError();
 }
 

@@ -114,14 +114,14 @@ def test_full_size_gqa_sampled_group(orc):
 
 
 def test_deterministic_and_document_isolation():
-    """Appendix B.5: the forward is deterministic; dK and dV (no atomics) too.
-    Section 4.1 probe: one document x 1e4 leaves the other documents' O, lse2,
-    dK and dV bitwise unchanged (document-local scales)."""
+    """Appendix B.5: the forward is deterministic; the backward here too (no
+    atomics).  Section 4.1 probe: one document x 1e4 leaves every output of
+    the other documents bitwise unchanged (document-local scales)."""
     inst = SMALL["gqa-outliers"]()
     say("[determinism/isolation] gqa-outliers")
     a = run_hip(inst)
     b = run_hip(inst)
-    for key in ("o", "lse2", "dk", "dv"):
+    for key in ("o", "lse2", "dq", "dk", "dv"):
         assert np.array_equal(a[key], b[key]), key
     lo, hi = int(inst["cu_seqlens"][1]), int(inst["cu_seqlens"][2])
     inst2 = dict(inst)
@@ -131,26 +131,32 @@ def test_deterministic_and_document_isolation():
         inst2[name] = x
     c = run_hip(inst2)
     keep = np.r_[0:lo, hi:inst["q"].shape[0]]
-    for key in ("o", "dk", "dv"):
+    for key in ("o", "dq", "dk", "dv"):
         assert np.array_equal(a[key][keep], c[key][keep]), key
     assert np.array_equal(a["lse2"][:, keep], c["lse2"][:, keep])
 
 
-def test_causal_invariant_forward():
-    """Perturbing token p changes no O / lse2 row before p's 32-token block."""
+def test_causal_invariant():
+    """Perturbing Q, K, V or dO of token p changes no O / lse2 / dQ row before
+    p's 32-token block (Section 3.2: no scale spans more than one block), and
+    no output of any other document."""
     inst = SMALL["ragged-gqa-d64"]()
     say("[causal] ragged-gqa-d64")
-    base = run_hip(inst, backward=False)
+    base = run_hip(inst)
     start = int(inst["cu_seqlens"][7])           # document of 300 tokens
+    end = int(inst["cu_seqlens"][8])
     p = start + 170
     first = start + 32 * (170 // 32)
-    for name in ("q", "k", "v"):
+    for name in ("q", "k", "v", "do"):
         inst2 = dict(inst)
         x = inst[name].copy()
         x[p] = W.bf16_bits(W.bits_to_f32(x[p]) * 9.0 + 3.0)
         inst2[name] = x
-        r = run_hip(inst2, backward=False)
-        assert np.array_equal(r["o"][:first], base["o"][:first]), name
+        r = run_hip(inst2)
+        for key in ("o", "dq"):
+            assert np.array_equal(r[key][:first], base[key][:first]), (name, key)
+            assert np.array_equal(r[key][end:], base[key][end:]), (name, key)
         assert np.array_equal(r["lse2"][:, :first], base["lse2"][:, :first]), name
-        end = int(inst["cu_seqlens"][8])
-        assert np.array_equal(r["o"][end:], base["o"][end:]), name
+        for key in ("dk", "dv"):
+            assert np.array_equal(r[key][:start], base[key][:start]), (name, key)
+            assert np.array_equal(r[key][end:], base[key][end:]), (name, key)
