@@ -60,7 +60,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     const int key_row = ds + min(key_loc, L - 1);
 
     // ---- staging of one 64-query step (prefetched into registers one step ahead)
-    uint4 pq[NQ], po[NQ];
+    u32x4 pq[NQ], po[NQ];
     uint32_t p_eq = 0, p_eo = 0;
     float p_lse = 0.f, p_dv = 0.f;
     bool p_in = true;
@@ -70,8 +70,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             const int c = tid + 256 * r;
             const int row = c / (D / 16), col = (c % (D / 16)) * 16;
             const long qr = ds + min(q0 + row, L - 1);
-            pq[r] = *reinterpret_cast<const uint4*>(a.qc + (qr * a.hq + h) * D + col);
-            po[r] = *reinterpret_cast<const uint4*>(a.oc + (qr * a.hq + h) * D + col);
+            pq[r] = *reinterpret_cast<const u32x4*>(a.qc + (qr * a.hq + h) * D + col);
+            po[r] = *reinterpret_cast<const u32x4*>(a.oc + (qr * a.hq + h) * D + col);
         }
         // Every thread issues the same loads (rows clamped into the document),
         // so the number of outstanding memory operations is static.
@@ -90,8 +90,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
         for (int r = 0; r < NQ; ++r) {
             const int c = tid + 256 * r;
             const int row = c / (D / 16), col = (c % (D / 16)) * 16;
-            *reinterpret_cast<uint4*>(&sm.q[row * STR + col]) = pq[r];
-            *reinterpret_cast<uint4*>(&sm.o[row * STR + col]) = po[r];
+            *reinterpret_cast<u32x4*>(&sm.q[row * STR + col]) = pq[r];
+            *reinterpret_cast<u32x4*>(&sm.o[row * STR + col]) = po[r];
         }
         if (tid < kQStep) {
             sm.eq[tid] = (uint8_t)p_eq;
@@ -140,7 +140,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
         q0 += kQStep;
         if (q0 >= L) { q0 = kt0; ++hh; }
         const bool more = hh < G;
-        if (more) load_step(g * G + hh, q0);
+        // unconditional (the last step re-fetches a valid step): a conditional
+        // update would keep the prefetch registers in scratch
+        load_step(g * G + min(hh, G - 1), q0);
 
         // ---- S and dP for the wave's 32 keys x 64 queries
         v16f sacc[2], pacc[2];

@@ -8,6 +8,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v2s __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // register-friendly 16-byte chunk
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -36,7 +37,8 @@ __device__ __forceinline__ v2i lds_read_tr8(const uint8_t* lds_addr) {
 // Four fp32 -> four E4M3 bytes (byte i = element i), round to nearest even;
 // bit-identical to the format's definition for |x| <= 448.
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    // both halves are overwritten, so the incoming register content is irrelevant
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 // Same with an exact power-of-two divisor: byte i = E4M3(x_i / scale).
@@ -47,6 +49,32 @@ __device__ __forceinline__ int pack_fp8x4_div(float a, float b, float c, float d
     int out;
     __builtin_memcpy(&out, &w, 4);
     return out;
+}
+
+// Sum of the four E4M3 values packed in w (hardware decode, exact).
+__device__ __forceinline__ float fp8x4_sum(int w) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    return (lo[0] + lo[1]) + (hi[0] + hi[1]);
+}
+
+// Cooperative fetch of one 128-row tile of two code tensors (K and V, [T][H][D])
+// plus their per-token scales into registers; rows are clamped into the buffer.
+template <int D, int N>
+__device__ __forceinline__ void fetch_kv_tile(u32x4 (&kr)[N], u32x4 (&vr)[N], uint32_t& ek, uint32_t& ev,
+                                              const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
+                                              const uint8_t* vs, int k0, int ttot, int heads, int g, int tid) {
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+        const int c = tid + 256 * r;
+        const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+        const long krow = min(k0 + row, ttot - 1);
+        kr[r] = *reinterpret_cast<const u32x4*>(kc + (krow * heads + g) * D + col);
+        vr[r] = *reinterpret_cast<const u32x4*>(vc + (krow * heads + g) * D + col);
+    }
+    const long kt = min(k0 + (tid & 127), ttot - 1);
+    ek = ks[(long)g * ttot + kt];
+    ev = vs[(long)g * ttot + kt];
 }
 
 __device__ __forceinline__ float fp8_to_f32(uint32_t code) {

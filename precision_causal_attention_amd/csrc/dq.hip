@@ -81,25 +81,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
     const int tr_key = 8 * ((s16 >> 1) >> 2) + 4 * lg + ((s16 >> 1) & 3);
     const int tr_col = 16 * grp + 8 * (s16 & 1);
 
-    uint4 kr[CHUNKS / 256], vr[CHUNKS / 256];
-    uint32_t ekr = 0, evr = 0;
-    auto load_tile = [&](int t) {
-        const int k0 = ds + kTile * t;
-#pragma unroll
-        for (int r = 0; r < CHUNKS / 256; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 16), col = (c % (D / 16)) * 16;
-            const long krow = min(k0 + row, a.ttot - 1);
-            kr[r] = *reinterpret_cast<const uint4*>(a.kc + (krow * a.hkv + g) * D + col);
-            vr[r] = *reinterpret_cast<const uint4*>(a.vc + (krow * a.hkv + g) * D + col);
-        }
-        {
-            const long kt = min(k0 + (tid & (kTile - 1)), a.ttot - 1);
-            ekr = a.ks[(long)g * a.ttot + kt];
-            evr = a.vs[(long)g * a.ttot + kt];
-        }
-    };
-    load_tile(0);
+    u32x4 kr[CHUNKS / 256], vr[CHUNKS / 256];
+    uint32_t ekr, evr;
+    fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds, a.ttot, a.hkv, g, tid);
 
     for (int t = 0; t < ntiles; ++t) {
         __syncthreads();
@@ -107,15 +91,18 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
         for (int r = 0; r < CHUNKS / 256; ++r) {
             const int c = tid + 256 * r;
             const int row = c / (D / 16), col = (c % (D / 16)) * 16;
-            *reinterpret_cast<uint4*>(&sm.k[row * STR + col]) = kr[r];
-            *reinterpret_cast<uint4*>(&sm.v[row * STR + col]) = vr[r];
+            *reinterpret_cast<u32x4*>(&sm.k[row * STR + col]) = kr[r];
+            *reinterpret_cast<u32x4*>(&sm.v[row * STR + col]) = vr[r];
         }
         if (tid < kTile) {
             sm.ek[tid] = (uint8_t)ekr;
             sm.ev[tid] = (uint8_t)evr;
         }
         __syncthreads();
-        if (t + 1 < ntiles) load_tile(t + 1);
+        // unconditional (the last iteration re-fetches its own tile): a
+        // conditional update would keep the prefetch registers in scratch
+        fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds + kTile * min(t + 1, ntiles - 1),
+                         a.ttot, a.hkv, g, tid);
 
         const bool diag = (t == ntiles - 1);
         int dsc[4][4], es[4];

@@ -32,8 +32,8 @@ struct FwdSmem {
     uint8_t ev[kTile];
 };
 
-template <int D>
-__global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
+template <int D, int ROWSUM>
+__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs a) {
     constexpr int KC = D / 64;                    // 64-channel contraction steps of S
     constexpr int DT = D / 32;                    // 32-row channel tiles of O^T
     constexpr int STR = FwdSmem<D>::kStride;
@@ -80,25 +80,9 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
     const int tr_col = 16 * grp + 8 * (s16 & 1);
 
     // ---- K^/V^ code tiles and scales, prefetched into registers one tile ahead
-    uint4 kr[CHUNKS / 256], vr[CHUNKS / 256];
-    uint32_t ekr = 0, evr = 0;
-    auto load_tile = [&](int t) {
-        const int k0 = ds + kTile * t;
-#pragma unroll
-        for (int r = 0; r < CHUNKS / 256; ++r) {
-            const int c = tid + 256 * r;
-            const int row = c / (D / 16), col = (c % (D / 16)) * 16;
-            const long krow = min(k0 + row, a.ttot - 1);
-            kr[r] = *reinterpret_cast<const uint4*>(a.kc + (krow * a.hkv + g) * D + col);
-            vr[r] = *reinterpret_cast<const uint4*>(a.vc + (krow * a.hkv + g) * D + col);
-        }
-        if (tid < kTile) {
-            const long kt = min(k0 + tid, a.ttot - 1);
-            ekr = a.ks[(long)g * a.ttot + kt];
-            evr = a.vs[(long)g * a.ttot + kt];
-        }
-    };
-    load_tile(0);
+    u32x4 kr[CHUNKS / 256], vr[CHUNKS / 256];
+    uint32_t ekr, evr;
+    fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds, a.ttot, a.hkv, g, tid);
 
     for (int t = 0; t < ntiles; ++t) {
         __syncthreads();
@@ -106,15 +90,18 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
         for (int r = 0; r < CHUNKS / 256; ++r) {
             const int c = tid + 256 * r;
             const int row = c / (D / 16), col = (c % (D / 16)) * 16;
-            *reinterpret_cast<uint4*>(&sm.k[row * STR + col]) = kr[r];
-            *reinterpret_cast<uint4*>(&sm.v[row * STR + col]) = vr[r];
+            *reinterpret_cast<u32x4*>(&sm.k[row * STR + col]) = kr[r];
+            *reinterpret_cast<u32x4*>(&sm.v[row * STR + col]) = vr[r];
         }
         if (tid < kTile) {
             sm.ek[tid] = (uint8_t)ekr;
             sm.ev[tid] = (uint8_t)evr;
         }
         __syncthreads();
-        if (t + 1 < ntiles) load_tile(t + 1);
+        // unconditional (the last iteration re-fetches its own tile): a
+        // conditional update would keep the prefetch registers in scratch
+        fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds + kTile * min(t + 1, ntiles - 1),
+                         a.ttot, a.hkv, g, tid);
 
         // ---- S^T = K^ Q^T for the 4 sub-tiles of 32 keys
         v16f s[4];
@@ -170,12 +157,8 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
                 const float p3 = exp2_fast(fmaf(s[kk][4 * j + 3], a.c1, nmc));
                 const int w = pack_fp8x4(p0, p1, p2, p3);
                 pc[kk][j] = w;
-                if (a.rowsum == 0) {
-                    l += (p0 + p1) + (p2 + p3);
-                } else {
-                    l += (fp8_to_f32(w & 0xFF) + fp8_to_f32((w >> 8) & 0xFF)) +
-                         (fp8_to_f32((w >> 16) & 0xFF) + fp8_to_f32((uint32_t)w >> 24));
-                }
+                if constexpr (ROWSUM == 0) l += (p0 + p1) + (p2 + p3);
+                else l += fp8x4_sum(w);
             }
         // ---- O^T += V^T P-hat^T, two 64-key chunks
 #pragma unroll
@@ -213,8 +196,14 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
 
 hipError_t launch_fwd(const FwdArgs& a, int d, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
-    if (d == 64) hipLaunchKernelGGL(fwd_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(fwd_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    const dim3 g((unsigned)grid), b(256);
+    if (d == 64) {
+        if (a.rowsum) hipLaunchKernelGGL((fwd_kernel<64, 1>), g, b, 0, st, a);
+        else hipLaunchKernelGGL((fwd_kernel<64, 0>), g, b, 0, st, a);
+    } else {
+        if (a.rowsum) hipLaunchKernelGGL((fwd_kernel<128, 1>), g, b, 0, st, a);
+        else hipLaunchKernelGGL((fwd_kernel<128, 0>), g, b, 0, st, a);
+    }
     return hipGetLastError();
 }
 
