@@ -81,8 +81,9 @@ typedef struct {
     /* Optional phase timing: when phase_events is non-NULL it points to
      * n_events hipEvent_t handles (created by the caller); the call records
      * event i on `stream` before its i-th internal launch and the next one
-     * after its last launch, as far as n_events allows.  flamia_fwd has 5
-     * phases (quantize Q, K, V; work list; forward kernel), flamia_bwd 4
+     * after its last launch, as far as n_events allows; NULL entries are
+     * skipped (no event recorded there).  flamia_fwd has 3 phases (quantize
+     * Q, K and V in one launch; work list; forward kernel), flamia_bwd 4
      * (quantize dO with D; work lists; key-major dK/dV kernel; query-major dQ
      * kernel).  NULL disables it. */
     void **phase_events;

@@ -56,9 +56,9 @@ flamia_status_t check_opts(const flamia_opts_t* o) {
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    long max_tiles, max_items;
+    long max_tiles;
     int max_cost;
-    size_t ctrl, prefix, items_q, items_k, ocodes, oscales, dvec, total;
+    size_t ctrl, prefix, tiles_q, tiles_k, ocodes, oscales, dvec, total;
 };
 
 Layout layout(const flamia_dims_t* d) {
@@ -66,12 +66,11 @@ Layout layout(const flamia_dims_t* d) {
     const long tc = d->ttot_cap;
     w.max_cost = (int)((tc + kTile - 1) / kTile) + 1;
     w.max_tiles = tc / kTile + d->ndocs_cap + 1;
-    w.max_items = w.max_tiles * (d->hq + d->hkv);
     size_t off = 0;
-    w.ctrl = off;    off += up256(sizeof(int32_t) * (16 + 3 * (size_t)(w.max_cost + 1)));
+    w.ctrl = off;    off += up256(sizeof(int32_t) * (16 + 2 * (size_t)(w.max_cost + 1)));
     w.prefix = off;  off += up256(sizeof(int32_t) * ((size_t)d->ndocs_cap + 1));
-    w.items_q = off; off += up256(sizeof(int4) * (size_t)w.max_tiles * d->hq);
-    w.items_k = off; off += up256(sizeof(int4) * (size_t)w.max_tiles * d->hkv);
+    w.tiles_q = off; off += up256(sizeof(int4) * (size_t)w.max_tiles);
+    w.tiles_k = off; off += up256(sizeof(int4) * (size_t)w.max_tiles);
     w.ocodes = off;  off += up256((size_t)tc * d->hq * d->d);
     w.oscales = off; off += up256((size_t)tc * d->hq);
     w.dvec = off;    off += up256(sizeof(float) * (size_t)tc * d->hq);
@@ -87,8 +86,9 @@ struct PhaseMarks {
     hipStream_t st;
     int next = 0;
     hipError_t mark() {
-        if (!o.phase_events || next >= o.n_events) { ++next; return hipSuccess; }
-        return hipEventRecord((hipEvent_t)o.phase_events[next++], st);
+        const int i = next++;
+        if (!o.phase_events || i >= o.n_events || !o.phase_events[i]) return hipSuccess;
+        return hipEventRecord((hipEvent_t)o.phase_events[i], st);
     }
 };
 
@@ -144,7 +144,10 @@ flamia_status_t flamia_quantize(const flamia_dims_t* dims, int32_t heads, const 
     if (heads <= 0) return FLAMIA_ERR_SHAPE;
     if (!x || !cu_seqlens || !out.codes || !out.scales) return FLAMIA_ERR_NULL;
     if (!aligned16(x) || !aligned16(out.codes)) return FLAMIA_ERR_ALIGN;
-    QuantArgs a{x, cu_seqlens, dims->ndocs, dims->ttot, heads, dims->d, out.codes, out.scales, nullptr, nullptr};
+    QuantArgs a{};
+    a.cu = cu_seqlens; a.ndocs = dims->ndocs; a.ttot = dims->ttot; a.d = dims->d;
+    a.t[0] = QuantTensor{x, out.codes, out.scales, heads};
+    a.ntensors = 1;
     hipError_t e = launch_quantize(a, (hipStream_t)stream);
     return e == hipSuccess ? FLAMIA_OK : hip_fail(e);
 }
@@ -172,27 +175,27 @@ flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     uint8_t* base = (uint8_t*)ws;
     const int d = dims->d;
 
-    // fused quantization of the three operands (Section 3.5.1)
-    const QuantArgs qa[3] = {
-        {q, cu_seqlens, dims->ndocs, dims->ttot, dims->hq, d, q_mx.codes, q_mx.scales, nullptr, nullptr},
-        {k, cu_seqlens, dims->ndocs, dims->ttot, dims->hkv, d, k_mx.codes, k_mx.scales, nullptr, nullptr},
-        {v, cu_seqlens, dims->ndocs, dims->ttot, dims->hkv, d, v_mx.codes, v_mx.scales, nullptr, nullptr}};
+    // quantization of the three operands in one launch (Section 3.5.1)
+    QuantArgs qa{};
+    qa.cu = cu_seqlens; qa.ndocs = dims->ndocs; qa.ttot = dims->ttot; qa.d = d;
+    qa.t[0] = QuantTensor{q, q_mx.codes, q_mx.scales, dims->hq};
+    qa.t[1] = QuantTensor{k, k_mx.codes, k_mx.scales, dims->hkv};
+    qa.t[2] = QuantTensor{v, v_mx.codes, v_mx.scales, dims->hkv};
+    qa.ntensors = 3;
     PhaseMarks pm{opts, st};
     hipError_t e;
-    for (const QuantArgs& a : qa) {
-        if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(a, st)) != hipSuccess) return hip_fail(e);
-    }
+    if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(qa, st)) != hipSuccess) return hip_fail(e);
     int32_t* ctrl = (int32_t*)(base + w.ctrl);
-    int4* items = (int4*)(base + w.items_q);
+    int4* tiles = (int4*)(base + w.tiles_q);
     PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
-                dims->hq, items, 0, nullptr};
+                tiles, nullptr};
     if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
     FwdArgs fa;
     fa.qc = q_mx.codes; fa.qs = q_mx.scales;
     fa.kc = k_mx.codes; fa.ks = k_mx.scales;
     fa.vc = v_mx.codes; fa.vs = v_mx.scales;
     fa.o = o; fa.lse2 = lse2;
-    fa.items = items; fa.nitems = ctrl;
+    fa.tiles = tiles; fa.ntiles = ctrl;
     fa.ttot = dims->ttot; fa.hq = dims->hq; fa.hkv = dims->hkv;
     fa.c1 = scale_of(opts, d) * 1.4426950408889634f;
     fa.c_log2 = (float)opts.c_log2;
@@ -232,15 +235,19 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     float* dvec = (float*)(base + w.dvec);
 
     // dO launch: codes + scales and D = dO~ . O (Section 3.5.1)
-    QuantArgs qa{d_o, cu_seqlens, dims->ndocs, dims->ttot, dims->hq, d, oc, os, o, dvec};
+    QuantArgs qa{};
+    qa.cu = cu_seqlens; qa.ndocs = dims->ndocs; qa.ttot = dims->ttot; qa.d = d;
+    qa.t[0] = QuantTensor{d_o, oc, os, dims->hq};
+    qa.ntensors = 1;
+    qa.o = o; qa.dvec = dvec;
     PhaseMarks pm{opts, st};
     hipError_t e;
     if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(qa, st)) != hipSuccess) return hip_fail(e);
     int32_t* ctrl = (int32_t*)(base + w.ctrl);
-    int4* items_q = (int4*)(base + w.items_q);
-    int4* items_k = (int4*)(base + w.items_k);
+    int4* tiles_q = (int4*)(base + w.tiles_q);
+    int4* tiles_k = (int4*)(base + w.tiles_k);
     PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
-                dims->hq, items_q, dims->hkv, items_k};
+                tiles_q, tiles_k};
     if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
     const float scale = scale_of(opts, d);
     BwdArgs ba;
@@ -250,7 +257,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     ba.oc = oc; ba.os = os;
     ba.lse2 = lse2; ba.dvec = dvec;
     ba.dk = dk; ba.dv = dv;
-    ba.items = items_k; ba.nitems = ctrl + 2;
+    ba.tiles = tiles_k; ba.ntiles = ctrl;
     ba.ttot = dims->ttot; ba.hq = dims->hq; ba.hkv = dims->hkv;
     ba.scale = scale;
     ba.c1 = scale * 1.4426950408889634f;
@@ -263,7 +270,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     qd.oc = oc; qd.os = os;
     qd.lse2 = lse2; qd.dvec = dvec;
     qd.dq = dq;
-    qd.items = items_q; qd.nitems = ctrl;
+    qd.tiles = tiles_q; qd.ntiles = ctrl;
     qd.ttot = dims->ttot; qd.hq = dims->hq; qd.hkv = dims->hkv;
     qd.scale = scale;
     qd.c1 = ba.c1;

@@ -21,6 +21,8 @@
 // dK and dV accumulate in registers across the query heads of the group
 // (GQA sum in fp32) and are written once.  dQ is the query-major pass
 // (dq.hip), which rebuilds the same dS-hat bit for bit.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -47,9 +49,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     constexpr int NQ = kQStep * D / 16 / 256;     // 16-byte chunks per thread of a 64-row code tile
     __shared__ BwdSmem<D> sm;
 
-    if ((int)blockIdx.x >= *a.nitems) return;
-    const int4 it = a.items[blockIdx.x];
-    const int k0 = it.x, ds = it.y, de = it.z, g = it.w;
+    const int ti = (int)blockIdx.x / a.hkv;
+    if (ti >= *a.ntiles) return;
+    const int4 it = a.tiles[ti];
+    const int k0 = it.x, ds = it.y, de = it.z;
+    const int g = (int)blockIdx.x - ti * a.hkv;
     const int G = a.hq / a.hkv;
     const int L = de - ds;
     const int kt0 = k0 - ds;
@@ -130,7 +134,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     const float inv256 = 1.f / 256.f;
 
     int hh = 0, q0 = kt0;
-    for (;;) {
+    // One 64-query step; MASK marks the steps that meet the causal boundary
+    // (the first two of every head, starting at the diagonal).  Returns
+    // whether another step follows.
+    auto step = [&](auto mask_tag) -> bool {
+        constexpr bool MASK = decltype(mask_tag)::value;
         // ---- publish the prefetched step in LDS, start fetching the next one
         __syncthreads();
         store_step();
@@ -164,7 +172,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             }
         }
         // ---- P, P-hat_b, dS, dS-hat (one 32x32 block per accumulator tile)
-        const bool overlap = qs0 < kt0 + kTile;    // step meets the causal boundary
+        // accumulator register i = 4j + r of query block st holds query
+        // qs0 + 32st + 8j + 4lg + r; masked while the wave's key lies after it
+        const int lim = key_loc - qs0 - 4 * lg;
         int pbc[2][4], dsc[2][4], es[2];   // es: dS block exponent + 127 per query block
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
@@ -180,14 +190,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
                 for (int r = 0; r < 4; ++r) {
                     const int i = 4 * j + r;
                     float p = exp2_fast(fmaf(sacc[st][i], a.c1, -lq[r]));
-                    if (overlap && key_loc > qs0 + q4 + r) p = 0.f;
+                    if constexpr (MASK)
+                        if (32 * st + 8 * j + r < lim) p = 0.f;
                     sacc[st][i] = p;
                     const float dsi = p * (pacc[st][i] - dq[r]);
                     dsv[i] = dsi;
                     amax = fmaxf(amax, fabsf(dsi));
                 }
             }
-            amax = wave_max(amax);
+            amax = wave_max_nonneg(amax);
             const int e = block_exponent(amax, -126);
             es[st] = e + 127;
             const float sc = __uint_as_float((uint32_t)(e + 127) << 23);   // 2^e
@@ -218,7 +229,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
                 dkt[dt] = mfma_mx(qa, db, dkt[dt], sq, es[lg]);
             }
         }
-        if (!more) break;
+        return more;
+    };
+    // two loops instead of a per-step choice, so that both bodies keep the
+    // accumulators in the same registers
+    bool more = true;
+    while (more) {
+        while (more && q0 < kt0 + kTile) more = step(std::true_type{});
+        while (more && q0 >= kt0 + kTile) more = step(std::false_type{});
     }
     // ---- epilogue: dK = softmax_scale * sum, dV; summed over the group's heads
     if (key_valid) {

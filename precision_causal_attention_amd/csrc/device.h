@@ -43,7 +43,9 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
 }
 // Same with an exact power-of-two divisor: byte i = E4M3(x_i / scale).
 __device__ __forceinline__ int pack_fp8x4_div(float a, float b, float c, float d, float scale) {
-    v2s w = v2s{0, 0};
+    // both halves are overwritten, so the incoming register content is irrelevant
+    v2s w;
+    __builtin_memcpy(&w, &a, 4);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, scale, false);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, scale, true);
     int out;
@@ -122,14 +124,6 @@ __device__ __forceinline__ int block_exponent(float amax, int lo) {
 // v_permlane16_swap / v_permlane32_swap across rows.  Each swap returns the
 // pair {own value, partner value} (order depends on the lane), so a
 // commutative combine of the two halves gives the same result in both lanes.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float max_xor16(float v) {      // rows 0<->1, 2<->3
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 __device__ __forceinline__ float max_xor32(float v) {      // lanes l <-> l ^ 32
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -138,14 +132,34 @@ __device__ __forceinline__ float add_xor32(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-// Maximum over all 64 lanes, returned in every lane.
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp<0xB1>(v));     // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp<0x4E>(v));     // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp<0x141>(v));    // row_half_mirror: the two quads of each 8
-    v = fmaxf(v, dpp<0x140>(v));    // row_mirror: the two halves of each 16
-    v = max_xor16(v);
-    return max_xor32(v);
+// Maximum over all 64 lanes of a non-negative value (+0 included, no NaN),
+// returned in every lane.  Non-negative IEEE floats order like their bit
+// patterns, so the reduction runs on unsigned integers: no NaN quieting, and
+// each DPP step fuses into one v_max_u32_dpp.
+template <int CTRL>
+__device__ __forceinline__ uint32_t umax_dpp(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    uint32_t v = __float_as_uint(x);
+    v = umax_dpp<0xB1>(v);          // quad_perm [1,0,3,2]
+    v = umax_dpp<0x4E>(v);          // quad_perm [2,3,0,1]
+    v = umax_dpp<0x141>(v);         // row_half_mirror: the two quads of each 8
+    v = umax_dpp<0x140>(v);         // row_mirror: the two halves of each 16
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);   // rows 0<->1, 2<->3
+    v = max((uint32_t)r[0], (uint32_t)r[1]);
+    r = __builtin_amdgcn_permlane32_swap(v, v, false, false);        // lanes l <-> l ^ 32
+    return __uint_as_float(max((uint32_t)r[0], (uint32_t)r[1]));
+}
+
+// Head of work item `local` (0 <= local < heads) of one tile.  Workgroups
+// are dispatched round-robin over the 8 XCDs (workgroup index % 8), each
+// with its own L2.  When heads % 8 == 0 the tile's items start at a multiple
+// of 8, and XCD x receives the contiguous heads x*heads/8 .. (x+1)*heads/8 - 1,
+// so query heads that share a key/value head (GQA) read its tiles through the
+// same L2.
+__device__ __forceinline__ int xcd_head(int local, int heads) {
+    return (heads & 7) ? local : (local & 7) * (heads >> 3) + (local >> 3);
 }
 
 // Position of document `doc`'s boundaries; binary search of the largest

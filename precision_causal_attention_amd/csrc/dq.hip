@@ -17,6 +17,8 @@
 // the key-major pass (role-swapped MFMA operands give identical bits), so
 // dS-hat here is bitwise the payload the key-major pass feeds to dK.  dQ is
 // owned by one workgroup: no atomics, deterministic, written once as bf16.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -39,9 +41,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
     constexpr int CHUNKS = kTile * D / 16;
     __shared__ DqSmem<D> sm;
 
-    if ((int)blockIdx.x >= *a.nitems) return;
-    const int4 it = a.items[blockIdx.x];
-    const int q0 = it.x, ds = it.y, de = it.z, h = it.w;
+    const int ti = (int)blockIdx.x / a.hq;
+    if (ti >= *a.ntiles) return;
+    const int4 it = a.tiles[ti];
+    const int q0 = it.x, ds = it.y, de = it.z;
+    const int h = xcd_head((int)blockIdx.x - ti * a.hq, a.hq);
     const int g = h / (a.hq / a.hkv);
     const int L = de - ds;
     const int lq0 = q0 - ds;
@@ -85,7 +89,10 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
     uint32_t ekr, evr;
     fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds, a.ttot, a.hkv, g, tid);
 
-    for (int t = 0; t < ntiles; ++t) {
+    // One 128-key tile; DIAG marks the last (diagonal) tile, the only one that
+    // needs the causal mask and the only one with nothing left to prefetch.
+    auto tile = [&](const int t, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < CHUNKS / 256; ++r) {
@@ -99,12 +106,12 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
             sm.ev[tid] = (uint8_t)evr;
         }
         __syncthreads();
-        // unconditional (the last iteration re-fetches its own tile): a
-        // conditional update would keep the prefetch registers in scratch
-        fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds + kTile * min(t + 1, ntiles - 1),
-                         a.ttot, a.hkv, g, tid);
+        if constexpr (!DIAG)
+            fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds + kTile * (t + 1), a.ttot, a.hkv, g, tid);
 
-        const bool diag = (t == ntiles - 1);
+        // accumulator register i of sub-tile kk holds key 128t + 32kk + 8(i/4)
+        // + 4lg + i%4; on the diagonal tile it is masked past the lane's query
+        const int lim = q_loc - kTile * t - 4 * lg;
         int dsc[4][4], es[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -126,15 +133,13 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 float p = exp2_fast(fmaf(s[i], a.c1, -lse));
-                if (diag) {
-                    const int key = kTile * t + 32 * kk + 8 * (i >> 2) + 4 * lg + (i & 3);
-                    if (key > q_loc) p = 0.f;
-                }
+                if constexpr (DIAG)
+                    if (32 * kk + 8 * (i >> 2) + (i & 3) > lim) p = 0.f;
                 const float d = p * (dp[i] - Dq);
                 dsv[i] = d;
                 amax = fmaxf(amax, fabsf(d));
             }
-            amax = wave_max(amax);
+            amax = wave_max_nonneg(amax);
             const int e = block_exponent(amax, -126);
             es[kk] = e + 127;
             const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
@@ -159,7 +164,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
                 acc[dt] = mfma_mx(ka, db, acc[dt], sk, sd);
             }
         }
-    }
+    };
+    for (int t = 0; t + 1 < ntiles; ++t) tile(t, std::false_type{});
+    tile(ntiles - 1, std::true_type{});
     // ---- epilogue: dQ = softmax_scale * sum, bf16
     if (q_valid) {
         uint16_t* qp = a.dq + ((long)(ds + q_loc) * a.hq + h) * D;

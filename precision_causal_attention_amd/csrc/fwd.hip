@@ -18,6 +18,8 @@
 //                                 layout), scale of each 32-key block of V.
 // The accumulator layout puts one query per lane column, so the online-softmax
 // statistics are per-lane scalars (plus one exchange between lane halves).
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -40,9 +42,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
     constexpr int CHUNKS = kTile * D / 16;        // 16-byte chunks of one code tile
     __shared__ FwdSmem<D> sm;
 
-    if ((int)blockIdx.x >= *a.nitems) return;
-    const int4 it = a.items[blockIdx.x];
-    const int q0 = it.x, ds = it.y, de = it.z, h = it.w;
+    const int ti = (int)blockIdx.x / a.hq;
+    if (ti >= *a.ntiles) return;
+    const int4 it = a.tiles[ti];
+    const int q0 = it.x, ds = it.y, de = it.z;
+    const int h = xcd_head((int)blockIdx.x - ti * a.hq, a.hq);
     const int g = h / (a.hq / a.hkv);
     const int L = de - ds;
     const int lq0 = q0 - ds;
@@ -84,7 +88,10 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
     uint32_t ekr, evr;
     fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds, a.ttot, a.hkv, g, tid);
 
-    for (int t = 0; t < ntiles; ++t) {
+    // One 128-key tile; DIAG marks the last (diagonal) tile, the only one that
+    // needs the causal mask and the only one with nothing left to prefetch.
+    auto tile = [&](const int t, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < CHUNKS / 256; ++r) {
@@ -98,10 +105,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
             sm.ev[tid] = (uint8_t)evr;
         }
         __syncthreads();
-        // unconditional (the last iteration re-fetches its own tile): a
-        // conditional update would keep the prefetch registers in scratch
-        fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds + kTile * min(t + 1, ntiles - 1),
-                         a.ttot, a.hkv, g, tid);
+        if constexpr (!DIAG)
+            fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds + kTile * (t + 1), a.ttot, a.hkv, g, tid);
 
         // ---- S^T = K^ Q^T for the 4 sub-tiles of 32 keys
         v16f s[4];
@@ -117,18 +122,18 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
                 s[kk] = mfma_mx(ka, qb[kc], s[kk], sm.ek[row], eq);
             }
         }
-        // ---- causal mask on the diagonal tile only; tile maximum on the raw
-        // scores (rounding is monotonic, so max(S) * c1 = max(S * c1) exactly)
-        const bool diag = (t == ntiles - 1);
+        // ---- causal mask (diagonal tile only): accumulator register i of
+        // sub-tile kk holds key 128t + 32kk + 8(i/4) + 4lg + i%4; it is masked
+        // when that key lies after the lane's query.  Tile maximum on the raw
+        // scores (rounding is monotonic, so max(S) * c1 = max(S * c1) exactly).
         float smax = -INFINITY;
+        const int lim = q_loc - kTile * t - 4 * lg;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                if (diag) {
-                    const int key = kTile * t + 32 * kk + 8 * (i >> 2) + 4 * lg + (i & 3);
-                    if (key > q_loc) s[kk][i] = -INFINITY;
-                }
+                if constexpr (DIAG)
+                    if (32 * kk + 8 * (i >> 2) + (i & 3) > lim) s[kk][i] = -INFINITY;
                 smax = fmaxf(smax, s[kk][i]);
             }
         const float mu = max_xor32(smax) * a.c1;
@@ -176,7 +181,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
                 acc[dt] = mfma_mx(va, pb, acc[dt], sv, 127);
             }
         }
-    }
+    };
+    for (int t = 0; t + 1 < ntiles; ++t) tile(t, std::false_type{});
+    tile(ntiles - 1, std::true_type{});
     // ---- epilogue: O = acc / l (both carry the 2^c factor), lse2 = m + log2(l/2^c)
     const float lt = add_xor32(l);
     if (q_valid) {

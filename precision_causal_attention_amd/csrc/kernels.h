@@ -8,19 +8,29 @@ namespace flamia {
 constexpr int kTile = 128;     // query and key tile (B_r = B_c = 128)
 constexpr int kBlock = 32;     // token block of the operand scales and of the dS blocks
 
-struct QuantArgs {
+// One tensor of a quantization launch: bf16 [T][heads][d] in, E4M3 codes
+// [T][heads][d] and UE8M0 scales [heads][T] out.
+struct QuantTensor {
     const uint16_t* x;
-    const int32_t* cu;
-    int ndocs, ttot, heads, d;
     uint8_t* codes;
     uint8_t* scales;
-    // dO variant only (nullptr otherwise): D = dO~ . O
+    int heads;
+};
+
+struct QuantArgs {
+    const int32_t* cu;
+    int ndocs, ttot, d;
+    QuantTensor t[3];
+    int ntensors;
+    // dO variant only (nullptr otherwise; then t[0] is dO): D = dO~ . O
     const uint16_t* o;
     float* dvec;
 };
 
-// Work items: int4 {first token of the tile (global), document start,
-// document end, head}.
+// Tile lists: int4 {first token of the 128-token tile (global), document
+// start, document end, 0}, ordered by decreasing cost; ctrl[0] holds the
+// number of tiles.  A work item is (tile, head): the attention kernels
+// decode it from the workgroup index (tile = index / heads).
 struct PlanArgs {
     const int32_t* cu;
     int ndocs;
@@ -28,18 +38,17 @@ struct PlanArgs {
     int32_t* tiles_prefix; // [ndocs + 1]
     int32_t* ctrl;         // control block, see plan.hip
     long max_tiles;
-    int heads_q;           // query-major list: cost = tile index + 1 (forward, dQ)
-    int4* items_q;
-    int heads_k;           // key-major list: cost = tiles from the diagonal to the end (dK/dV);
-    int4* items_k;         // nullptr: not built
+    int4* tiles_q;         // query-major order: cost = tile index + 1 (forward, dQ)
+    int4* tiles_k;         // key-major order: cost = tiles from the diagonal to the end
+                           // (dK/dV); nullptr: not built
 };
 
 struct FwdArgs {
     const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;
     uint16_t* o;
     float* lse2;
-    const int4* items;
-    const int32_t* nitems;
+    const int4* tiles;
+    const int32_t* ntiles;
     int ttot, hq, hkv;
     float c1;              // softmax_scale * log2(e)
     float c_log2, tau;
@@ -51,8 +60,8 @@ struct BwdArgs {
     const float* lse2;
     const float* dvec;
     uint16_t *dk, *dv;
-    const int4* items;
-    const int32_t* nitems;
+    const int4* tiles;
+    const int32_t* ntiles;
     int ttot, hq, hkv;
     float c1, scale;
 };
@@ -62,8 +71,8 @@ struct DqArgs {
     const float* lse2;
     const float* dvec;
     uint16_t* dq;
-    const int4* items;
-    const int32_t* nitems;
+    const int4* tiles;
+    const int32_t* ntiles;
     int ttot, hq, hkv;
     float c1, scale;
 };

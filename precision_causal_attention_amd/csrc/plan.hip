@@ -1,22 +1,22 @@
-// GPU-built, cost-sorted work lists (FLAMIA paper, Section 3.6.2 and
-// Appendix B.6): built once per call on the device, no host synchronization,
-// a fixed number of launches.
+// GPU-built, cost-sorted tile lists (FLAMIA paper, Section 3.6.2 and
+// Appendix B.6): built on the device in one single-workgroup launch, no
+// host synchronization.
 //
-// A tile item is (document, 128-token tile t, head).  A document of L tokens
-// has n = ceil(L/128) tiles, anchored at its first token.
-//   forward : query tile t attends t+1 key tiles      -> cost t + 1
-//   backward: key tile t meets n - t query tiles      -> cost n - t
+// A document of L tokens has n = ceil(L/128) tiles of 128 tokens, anchored at
+// its first token.
+//   query-major (forward, dQ): query tile t attends t+1 key tiles  -> cost t + 1
+//   key-major (dK/dV)        : key tile t meets n - t query tiles  -> cost n - t
 // Both give every document the costs 1..n, so one histogram serves both.
-// Items are ordered by decreasing cost (longest first; the hardware dispatches
-// workgroups in index order, so the expensive items start first and the
-// cheap ones fill in at the end).  Sorting is a counting sort on the small
-// integer cost instead of a comparison sort.  Within one cost class the order
-// is whatever the atomics give; it does not change any result.
+// Tiles are ordered by decreasing cost (longest first; the hardware
+// dispatches workgroups in index order, so the expensive items start first
+// and the cheap ones fill in at the end).  Sorting is a counting sort on the
+// small integer cost instead of a comparison sort.  Within one cost class the
+// order is whatever the atomics give; it does not change any result.
+// Work item (tile, head) is decoded by the attention kernels from the
+// workgroup index, heads innermost.
 //
-// ctrl layout (int32): [0] query-major item count, [1] tile count,
-//   [2] key-major item count, [16, 16+C1) offset of each cost class,
-//   [16+C1, 16+2 C1) query-major cursors, [16+2 C1, 16+3 C1) key-major cursors
-//   (C1 = max_cost + 1).
+// ctrl layout (int32): [0] number of tiles, [16, 16+C1) query-major cursors,
+// [16+C1, 16+2 C1) key-major cursors (C1 = max_cost + 1).
 #include "device.h"
 #include "kernels.h"
 
@@ -50,8 +50,8 @@ __device__ void block_scan(int* buf, int n, bool reverse, int* partial) {
 }
 
 __global__ void __launch_bounds__(kPlanThreads)
-plan_count_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost,
-                  int32_t* __restrict__ tiles_prefix, int32_t* __restrict__ ctrl, int heads_q, int heads_k) {
+plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __restrict__ tiles_prefix,
+            int32_t* __restrict__ ctrl, long max_tiles, int4* __restrict__ tiles_q, int4* __restrict__ tiles_k) {
     extern __shared__ int smem[];
     int* partial = smem;                       // kPlanThreads
     int* hist = smem + kPlanThreads;           // max_cost + 1
@@ -65,30 +65,18 @@ plan_count_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost,
         if (n > 0) atomicAdd(&hist[n], 1);
     }
     __syncthreads();
-    block_scan(hist, C1, true, partial);       // hist[c] = #docs with n >= c = items of cost c
-    int* cnt = hist;
-    // offsets: classes ordered by decreasing cost -> exclusive suffix sum
-    for (int c = tid; c < C1; c += kPlanThreads) ctrl[16 + c] = cnt[c];
-    __syncthreads();
-    // exclusive suffix of cnt over c >= 1, in place in LDS (hist reused)
-    for (int c = tid; c < C1; c += kPlanThreads) hist[c] = c >= 1 ? ctrl[16 + c] : 0;
-    __syncthreads();
-    block_scan(hist, C1, true, partial);       // inclusive suffix
+    // hist[c] = #docs with n >= c = number of tiles of cost c (c >= 1)
+    block_scan(hist, C1, true, partial);
+    // hist[c] = number of tiles of cost >= c; the class of cost c starts at
+    // hist[c + 1] (classes by decreasing cost) and hist[1] is the total
+    block_scan(hist, C1, true, partial);
+    const int total = C1 > 1 ? (int)min((long)hist[1], max_tiles) : 0;
     for (int c = tid; c < C1; c += kPlanThreads) {
-        const int incl = hist[c];
-        const int own = c >= 1 ? ctrl[16 + c] : 0;
-        ctrl[16 + c] = incl - own;             // exclusive: sum over c' > c
-        ctrl[16 + C1 + c] = 0;                 // cursors
-        ctrl[16 + 2 * C1 + c] = 0;
+        ctrl[16 + c] = 0;                      // query-major cursors
+        ctrl[16 + C1 + c] = 0;                 // key-major cursors
     }
-    if (tid == 0) {
-        ctrl[1] = hist[1];                     // all tiles
-        ctrl[0] = hist[1] * heads_q;
-        ctrl[2] = hist[1] * heads_k;
-    }
-    __syncthreads();
+    if (tid == 0) ctrl[0] = total;
     // exclusive prefix of tile counts over documents
-    // (chunked over the documents; reuses `hist` as a staging buffer of kPlanThreads)
     {
         const int chunk = (ndocs + kPlanThreads - 1) / kPlanThreads;
         const int lo = tid * chunk, hi = min(lo + chunk, ndocs);
@@ -96,8 +84,8 @@ plan_count_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost,
         for (int d = lo; d < hi; ++d) sum += (cu[d + 1] - cu[d] + kTile - 1) / kTile;
         partial[tid] = sum;
         __syncthreads();
-        for (int off = 1; off < kPlanThreads; off <<= 1) {
-            const int v = tid >= off ? partial[tid - off] : 0;
+        for (int o = 1; o < kPlanThreads; o <<= 1) {
+            const int v = tid >= o ? partial[tid - o] : 0;
             __syncthreads();
             partial[tid] += v;
             __syncthreads();
@@ -109,41 +97,33 @@ plan_count_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost,
         }
         if (tid == kPlanThreads - 1) tiles_prefix[ndocs] = partial[kPlanThreads - 1];
     }
-}
-
-__global__ void __launch_bounds__(256)
-plan_fill_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost,
-                 const int32_t* __restrict__ tiles_prefix, int32_t* __restrict__ ctrl, long max_tiles,
-                 int heads_q, int4* __restrict__ items_q, int heads_k, int4* __restrict__ items_k) {
-    const long p = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    const int total = ctrl[1];
-    if (p >= total || p >= max_tiles) return;
-    const int doc = find_doc(tiles_prefix, ndocs, (int)p);
-    const int t = (int)p - tiles_prefix[doc];
-    const int n = tiles_prefix[doc + 1] - tiles_prefix[doc];
-    const int C1 = max_cost + 1;
-    const int ds = cu[doc], de = cu[doc + 1];
-    {
-        const int cost = t + 1;
-        const int slot = ctrl[16 + cost] + atomicAdd(&ctrl[16 + C1 + cost], 1);
-        for (int h = 0; h < heads_q; ++h) items_q[(long)slot * heads_q + h] = make_int4(ds + kTile * t, ds, de, h);
-    }
-    if (items_k) {
-        const int cost = n - t;
-        const int slot = ctrl[16 + cost] + atomicAdd(&ctrl[16 + 2 * C1 + cost], 1);
-        for (int h = 0; h < heads_k; ++h) items_k[(long)slot * heads_k + h] = make_int4(ds + kTile * t, ds, de, h);
+    // the cursor zeros and the prefix table must have reached L2 before any
+    // thread of the workgroup uses them
+    __threadfence();
+    __syncthreads();
+    for (int p = tid; p < total; p += kPlanThreads) {
+        const int doc = find_doc(tiles_prefix, ndocs, p);
+        const int t = p - tiles_prefix[doc];
+        const int n = tiles_prefix[doc + 1] - tiles_prefix[doc];
+        const int ds = cu[doc], de = cu[doc + 1];
+        const int4 tile = make_int4(ds + kTile * t, ds, de, 0);
+        {
+            const int cost = t + 1;
+            const int slot = (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&ctrl[16 + cost], 1);
+            if (slot < max_tiles) tiles_q[slot] = tile;
+        }
+        if (tiles_k) {
+            const int cost = n - t;
+            const int slot = (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&ctrl[16 + C1 + cost], 1);
+            if (slot < max_tiles) tiles_k[slot] = tile;
+        }
     }
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
     const size_t smem = sizeof(int) * (kPlanThreads + a.max_cost + 1);
-    hipLaunchKernelGGL(plan_count_kernel, dim3(1), dim3(kPlanThreads), smem, st, a.cu, a.ndocs, a.max_cost,
-                       a.tiles_prefix, a.ctrl, a.heads_q, a.items_k ? a.heads_k : 0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const unsigned blocks = (unsigned)((a.max_tiles + 255) / 256);
-    hipLaunchKernelGGL(plan_fill_kernel, dim3(blocks), dim3(256), 0, st, a.cu, a.ndocs, a.max_cost,
-                       a.tiles_prefix, a.ctrl, a.max_tiles, a.heads_q, a.items_q, a.heads_k, a.items_k);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), smem, st, a.cu, a.ndocs, a.max_cost,
+                       a.tiles_prefix, a.ctrl, a.max_tiles, a.tiles_q, a.tiles_k);
     return hipGetLastError();
 }
 

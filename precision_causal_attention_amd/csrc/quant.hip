@@ -1,110 +1,144 @@
-// Token-block quantization kernels (FLAMIA paper, Section 3.1 token-block
-// scaling, Section 3.2 rounded-up shared exponent, Section 3.5.1 one fused
-// launch per input tensor, Section 3.6.1 document-local blocks and dense
-// per-token scale tables).
+// Token-block quantization (FLAMIA paper, Section 3.1 token-block scaling,
+// Section 3.2 rounded-up shared exponent, Section 3.5.1 fused quantization
+// launch, Section 3.6.1 document-local blocks and dense per-token scale
+// tables).
 //
-// Grid: one workgroup per 32-token window of the packed axis.  A workgroup
-// owns every document-local block whose first token falls in its window (a
-// document contributes at most one block start per window), so all blocks are
-// covered exactly once without a host-side or device-side block list.
-// Four waves per workgroup; a wave quantizes one (block, head) pair at a time:
-// lane l carries token l/2 of the block and half l%2 of its d channels.
-// HBM-bound: the input is read once, codes and scales written once.
+// One launch quantizes up to three tensors of the packed layout [T][H][d]
+// (bf16 in, E4M3 codes [T][H][d] and one UE8M0 scale per (head, token) out).
+// Grid: x = head chunk of 4 heads (over all tensors of the launch), y = 32-token
+// window of the packed axis.  A workgroup owns every document-local block
+// whose first token falls in its window (a document contributes at most one
+// block start per window), so all blocks are covered exactly once without a
+// block list.  Wave w of the workgroup takes head 4 * chunk + w.
+// A wave quantizes one (block, head) pair of 32 tokens x d channels with all
+// loads and stores coalesced: chunk c = lane + 64 r (r < d/16) is the 16-byte
+// piece c % (d/8) of token c / (d/8), so each load instruction of the wave
+// reads whole 2d-byte rows.
+// HBM-bound: the input is read once, codes and scales are written once.
 #include "device.h"
 #include "kernels.h"
 
 namespace flamia {
 
-template <int D, bool kDO>
-__global__ void __launch_bounds__(256)
-quantize_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, int ndocs,
-                int ttot, int heads, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                const uint16_t* __restrict__ o, float* __restrict__ dvec) {
-    constexpr int HALF = D / 2;              // channels per lane
-    constexpr int NV = HALF / 8;             // 16-byte bf16 vectors per lane
-    const int w0 = blockIdx.x * kBlock;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int tok = lane >> 1, half = lane & 1;
-    if (ndocs <= 0 || w0 >= ttot) return;
+namespace {
 
-    for (int doc = find_doc(cu, ndocs, w0); doc < ndocs; ++doc) {
-        const int ds = cu[doc], de = cu[doc + 1];
+// Sum over the d/8 consecutive lanes that hold the chunks of one token
+// (8 lanes at d = 64, 16 at d = 128), returned in each of them.
+template <int CPT>
+__device__ __forceinline__ float token_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // lane ^ 1
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // lane ^ 2
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // other quad of 8
+    if constexpr (CPT == 16)
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // other 8 of 16
+    return v;
+}
+
+}  // namespace
+
+template <int D, bool kDO>
+__global__ void __launch_bounds__(256) quantize_kernel(const QuantArgs a) {
+    constexpr int CPT = D / 8;               // 16-byte bf16 chunks per token row
+    constexpr int R = kBlock * CPT / 64;     // chunks per lane
+    const int w0 = blockIdx.y * kBlock;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (a.ndocs <= 0 || w0 >= a.ttot) return;
+
+    // tensor and head of this wave
+    int chunk = blockIdx.x, ti = 0;
+    while (ti < a.ntensors && chunk >= (a.t[ti].heads + 3) / 4) { chunk -= (a.t[ti].heads + 3) / 4; ++ti; }
+    if (ti >= a.ntensors) return;
+    const QuantTensor tz = a.t[ti];
+    const int h = 4 * chunk + wave;
+    if (h >= tz.heads) return;
+    const int H = tz.heads;
+
+    const int ch = lane % CPT;               // chunk of the token row
+    const int tok0 = lane / CPT;             // token of chunk r is tok0 + r * (64 / CPT)
+
+    for (int doc = find_doc(a.cu, a.ndocs, w0); doc < a.ndocs; ++doc) {
+        const int ds = a.cu[doc], de = a.cu[doc + 1];
         if (ds >= w0 + kBlock) break;
         if (de <= w0) continue;
         const int rel = w0 - ds;
         const int bs = rel <= 0 ? ds : ds + ((rel + kBlock - 1) / kBlock) * kBlock;
         if (bs >= w0 + kBlock || bs >= de) continue;
         const int nt = min(kBlock, de - bs);
-        const bool active = tok < nt;
-        const int t = bs + (active ? tok : 0);
 
-        for (int h = wave; h < heads; h += 4) {
-            const long base = ((long)t * heads + h) * D + half * HALF;
-            float v[HALF];
-            float amax = 0.f;
+        float v[R][8];
+        float amax = 0.f;
 #pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                uint4 u = active ? *reinterpret_cast<const uint4*>(x + base + 8 * j) : make_uint4(0, 0, 0, 0);
+        for (int r = 0; r < R; ++r) {
+            const int tok = tok0 + r * (64 / CPT);
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (tok < nt) u = *reinterpret_cast<const uint4*>(tz.x + ((long)(bs + tok) * H + h) * D + 8 * ch);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[r][2 * k] = bf16_to_f32(w[k] & 0xFFFFu);
+                v[r][2 * k + 1] = bf16_to_f32(w[k] >> 16);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[r][k]));
+        }
+        amax = wave_max_nonneg(amax);
+        const int e = block_exponent(amax, -127);
+        // codes = E4M3(x * 2^-e): the power-of-two scaling is exact, the
+        // convert rounds to nearest even.
+        uint32_t packed[R][2];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int tok = tok0 + r * (64 / CPT);
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                packed[r][k] = (uint32_t)pack_fp8x4(ldexpf(v[r][4 * k], -e), ldexpf(v[r][4 * k + 1], -e),
+                                                    ldexpf(v[r][4 * k + 2], -e), ldexpf(v[r][4 * k + 3], -e));
+            if (tok < nt)
+                *reinterpret_cast<uint2*>(tz.codes + ((long)(bs + tok) * H + h) * D + 8 * ch) =
+                    make_uint2(packed[r][0], packed[r][1]);
+        }
+        if (lane < nt) tz.scales[(long)h * a.ttot + bs + lane] = (uint8_t)(e + 127);
+
+        if constexpr (kDO) {
+            // D_i = dO~_i . O_i with the dequantized dO and the bf16 output
+            // (paper, Section 3.3), fp32 accumulation: each lane sums its 8
+            // products code value x O (exact in fp32), the lanes of a token
+            // are summed, and the block factor 2^e is applied last (exact).
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int tok = tok0 + r * (64 / CPT);
+                uint4 u = make_uint4(0, 0, 0, 0);
+                if (tok < nt) u = *reinterpret_cast<const uint4*>(a.o + ((long)(bs + tok) * H + h) * D + 8 * ch);
                 const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    v[8 * j + 2 * k] = bf16_to_f32(w[k] & 0xFFFFu);
-                    v[8 * j + 2 * k + 1] = bf16_to_f32(w[k] >> 16);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < HALF; ++j) amax = fmaxf(amax, fabsf(v[j]));
-            amax = wave_max(amax);
-            const int e = block_exponent(amax, -127);
-            // codes = E4M3(x * 2^-e): the power-of-two scaling is exact, the
-            // convert rounds to nearest even.
-            uint32_t packed[HALF / 4];
-#pragma unroll
-            for (int j = 0; j < HALF / 4; ++j) {
-                packed[j] = (uint32_t)pack_fp8x4(ldexpf(v[4 * j], -e), ldexpf(v[4 * j + 1], -e),
-                                                 ldexpf(v[4 * j + 2], -e), ldexpf(v[4 * j + 3], -e));
-            }
-            if (active) {
-#pragma unroll
-                for (int j = 0; j < HALF / 16; ++j)
-                    *reinterpret_cast<uint4*>(codes + base + 16 * j) =
-                        make_uint4(packed[4 * j], packed[4 * j + 1], packed[4 * j + 2], packed[4 * j + 3]);
-                if (half == 0) scales[(long)h * ttot + t] = (uint8_t)(e + 127);
-            }
-            if constexpr (kDO) {
-                // D_i = dO~_i . O_i with the dequantized dO and the bf16 output
-                // (paper, Section 3.3), fp32 accumulation.
                 float dot = 0.f;
 #pragma unroll
-                for (int j = 0; j < NV; ++j) {
-                    uint4 u = active ? *reinterpret_cast<const uint4*>(o + base + 8 * j) : make_uint4(0, 0, 0, 0);
-                    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t cw = packed[(8 * j + 2 * k) / 4] >> (8 * ((8 * j + 2 * k) % 4));
-                        const float d0 = ldexpf(fp8_to_f32(cw & 0xFFu), e);
-                        const float d1 = ldexpf(fp8_to_f32((cw >> 8) & 0xFFu), e);
-                        dot = fmaf(d0, bf16_to_f32(w[k] & 0xFFFFu), dot);
-                        dot = fmaf(d1, bf16_to_f32(w[k] >> 16), dot);
-                    }
+                for (int k = 0; k < 2; ++k) {
+                    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)packed[r][k], false);
+                    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)packed[r][k], true);
+                    dot = fmaf(lo[0], bf16_to_f32(w[2 * k] & 0xFFFFu), dot);
+                    dot = fmaf(lo[1], bf16_to_f32(w[2 * k] >> 16), dot);
+                    dot = fmaf(hi[0], bf16_to_f32(w[2 * k + 1] & 0xFFFFu), dot);
+                    dot = fmaf(hi[1], bf16_to_f32(w[2 * k + 1] >> 16), dot);
                 }
-                dot += __shfl_xor(dot, 1, 64);
-                if (active && half == 0) dvec[(long)h * ttot + t] = dot;
+                dot = ldexpf(token_sum<CPT>(dot), e);
+                if (tok < nt && ch == 0) a.dvec[(long)h * a.ttot + bs + tok] = dot;
             }
         }
     }
 }
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
-    if (a.ttot <= 0) return hipSuccess;
-    const dim3 grid((a.ttot + kBlock - 1) / kBlock), block(256);
+    if (a.ttot <= 0 || a.ntensors <= 0) return hipSuccess;
+    int chunks = 0;
+    for (int i = 0; i < a.ntensors; ++i) chunks += (a.t[i].heads + 3) / 4;
+    const dim3 grid((unsigned)chunks, (unsigned)((a.ttot + kBlock - 1) / kBlock)), block(256);
     const bool dO = a.o != nullptr;
     if (a.d == 64) {
-        if (dO) hipLaunchKernelGGL((quantize_kernel<64, true>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec);
-        else hipLaunchKernelGGL((quantize_kernel<64, false>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec);
+        if (dO) hipLaunchKernelGGL((quantize_kernel<64, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((quantize_kernel<64, false>), grid, block, 0, st, a);
     } else {
-        if (dO) hipLaunchKernelGGL((quantize_kernel<128, true>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec);
-        else hipLaunchKernelGGL((quantize_kernel<128, false>), grid, block, 0, st, a.x, a.cu, a.ndocs, a.ttot, a.heads, a.codes, a.scales, a.o, a.dvec);
+        if (dO) hipLaunchKernelGGL((quantize_kernel<128, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((quantize_kernel<128, false>), grid, block, 0, st, a);
     }
     return hipGetLastError();
 }
