@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--workload", default="gqa-4x8k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a fill and a widening copy of this many MiB (known-size "
+                         "references for hardware byte counters collected over the same run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build runs the attention call on a single "
@@ -138,6 +141,15 @@ def main():
         else:
             call.opts.phase_events, call.opts.n_events = ctypes.cast(be, ctypes.POINTER(ctypes.c_void_p)), len(be)
         call.backward(do, cu, stream)
+
+    if args.copy_mib > 0:
+        # fill: writes N MiB; widening copy uint8 -> int16 (an elementwise
+        # kernel, not a DMA blit): reads N MiB, writes 2N MiB
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(args.copy_mib << 20, dtype=torch.int16, device="cuda")
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):

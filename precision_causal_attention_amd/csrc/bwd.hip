@@ -13,7 +13,8 @@
 //   dP [query][key] = dO^ V^T   same structure; both bitwise equal to the
 //                               forward's S^T (role-swapped operands give identical
 //                               accumulator bits on this hardware)
-//   P = 2^(x - lse2), P-hat_b = E4M3(2^8 P), dS = P (dP - D)
+//   P = 2^(x - lse2), P-hat_b = E4M3(2^8 P), dS = P (dP - D) (the dP product
+//   starts from -D)
 //   dS-hat: one exponent per 32x32 block = one accumulator tile (block max via
 //   a wave reduction):
 //   dV^T += dO^T P-hat_b   (A = dO^T by transposed LDS read, B = accumulator bytes)
@@ -36,7 +37,7 @@ struct BwdSmem {
     uint8_t q[kQStep * kStride];
     uint8_t o[kQStep * kStride];                 // quantized dO
     alignas(16) float lse[kQStep];
-    alignas(16) float dv[kQStep];                // D
+    alignas(16) float dv[kQStep];                // -D
     uint8_t eq[kQStep];
     uint8_t eo[kQStep];
 };
@@ -58,6 +59,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     const int L = de - ds;
     const int kt0 = k0 - ds;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // provably wave-uniform copy
     const int lg = lane >> 5, lr = lane & 31;
     const int key_loc = kt0 + 32 * wave + lr;
     const bool key_valid = key_loc < L;
@@ -101,7 +103,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             sm.eq[tid] = (uint8_t)p_eq;
             sm.eo[tid] = (uint8_t)p_eo;
             sm.lse[tid] = p_in ? p_lse : INFINITY;   // +inf: row outside the document
-            sm.dv[tid] = p_dv;
+            sm.dv[tid] = -p_dv;                       // -D: accumulator input of dP
         }
     };
     load_step(g * G, kt0);
@@ -152,13 +154,31 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
         // update would keep the prefetch registers in scratch
         load_step(g * G + min(hh, G - 1), q0);
 
+        // In a step that meets the causal boundary, the 32-query block st is
+        // block qb = (qs0 - kt0) / 32 + st of the key tile's diagonal: blocks
+        // qb < wave lie entirely before the wave's keys (P = 0, dS = 0) and
+        // are skipped, qb == wave is the only one that needs the mask.
+        const int qb0 = (qs0 - kt0) >> 5;
+        auto skipped = [&](int st) { return MASK && qb0 + st < wave_u; };
+        auto partial = [&](int st) { return MASK && qb0 + st == wave_u; };
         // ---- S and dP for the wave's 32 keys x 64 queries
         v16f sacc[2], pacc[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
+            if (skipped(st)) continue;
             const int row = 32 * st + lr;
             sacc[st] = v16f{0};
-            pacc[st] = v16f{0};
+            // dP starts from -D of each register's query (register 4j + r holds
+            // query 32st + 8j + 4lg + r): the MFMA returns dP - D directly, with
+            // the same error as a separate fp32 subtraction
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 d4 = *reinterpret_cast<const float4*>(&sm.dv[32 * st + 8 * j + 4 * lg]);
+                pacc[st][4 * j] = d4.x;
+                pacc[st][4 * j + 1] = d4.y;
+                pacc[st][4 * j + 2] = d4.z;
+                pacc[st][4 * j + 3] = d4.w;
+            }
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 uint4 lo = *reinterpret_cast<const uint4*>(&sm.q[row * STR + 64 * kc + 16 * lg]);
@@ -178,28 +198,33 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
         int pbc[2][4], dsc[2][4], es[2];   // es: dS block exponent + 127 per query block
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
+            if (skipped(st)) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pbc[st][j] = dsc[st][j] = 0;
+                es[st] = 127;
+                continue;
+            }
             float dsv[16];
             float amax = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int q4 = 32 * st + 8 * j + 4 * lg;            // 4 consecutive query rows
                 const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse[q4]);
-                const float4 d4 = *reinterpret_cast<const float4*>(&sm.dv[q4]);
-                const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq[4] = {d4.x, d4.y, d4.z, d4.w};
+                const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 4 * j + r;
                     float p = exp2_fast(fmaf(sacc[st][i], a.c1, -lq[r]));
-                    if constexpr (MASK)
+                    if (partial(st))
                         if (32 * st + 8 * j + r < lim) p = 0.f;
                     sacc[st][i] = p;
-                    const float dsi = p * (pacc[st][i] - dq[r]);
+                    const float dsi = p * pacc[st][i];
                     dsv[i] = dsi;
                     amax = fmaxf(amax, fabsf(dsi));
                 }
             }
             amax = wave_max_nonneg(amax);
-            const int e = block_exponent(amax, -126);
+            const int e = block_exponent_uniform(amax, -126);
             es[st] = e + 127;
             const float sc = __uint_as_float((uint32_t)(e + 127) << 23);   // 2^e
 #pragma unroll
@@ -210,7 +235,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             }
         }
         // ---- dV^T += dO^T P-hat_b and dK^T += Q^T dS-hat (contraction over the 64 queries)
-        {
+        if (!skipped(1)) {                     // (block 1 skipped implies block 0 skipped)
             const v8i pb = v8i{pbc[0][0], pbc[0][1], pbc[0][2], pbc[0][3], pbc[1][0], pbc[1][1], pbc[1][2], pbc[1][3]};
             const v8i db = v8i{dsc[0][0], dsc[0][1], dsc[0][2], dsc[0][3], dsc[1][0], dsc[1][1], dsc[1][2], dsc[1][3]};
             const int so = sm.eo[32 * lg], sq = sm.eq[32 * lg];
@@ -248,11 +273,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             for (int j = 0; j < 4; ++j) {
                 const int dd = 32 * dt + 8 * j + 4 * lg;
                 *reinterpret_cast<uint2*>(kp + dd) = make_uint2(
-                    f32_to_bf16(dkt[dt][4 * j] * a.scale) | (f32_to_bf16(dkt[dt][4 * j + 1] * a.scale) << 16),
-                    f32_to_bf16(dkt[dt][4 * j + 2] * a.scale) | (f32_to_bf16(dkt[dt][4 * j + 3] * a.scale) << 16));
+                    pack_bf16x2(dkt[dt][4 * j] * a.scale, dkt[dt][4 * j + 1] * a.scale),
+                    pack_bf16x2(dkt[dt][4 * j + 2] * a.scale, dkt[dt][4 * j + 3] * a.scale));
                 *reinterpret_cast<uint2*>(vp + dd) = make_uint2(
-                    f32_to_bf16(dvt[dt][4 * j]) | (f32_to_bf16(dvt[dt][4 * j + 1]) << 16),
-                    f32_to_bf16(dvt[dt][4 * j + 2]) | (f32_to_bf16(dvt[dt][4 * j + 3]) << 16));
+                    pack_bf16x2(dvt[dt][4 * j], dvt[dt][4 * j + 1]),
+                    pack_bf16x2(dvt[dt][4 * j + 2], dvt[dt][4 * j + 3]));
             }
     }
 }

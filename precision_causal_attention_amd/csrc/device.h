@@ -89,11 +89,15 @@ __device__ __forceinline__ float fp8_to_f32(uint32_t code) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
-// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two fp32 -> two bf16 packed in one word (a in the low half), round to
+// nearest even (one v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2_t r = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+    uint32_t u;
+    __builtin_memcpy(&u, &r, 4);
+    return u;
 }
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -118,6 +122,13 @@ __device__ __forceinline__ int block_exponent(float amax, int lo) {
     int e = E - 8 + (frac > 0x600000u ? 1 : 0);
     e = e < lo ? lo : e;
     return e > 127 ? 127 : e;
+}
+
+// block_exponent of a wave-uniform maximum, evaluated on the scalar unit
+// (the value is read from lane 0; every lane must hold the same value).
+__device__ __forceinline__ int block_exponent_uniform(float amax, int lo) {
+    const uint32_t u = __builtin_amdgcn_readfirstlane(__float_as_uint(amax));
+    return block_exponent(__uint_as_float(u), lo);
 }
 
 // Lane exchange without the LDS crossbar: DPP within 16-lane rows, then

@@ -9,7 +9,8 @@
 // Per 128-key tile:
 //   S^T [key][query] = K^ Q^T     (A = key rows from LDS, B = query rows in registers)
 //   dP^T[key][query] = V^ dO^T    (A = value rows from LDS, B = dO rows in registers)
-//   P = 2^(x - lse2), dS = P (dP - D); each 32x32 accumulator tile is one dS
+//   P = 2^(x - lse2), dS = P (dP - D) (the dP product starts from -D); each
+//   32x32 accumulator tile is one dS
 //   block: its maximum gives the exponent, the convert divides by 2^e
 //   dQ^T[d][query] += K^T dS-hat^T   (A = K^T by the transposing LDS read,
 //                                     B = dS-hat straight from the accumulators)
@@ -51,6 +52,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
     const int lq0 = q0 - ds;
     const int ntiles = lq0 / kTile + 1;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // provably wave-uniform copy
     const int lg = lane >> 5, lr = lane & 31;
     const int q_loc = lq0 + 32 * wave + lr;
     const bool q_valid = q_loc < L;
@@ -75,7 +77,13 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
     const int eo = a.os[(long)h * a.ttot + q_row];
     const float lse_raw = a.lse2[(long)h * a.ttot + q_row];
     const float lse = q_valid ? lse_raw : INFINITY;      // P = 0 on rows outside the document
-    const float Dq = a.dvec[(long)h * a.ttot + q_row];
+    // -D as the accumulator input of the dP^T product (every register of a
+    // lane belongs to the lane's query): the MFMA returns dP - D directly,
+    // with the same error as a separate fp32 subtraction
+    const float nD = -a.dvec[(long)h * a.ttot + q_row];
+    v16f negD;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negD[i] = nD;
 
     v16f acc[DT];
 #pragma unroll
@@ -112,11 +120,20 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
         // accumulator register i of sub-tile kk holds key 128t + 32kk + 8(i/4)
         // + 4lg + i%4; on the diagonal tile it is masked past the lane's query
         const int lim = q_loc - kTile * t - 4 * lg;
+        // On the diagonal tile, sub-tiles kk > wave lie entirely after every
+        // query of the wave (P = 0, dS = 0): skipped; only kk == wave needs
+        // the mask.
         int dsc[4][4], es[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+            if (DIAG && kk > wave_u) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dsc[kk][j] = 0;
+                es[kk] = 127;
+                continue;
+            }
             const int row = 32 * kk + lr;
-            v16f s = v16f{0}, dp = v16f{0};
+            v16f s = v16f{0}, dp = negD;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 uint4 lo = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 16 * lg]);
@@ -133,14 +150,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 float p = exp2_fast(fmaf(s[i], a.c1, -lse));
-                if constexpr (DIAG)
+                if (DIAG && kk == wave_u)
                     if (32 * kk + 8 * (i >> 2) + (i & 3) > lim) p = 0.f;
-                const float d = p * (dp[i] - Dq);
+                const float d = p * dp[i];
                 dsv[i] = d;
                 amax = fmaxf(amax, fabsf(d));
             }
             amax = wave_max_nonneg(amax);
-            const int e = block_exponent(amax, -126);
+            const int e = block_exponent_uniform(amax, -126);
             es[kk] = e + 127;
             const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
 #pragma unroll
@@ -150,6 +167,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
         // ---- dQ^T += K^T dS-hat^T, two 64-key chunks
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
+            if (DIAG && 2 * c > wave_u) continue;      // both sub-tiles skipped: dS-hat = 0
             const v8i db = v8i{dsc[2 * c][0], dsc[2 * c][1], dsc[2 * c][2], dsc[2 * c][3],
                                dsc[2 * c + 1][0], dsc[2 * c + 1][1], dsc[2 * c + 1][2], dsc[2 * c + 1][3]};
             const int sk = sm.ek[64 * c + 32 * lg];
@@ -174,9 +192,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t b0 = f32_to_bf16(acc[dt][4 * j] * a.scale), b1 = f32_to_bf16(acc[dt][4 * j + 1] * a.scale);
-                const uint32_t b2 = f32_to_bf16(acc[dt][4 * j + 2] * a.scale), b3 = f32_to_bf16(acc[dt][4 * j + 3] * a.scale);
-                *reinterpret_cast<uint2*>(qp + 32 * dt + 8 * j + 4 * lg) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                const uint32_t b01 = pack_bf16x2(acc[dt][4 * j] * a.scale, acc[dt][4 * j + 1] * a.scale);
+                const uint32_t b23 = pack_bf16x2(acc[dt][4 * j + 2] * a.scale, acc[dt][4 * j + 3] * a.scale);
+                *reinterpret_cast<uint2*>(qp + 32 * dt + 8 * j + 4 * lg) = make_uint2(b01, b23);
             }
     }
 }

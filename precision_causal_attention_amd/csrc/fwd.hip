@@ -52,6 +52,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
     const int lq0 = q0 - ds;
     const int ntiles = lq0 / kTile + 1;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // provably wave-uniform copy
     const int lg = lane >> 5, lr = lane & 31;
     const int q_loc = lq0 + 32 * wave + lr;       // document-local query of this lane
     const bool q_valid = q_loc < L;
@@ -108,10 +109,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
         if constexpr (!DIAG)
             fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds + kTile * (t + 1), a.ttot, a.hkv, g, tid);
 
+        // On the diagonal tile, sub-tiles kk > wave lie entirely after every
+        // query of the wave: they contribute p = 0, so they are skipped (no
+        // product, no exponential); sub-tile kk == wave is the only one that
+        // needs the mask, sub-tiles kk < wave lie entirely before the queries.
         // ---- S^T = K^ Q^T for the 4 sub-tiles of 32 keys
         v16f s[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+            if (DIAG && kk > wave_u) continue;
             const int row = 32 * kk + lr;
             s[kk] = v16f{0};
 #pragma unroll
@@ -122,20 +128,24 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
                 s[kk] = mfma_mx(ka, qb[kc], s[kk], sm.ek[row], eq);
             }
         }
-        // ---- causal mask (diagonal tile only): accumulator register i of
-        // sub-tile kk holds key 128t + 32kk + 8(i/4) + 4lg + i%4; it is masked
-        // when that key lies after the lane's query.  Tile maximum on the raw
-        // scores (rounding is monotonic, so max(S) * c1 = max(S * c1) exactly).
+        // ---- causal mask (sub-tile kk == wave of the diagonal tile):
+        // accumulator register i of sub-tile kk holds key 128t + 32kk +
+        // 8(i/4) + 4lg + i%4; it is masked when that key lies after the lane's
+        // query.  Tile maximum on the raw scores (rounding is monotonic, so
+        // max(S) * c1 = max(S * c1) exactly).
         float smax = -INFINITY;
         const int lim = q_loc - kTile * t - 4 * lg;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; ++kk) {
+            if (DIAG && kk > wave_u) continue;
+            if (DIAG && kk == wave_u) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if constexpr (DIAG)
+                for (int i = 0; i < 16; ++i)
                     if (32 * kk + 8 * (i >> 2) + (i & 3) > lim) s[kk][i] = -INFINITY;
-                smax = fmaxf(smax, s[kk][i]);
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) smax = fmaxf(smax, s[kk][i]);
+        }
         const float mu = max_xor32(smax) * a.c1;
         // ---- conditional running maximum (replace when exceeded by more than tau)
         const float m_new = (m == -INFINITY || mu - m > a.tau) ? mu : m;
@@ -156,6 +166,10 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                if (DIAG && kk > wave_u) {
+                    pc[kk][j] = 0;
+                    continue;
+                }
                 const float p0 = exp2_fast(fmaf(s[kk][4 * j], a.c1, nmc));
                 const float p1 = exp2_fast(fmaf(s[kk][4 * j + 1], a.c1, nmc));
                 const float p2 = exp2_fast(fmaf(s[kk][4 * j + 2], a.c1, nmc));
@@ -168,6 +182,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
         // ---- O^T += V^T P-hat^T, two 64-key chunks
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
+            if (DIAG && 2 * c > wave_u) continue;      // both sub-tiles skipped: P-hat = 0
             const v8i pb = v8i{pc[2 * c][0], pc[2 * c][1], pc[2 * c][2], pc[2 * c][3],
                                pc[2 * c + 1][0], pc[2 * c + 1][1], pc[2 * c + 1][2], pc[2 * c + 1][3]};
             const int sv = sm.ev[64 * c + 32 * lg];
@@ -193,9 +208,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t b0 = f32_to_bf16(acc[dt][4 * j] * inv), b1 = f32_to_bf16(acc[dt][4 * j + 1] * inv);
-                const uint32_t b2 = f32_to_bf16(acc[dt][4 * j + 2] * inv), b3 = f32_to_bf16(acc[dt][4 * j + 3] * inv);
-                *reinterpret_cast<uint2*>(op + 32 * dt + 8 * j + 4 * lg) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                const uint32_t b01 = pack_bf16x2(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv);
+                const uint32_t b23 = pack_bf16x2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv);
+                *reinterpret_cast<uint2*>(op + 32 * dt + 8 * j + 4 * lg) = make_uint2(b01, b23);
             }
         if (lg == 0) a.lse2[(long)h * a.ttot + ds + q_loc] = m + (log2_fast(lt) - a.c_log2);
     }

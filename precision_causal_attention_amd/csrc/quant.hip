@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const QuantArgs a) {
             for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[r][k]));
         }
         amax = wave_max_nonneg(amax);
-        const int e = block_exponent(amax, -127);
+        const int e = block_exponent_uniform(amax, -127);
         // codes = E4M3(x * 2^-e): the power-of-two scaling is exact, the
         // convert rounds to nearest even.
         uint32_t packed[R][2];
