@@ -101,6 +101,10 @@ def main():
     ap.add_argument("--workload", default="gqa-4x8k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--doclen-cap", type=int, default=-1,
+                    help="dS store capacity as the longest document; 0: no store, dQ rebuilds "
+                         "dS-hat.  Default: the row length at d = 128, where reading the stored "
+                         "blocks is faster on MI355X, and no store at d = 64, where rebuilding is")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a fill and a widening copy of this many MiB (known-size "
                          "references for hardware byte counters collected over the same run)")
@@ -125,7 +129,9 @@ def main():
     dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v, do = (dev(inst[n]) for n in ("q", "k", "v", "do"))
     cu = torch.from_numpy(inst["cu_seqlens"]).cuda()
-    call = F.TrainingCall(T, hq, hkv, d, ndocs_cap=ndocs)
+    # dS store sized for the longest possible document (a whole row), at d = 128
+    doclen_cap = (wl.row_len if d == 128 else 0) if args.doclen_cap < 0 else args.doclen_cap
+    call = F.TrainingCall(T, hq, hkv, d, ndocs_cap=ndocs, doclen_cap=doclen_cap)
     hip = Hip()
     nf, nb = len(FWD_PHASES) + 1, len(BWD_PHASES) + 1
     stream = torch.cuda.current_stream()
@@ -222,7 +228,7 @@ def main():
         "frac_of_mxfp8_peak": round(tflops / MXFP8_PEAK_TFLOPS, 4),
         "config": {"workload": wl.name, "rows": wl.rows, "row_len": wl.row_len, "tokens": T, "hq": hq,
                    "hkv": hkv, "d": d, "docs": ndocs, "sum_L2": sum_l2, "seed": args.seed,
-                   "doc_law": wl.docs, "parallelism": "single-gpu"},
+                   "doc_law": wl.docs, "doclen_cap": doclen_cap, "parallelism": "single-gpu"},
         "phases_ms": {p: round(t, 4) for p, t in phases.items()},
         "roofline": {"kernel": dom, "kernel_ms": round(dom_ms, 4), "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MXFP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MXFP8_PEAK_TFLOPS, 4),

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FLAMIA_ABI_VERSION 1
+#define FLAMIA_ABI_VERSION 2
 
 typedef enum {
     FLAMIA_OK = 0,
@@ -63,9 +63,16 @@ typedef enum {
 
 /* Host struct.  ttot_cap / ndocs_cap are the capacities the workspace is sized
  * for (Section 3.6.1: buffer capacities depend on T only); ttot <= ttot_cap,
- * ndocs <= ndocs_cap. */
+ * ndocs <= ndocs_cap.
+ * doclen_cap sizes the backward's dS store: the longest document the
+ * workspace keeps the quantized dS blocks for (at most ttot_cap; 0 = no store).
+ * With a store, the key-major pass writes each 32x32 dS-hat block once and the
+ * dQ pass reads it back instead of rebuilding S, P and dP; whether a call's
+ * documents fit is decided on the device, and a call that does not fit takes
+ * the rebuilding dQ pass (same result, bit for bit). */
 typedef struct {
     int32_t ttot, ttot_cap, ndocs, ndocs_cap, hq, hkv, d;
+    int32_t doclen_cap;
 } flamia_dims_t;
 
 /* Host struct of numerical options.  A NULL opts pointer means the defaults
@@ -102,9 +109,11 @@ const char *flamia_status_str(flamia_status_t s);
 const char *flamia_last_error(void);
 
 /* Bytes of device workspace that flamia_fwd / flamia_bwd need for these
- * capacities; depends on ttot_cap, ndocs_cap and the head counts only.
- * ttot and ndocs are ignored.  Returns 0 if dims is NULL or the head layout
- * or a capacity is invalid. */
+ * capacities; depends on ttot_cap, ndocs_cap, doclen_cap, d and the head
+ * counts only.  ttot and ndocs are ignored.  Returns 0 if dims is NULL or the
+ * head layout or a capacity is invalid.  With doclen_cap > 0 the dS store takes
+ * hq * B * 1025 bytes, B = (ttot_cap / 32 + ndocs_cap) * (ceil(doclen_cap / 32) + 1) / 2
+ * (a bound on the number of 32x32 causal blocks per head). */
 size_t flamia_workspace_bytes(const flamia_dims_t *dims, const flamia_opts_t *opts);
 
 /*
@@ -151,11 +160,13 @@ flamia_status_t flamia_fwd(const flamia_dims_t *dims, const flamia_opts_t *opts,
  *   dq                 : bf16 output [ttot][hq][d]
  *   dk, dv             : bf16 outputs [ttot][hkv][d] (summed over the query
  *                        heads of each group)
- *   ws / ws_bytes      : workspace (holds the dO codes and scales, D and the
- *                        work lists)
- * Two passes rebuild the same dS-hat payload: a key-major pass accumulates dK
- * and dV, a query-major pass accumulates dQ; each output element is owned by
- * one workgroup, so the backward is deterministic (no atomics).
+ *   ws / ws_bytes      : workspace (holds the dO codes and scales, D, the work
+ *                        lists and, with doclen_cap > 0, the dS store)
+ * A key-major pass accumulates dK and dV; a query-major pass accumulates dQ,
+ * either from the dS-hat blocks the key-major pass stored or, without a store
+ * (or when the call's documents do not fit it), by rebuilding the same dS-hat
+ * payload bit for bit.  Each output element is owned by one workgroup, so the
+ * backward is deterministic (no atomics).
  */
 flamia_status_t flamia_bwd(const flamia_dims_t *dims, const flamia_opts_t *opts,
                            const uint16_t *d_o, const uint16_t *o, const float *lse2,

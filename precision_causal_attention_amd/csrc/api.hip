@@ -30,6 +30,7 @@ flamia_status_t check_caps(const flamia_dims_t* d) {
     if (d->hq <= 0 || d->hkv <= 0 || d->hq % d->hkv) return FLAMIA_ERR_SHAPE;
     if (d->ttot_cap < 0 || d->ttot_cap > kMaxTokens) return FLAMIA_ERR_SHAPE;
     if (d->ndocs_cap < 0 || d->ndocs_cap > kMaxTokens) return FLAMIA_ERR_SHAPE;
+    if (d->doclen_cap < 0 || d->doclen_cap > d->ttot_cap) return FLAMIA_ERR_SHAPE;
     return FLAMIA_OK;
 }
 
@@ -58,7 +59,8 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Layout {
     long max_tiles;
     int max_cost;
-    size_t ctrl, prefix, tiles_q, tiles_k, ocodes, oscales, dvec, total;
+    long ds_blocks;        // dS store capacity, 32x32 blocks per head (0: none)
+    size_t ctrl, prefix, tiles_q, tiles_k, ocodes, oscales, dvec, dboff, ds_codes, ds_scales, total;
 };
 
 Layout layout(const flamia_dims_t* d) {
@@ -74,6 +76,18 @@ Layout layout(const flamia_dims_t* d) {
     w.ocodes = off;  off += up256((size_t)tc * d->hq * d->d);
     w.oscales = off; off += up256((size_t)tc * d->hq);
     w.dvec = off;    off += up256(sizeof(float) * (size_t)tc * d->hq);
+    // dS store: sum over documents of nb (nb + 1) / 2 with nb = ceil(L / 32)
+    // is at most (sum of nb) * (max nb + 1) / 2, sum of nb <= ttot / 32 + ndocs
+    if (d->doclen_cap > 0) {
+        const long nb_sum = tc / kBlock + d->ndocs_cap;
+        const long nb_max = (d->doclen_cap + kBlock - 1) / kBlock;
+        w.ds_blocks = nb_sum * (nb_max + 1) / 2;
+    } else {
+        w.ds_blocks = 0;
+    }
+    w.dboff = off;     off += up256(sizeof(int32_t) * ((size_t)d->ndocs_cap + 1));
+    w.ds_codes = off;  off += up256((size_t)w.ds_blocks * d->hq * kDsBlockBytes);
+    w.ds_scales = off; off += up256((size_t)w.ds_blocks * d->hq);
     w.total = off;
     return w;
 }
@@ -188,7 +202,7 @@ flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     int32_t* ctrl = (int32_t*)(base + w.ctrl);
     int4* tiles = (int4*)(base + w.tiles_q);
     PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
-                tiles, nullptr};
+                tiles, nullptr, nullptr, 0};
     if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
     FwdArgs fa;
     fa.qc = q_mx.codes; fa.qs = q_mx.scales;
@@ -246,8 +260,11 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     int32_t* ctrl = (int32_t*)(base + w.ctrl);
     int4* tiles_q = (int4*)(base + w.tiles_q);
     int4* tiles_k = (int4*)(base + w.tiles_k);
+    int32_t* dboff = (int32_t*)(base + w.dboff);
+    uint8_t* ds_codes = base + w.ds_codes;
+    uint8_t* ds_scales = base + w.ds_scales;
     PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
-                tiles_q, tiles_k};
+                tiles_q, tiles_k, dboff, w.ds_blocks};
     if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
     const float scale = scale_of(opts, d);
     BwdArgs ba;
@@ -261,6 +278,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     ba.ttot = dims->ttot; ba.hq = dims->hq; ba.hkv = dims->hkv;
     ba.scale = scale;
     ba.c1 = scale * 1.4426950408889634f;
+    ba.ds_codes = ds_codes; ba.ds_scales = ds_scales; ba.dboff = dboff; ba.ds_blocks = w.ds_blocks;
     if ((e = pm.mark()) != hipSuccess || (e = launch_bwd(ba, d, w.max_tiles * dims->hkv, st)) != hipSuccess)
         return hip_fail(e);
     DqArgs qd;
@@ -274,8 +292,13 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     qd.ttot = dims->ttot; qd.hq = dims->hq; qd.hkv = dims->hkv;
     qd.scale = scale;
     qd.c1 = ba.c1;
-    if ((e = pm.mark()) != hipSuccess || (e = launch_dq(qd, d, w.max_tiles * dims->hq, st)) != hipSuccess)
+    qd.ds_codes = ds_codes; qd.ds_scales = ds_scales; qd.dboff = dboff; qd.ds_blocks = w.ds_blocks;
+    // dQ: from the stored blocks when the call fits the store (decided on the
+    // device; the other kernel returns at once), else by rebuilding dS-hat
+    if ((e = pm.mark()) != hipSuccess) return hip_fail(e);
+    if (w.ds_blocks > 0 && (e = launch_dq_store(qd, d, w.max_tiles * dims->hq, st)) != hipSuccess)
         return hip_fail(e);
+    if ((e = launch_dq(qd, d, w.max_tiles * dims->hq, st)) != hipSuccess) return hip_fail(e);
     e = pm.mark();
     return e == hipSuccess ? FLAMIA_OK : hip_fail(e);
 }

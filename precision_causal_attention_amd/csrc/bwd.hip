@@ -53,8 +53,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     const int ti = (int)blockIdx.x / a.hkv;
     if (ti >= *a.ntiles) return;
     const int4 it = a.tiles[ti];
-    const int k0 = it.x, ds = it.y, de = it.z;
+    const int k0 = it.x, ds = it.y, de = it.z, doc = it.w;
     const int g = (int)blockIdx.x - ti * a.hkv;
+    // the dS store holds this call's blocks: write each dS-hat block once
+    const bool use_store = a.ntiles[1] != 0;
+    const long doc_blk = use_store ? (long)a.dboff[doc] : 0;
     const int G = a.hq / a.hkv;
     const int L = de - ds;
     const int kt0 = k0 - ds;
@@ -136,6 +139,21 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     const float inv256 = 1.f / 256.f;
 
     int hh = 0, q0 = kt0;
+    // dS blocks of the previous step, stored at the start of the next one
+    u32x4 pend_w[2];
+    long pend_blk[2] = {0, 0};
+    int pend_e[2] = {127, 127};
+    bool pend_ok[2] = {false, false};
+    auto flush_store = [&]() {
+        if (!use_store) return;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            if (!pend_ok[st]) continue;
+            *reinterpret_cast<u32x4*>(a.ds_codes + pend_blk[st] * kDsBlockBytes + 16 * lane) = pend_w[st];
+            if (lane == 0) a.ds_scales[pend_blk[st]] = (uint8_t)pend_e[st];
+            pend_ok[st] = false;
+        }
+    };
     // One 64-query step; MASK marks the steps that meet the causal boundary
     // (the first two of every head, starting at the diagonal).  Returns
     // whether another step follows.
@@ -150,6 +168,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
         q0 += kQStep;
         if (q0 >= L) { q0 = kt0; ++hh; }
         const bool more = hh < G;
+        flush_store();
         // unconditional (the last step re-fetches a valid step): a conditional
         // update would keep the prefetch registers in scratch
         load_step(g * G + min(hh, G - 1), q0);
@@ -234,6 +253,29 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
                 dsc[st][j] = pack_fp8x4_div(dsv[4 * j], dsv[4 * j + 1], dsv[4 * j + 2], dsv[4 * j + 3], sc);
             }
         }
+        // ---- dS store: block (qb, kb) as [query half][32 keys][16 queries]
+        // (lane l writes bytes 16 l .. 16 l + 15: whole lines per wave); lane
+        // half lg holds queries 8j + 4lg + (0..3) in word j and stores queries
+        // 16 lg .. 16 lg + 15 of its key after one exchange with lane l ^ 32.
+        // The stores are issued at the start of the next step, before its
+        // prefetch loads: vector memory operations complete in issue order,
+        // so a store issued after a load would make the wait for that load
+        // wait for the store as well.
+        if (use_store) {
+            const int kb = (kt0 >> 5) + wave_u;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                // skipped blocks lie above the diagonal; blocks past the end
+                // of the document do not exist in the store
+                pend_ok[st] = !skipped(st) && qs0 + 32 * st < L;
+                const int qb = (qs0 >> 5) + st;
+                pend_blk[st] = (long)h * a.ds_blocks + doc_blk + (long)qb * (qb + 1) / 2 + kb;
+                const auto x02 = __builtin_amdgcn_permlane32_swap(dsc[st][0], dsc[st][2], false, false);
+                const auto x13 = __builtin_amdgcn_permlane32_swap(dsc[st][1], dsc[st][3], false, false);
+                pend_w[st] = u32x4{(uint32_t)x02[0], (uint32_t)x02[1], (uint32_t)x13[0], (uint32_t)x13[1]};
+                pend_e[st] = es[st];
+            }
+        }
         // ---- dV^T += dO^T P-hat_b and dK^T += Q^T dS-hat (contraction over the 64 queries)
         if (!skipped(1)) {                     // (block 1 skipped implies block 0 skipped)
             const v8i pb = v8i{pbc[0][0], pbc[0][1], pbc[0][2], pbc[0][3], pbc[1][0], pbc[1][1], pbc[1][2], pbc[1][3]};
@@ -263,6 +305,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
         while (more && q0 < kt0 + kTile) more = step(std::true_type{});
         while (more && q0 >= kt0 + kTile) more = step(std::false_type{});
     }
+    flush_store();
     // ---- epilogue: dK = softmax_scale * sum, dV; summed over the group's heads
     if (key_valid) {
         uint16_t* kp = a.dk + ((long)(ds + key_loc) * a.hkv + g) * D;

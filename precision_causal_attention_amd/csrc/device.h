@@ -105,23 +105,17 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_floa
 // the smallest e with amax <= 448 * 2^e ("rounded up", so no element of the
 // block saturates), clamped to [lo, 127]; amax == 0 gives lo.
 __device__ __forceinline__ int block_exponent(float amax, int lo) {
+    // branch-free (selects only), so that callers stay one basic block
     const uint32_t u = __float_as_uint(amax);
-    int E;
-    uint32_t frac;             // 23-bit fraction of amax normalised to [1, 2)
-    if (u == 0u) return lo;
     const uint32_t ef = u >> 23;
-    if (ef != 0u) {
-        E = (int)ef - 127;
-        frac = u & 0x7FFFFFu;
-    } else {                   // fp32 subnormal: normalise the fraction
-        const int lz = __clz(u) - 8;          // leading zeros inside the 23-bit field + 1
-        E = -126 - lz;
-        frac = (u << lz) & 0x7FFFFFu;
-    }
+    const int lz = __clz(u) - 8;               // fp32 subnormal: leading zeros inside the fraction + 1
+    const int E = ef ? (int)ef - 127 : -126 - lz;
+    const uint32_t frac = ef ? (u & 0x7FFFFFu) : ((u << (lz & 31)) & 0x7FFFFFu);   // fraction of 1.f
     // mantissa 1.f > 1.75  <=>  frac > 0.75 * 2^23
     int e = E - 8 + (frac > 0x600000u ? 1 : 0);
     e = e < lo ? lo : e;
-    return e > 127 ? 127 : e;
+    e = e > 127 ? 127 : e;
+    return u == 0u ? lo : e;
 }
 
 // block_exponent of a wave-uniform maximum, evaluated on the scalar unit

@@ -42,6 +42,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
     constexpr int CHUNKS = kTile * D / 16;
     __shared__ DqSmem<D> sm;
 
+    if (a.ntiles[1] != 0) return;                    // the dS store is in use: dq_store.hip runs
     const int ti = (int)blockIdx.x / a.hq;
     if (ti >= *a.ntiles) return;
     const int4 it = a.tiles[ti];
@@ -123,55 +124,47 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
         // On the diagonal tile, sub-tiles kk > wave lie entirely after every
         // query of the wave (P = 0, dS = 0): skipped; only kk == wave needs
         // the mask.
-        int dsc[4][4], es[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            if (DIAG && kk > wave_u) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dsc[kk][j] = 0;
-                es[kk] = 127;
-                continue;
-            }
+        // S^T and dP^T of 32-key block kk (dP starts from -D)
+        auto products = [&](const int kk, v16f& sb, v16f& dpb) {
             const int row = 32 * kk + lr;
-            v16f s = v16f{0}, dp = negD;
+            sb = v16f{0};
+            dpb = negD;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 uint4 lo = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 16 * lg]);
                 uint4 hi = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 32 + 16 * lg]);
                 const v8i ka = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                s = mfma_mx(ka, qb[kc], s, sm.ek[row], eq);
+                sb = mfma_mx(ka, qb[kc], sb, sm.ek[row], eq);
                 lo = *reinterpret_cast<const uint4*>(&sm.v[row * STR + 64 * kc + 16 * lg]);
                 hi = *reinterpret_cast<const uint4*>(&sm.v[row * STR + 64 * kc + 32 + 16 * lg]);
                 const v8i va = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                dp = mfma_mx(va, ob[kc], dp, sm.ev[row], eo);
+                dpb = mfma_mx(va, ob[kc], dpb, sm.ev[row], eo);
             }
-            float dsv[16];
+        };
+        // P, dS and the dS-hat codes of block kk (in place in dpb); `masked`:
+        // the block holds the diagonal of the wave's queries
+        auto softmax = [&](const int kk, const v16f& sb, v16f& dpb, int (&codes)[4], int& ebyte, bool masked) {
             float amax = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float p = exp2_fast(fmaf(s[i], a.c1, -lse));
-                if (DIAG && kk == wave_u)
-                    if (32 * kk + 8 * (i >> 2) + (i & 3) > lim) p = 0.f;
-                const float d = p * dp[i];
-                dsv[i] = d;
-                amax = fmaxf(amax, fabsf(d));
+                float p = exp2_fast(fmaf(sb[i], a.c1, -lse));
+                if (masked && 32 * kk + 8 * (i >> 2) + (i & 3) > lim) p = 0.f;
+                dpb[i] = p * dpb[i];
+                amax = fmaxf(amax, fabsf(dpb[i]));
             }
             amax = wave_max_nonneg(amax);
             const int e = block_exponent_uniform(amax, -126);
-            es[kk] = e + 127;
+            ebyte = e + 127;
             const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                dsc[kk][j] = pack_fp8x4_div(dsv[4 * j], dsv[4 * j + 1], dsv[4 * j + 2], dsv[4 * j + 3], sc);
-        }
-        // ---- dQ^T += K^T dS-hat^T, two 64-key chunks
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            if (DIAG && 2 * c > wave_u) continue;      // both sub-tiles skipped: dS-hat = 0
-            const v8i db = v8i{dsc[2 * c][0], dsc[2 * c][1], dsc[2 * c][2], dsc[2 * c][3],
-                               dsc[2 * c + 1][0], dsc[2 * c + 1][1], dsc[2 * c + 1][2], dsc[2 * c + 1][3]};
+                codes[j] = pack_fp8x4_div(dpb[4 * j], dpb[4 * j + 1], dpb[4 * j + 2], dpb[4 * j + 3], sc);
+        };
+        // dQ^T += K^T dS-hat^T over the 64 keys of chunk c
+        auto dq_chunk = [&](const int c, const int (&c0)[4], const int (&c1)[4], int e0, int e1) {
+            const v8i db = v8i{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
             const int sk = sm.ek[64 * c + 32 * lg];
-            const int sd = lg ? es[2 * c + 1] : es[2 * c];
+            const int sd = lg ? e1 : e0;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 v2i r[4];
@@ -180,6 +173,42 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
                     r[rr] = lds_read_tr8(&sm.k[(64 * c + 16 * rr + tr_key) * STR + 32 * dt + tr_col]);
                 const v8i ka = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
                 acc[dt] = mfma_mx(ka, db, acc[dt], sk, sd);
+            }
+        };
+        int dsc[4][4], es[4];
+        if constexpr (!DIAG) {
+            // software pipeline: the products of block kk + 1 are issued before
+            // the softmax of block kk, so the matrix cores run under the VALU work
+            v16f sA, dpA, sB, dpB;
+            products(0, sA, dpA);
+            products(1, sB, dpB);
+            softmax(0, sA, dpA, dsc[0], es[0], false);
+            products(2, sA, dpA);
+            softmax(1, sB, dpB, dsc[1], es[1], false);
+            dq_chunk(0, dsc[0], dsc[1], es[0], es[1]);
+            products(3, sB, dpB);
+            softmax(2, sA, dpA, dsc[2], es[2], false);
+            softmax(3, sB, dpB, dsc[3], es[3], false);
+            dq_chunk(1, dsc[2], dsc[3], es[2], es[3]);
+        } else {
+            // diagonal tile: blocks kk > wave are skipped (P = 0), block
+            // kk == wave is masked
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk > wave_u) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) dsc[kk][j] = 0;
+                    es[kk] = 127;
+                    continue;
+                }
+                v16f sb, dpb;
+                products(kk, sb, dpb);
+                softmax(kk, sb, dpb, dsc[kk], es[kk], kk == wave_u);
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                if (2 * c > wave_u) continue;      // both blocks skipped: dS-hat = 0
+                dq_chunk(c, dsc[2 * c], dsc[2 * c + 1], es[2 * c], es[2 * c + 1]);
             }
         }
     };

@@ -28,9 +28,15 @@ struct QuantArgs {
 };
 
 // Tile lists: int4 {first token of the 128-token tile (global), document
-// start, document end, 0}, ordered by decreasing cost; ctrl[0] holds the
-// number of tiles.  A work item is (tile, head): the attention kernels
-// decode it from the workgroup index (tile = index / heads).
+// start, document end, document index}, ordered by decreasing cost; ctrl[0]
+// holds the number of tiles.  A work item is (tile, head): the attention
+// kernels decode it from the workgroup index (tile = index / heads).
+// dS store: per query head, the 32x32 causal blocks (qb >= kb, document-local
+// 32-token block indices) of every document; block (qb, kb) of document d is
+// block dboff[d] + qb (qb + 1) / 2 + kb of the head, 1024 code bytes
+// ([2][32][16]: query half, key, 16 queries) and one UE8M0 scale byte.
+constexpr int kDsBlockBytes = kBlock * kBlock;
+
 struct PlanArgs {
     const int32_t* cu;
     int ndocs;
@@ -41,6 +47,8 @@ struct PlanArgs {
     int4* tiles_q;         // query-major order: cost = tile index + 1 (forward, dQ)
     int4* tiles_k;         // key-major order: cost = tiles from the diagonal to the end
                            // (dK/dV); nullptr: not built
+    int32_t* dboff;        // [ndocs] first dS block of each document (nullptr: none)
+    long ds_blocks;        // dS store capacity in blocks per head (0: no store)
 };
 
 struct FwdArgs {
@@ -61,9 +69,13 @@ struct BwdArgs {
     const float* dvec;
     uint16_t *dk, *dv;
     const int4* tiles;
-    const int32_t* ntiles;
+    const int32_t* ntiles;    // ntiles[1] != 0: store dS-hat blocks
     int ttot, hq, hkv;
     float c1, scale;
+    uint8_t* ds_codes;        // dS store (see PlanArgs)
+    uint8_t* ds_scales;
+    const int32_t* dboff;
+    long ds_blocks;
 };
 
 struct DqArgs {
@@ -72,9 +84,14 @@ struct DqArgs {
     const float* dvec;
     uint16_t* dq;
     const int4* tiles;
-    const int32_t* ntiles;
+    const int32_t* ntiles;    // ntiles[1]: the dS store is in use (the rebuilding
+                              // pass runs when it is 0, the store pass when it is 1)
     int ttot, hq, hkv;
     float c1, scale;
+    const uint8_t* ds_codes;  // dS store (see PlanArgs)
+    const uint8_t* ds_scales;
+    const int32_t* dboff;
+    long ds_blocks;
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
@@ -82,5 +99,6 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, int d, long grid, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, int d, long grid, hipStream_t st);
 hipError_t launch_dq(const DqArgs& a, int d, long grid, hipStream_t st);
+hipError_t launch_dq_store(const DqArgs& a, int d, long grid, hipStream_t st);
 
 }  // namespace flamia

@@ -15,8 +15,10 @@
 // Work item (tile, head) is decoded by the attention kernels from the
 // workgroup index, heads innermost.
 //
-// ctrl layout (int32): [0] number of tiles, [16, 16+C1) query-major cursors,
-// [16+C1, 16+2 C1) key-major cursors (C1 = max_cost + 1).
+// ctrl layout (int32): [0] number of tiles, [1] 1 if the backward's dS store
+// holds this call's blocks (capacity given and not exceeded), else 0,
+// [16, 16+C1) query-major cursors, [16+C1, 16+2 C1) key-major cursors
+// (C1 = max_cost + 1).  The dS block offsets of the documents go to dboff.
 #include "device.h"
 #include "kernels.h"
 
@@ -51,7 +53,8 @@ __device__ void block_scan(int* buf, int n, bool reverse, int* partial) {
 
 __global__ void __launch_bounds__(kPlanThreads)
 plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __restrict__ tiles_prefix,
-            int32_t* __restrict__ ctrl, long max_tiles, int4* __restrict__ tiles_q, int4* __restrict__ tiles_k) {
+            int32_t* __restrict__ ctrl, long max_tiles, int4* __restrict__ tiles_q, int4* __restrict__ tiles_k,
+            int32_t* __restrict__ dboff, long ds_blocks) {
     extern __shared__ int smem[];
     int* partial = smem;                       // kPlanThreads
     int* hist = smem + kPlanThreads;           // max_cost + 1
@@ -97,6 +100,38 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __
         }
         if (tid == kPlanThreads - 1) tiles_prefix[ndocs] = partial[kPlanThreads - 1];
     }
+    // dS store: first causal 32x32 block of each document (nb (nb + 1) / 2
+    // blocks for nb = ceil(L / 32)), and whether the call fits the capacity
+    if (dboff) {
+        __syncthreads();
+        const int chunk = (ndocs + kPlanThreads - 1) / kPlanThreads;
+        const int lo = tid * chunk, hi = min(lo + chunk, ndocs);
+        long sum = 0;
+        for (int d = lo; d < hi; ++d) {
+            const long nb = (cu[d + 1] - cu[d] + kBlock - 1) / kBlock;
+            sum += nb * (nb + 1) / 2;
+        }
+        __shared__ long lpartial[kPlanThreads];
+        lpartial[tid] = sum;
+        __syncthreads();
+        for (int o = 1; o < kPlanThreads; o <<= 1) {
+            const long v = tid >= o ? lpartial[tid - o] : 0;
+            __syncthreads();
+            lpartial[tid] += v;
+            __syncthreads();
+        }
+        const long total_blocks = lpartial[kPlanThreads - 1];
+        const bool fits = ds_blocks > 0 && total_blocks <= ds_blocks;
+        long run = tid > 0 ? lpartial[tid - 1] : 0;
+        for (int d = lo; d < hi; ++d) {
+            dboff[d] = fits ? (int32_t)run : 0;
+            const long nb = (cu[d + 1] - cu[d] + kBlock - 1) / kBlock;
+            run += nb * (nb + 1) / 2;
+        }
+        if (tid == 0) ctrl[1] = fits ? 1 : 0;
+    } else if (tid == 0) {
+        ctrl[1] = 0;
+    }
     // the cursor zeros and the prefix table must have reached L2 before any
     // thread of the workgroup uses them
     __threadfence();
@@ -106,7 +141,7 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __
         const int t = p - tiles_prefix[doc];
         const int n = tiles_prefix[doc + 1] - tiles_prefix[doc];
         const int ds = cu[doc], de = cu[doc + 1];
-        const int4 tile = make_int4(ds + kTile * t, ds, de, 0);
+        const int4 tile = make_int4(ds + kTile * t, ds, de, doc);
         {
             const int cost = t + 1;
             const int slot = (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&ctrl[16 + cost], 1);
@@ -123,7 +158,7 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
     const size_t smem = sizeof(int) * (kPlanThreads + a.max_cost + 1);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), smem, st, a.cu, a.ndocs, a.max_cost,
-                       a.tiles_prefix, a.ctrl, a.max_tiles, a.tiles_q, a.tiles_k);
+                       a.tiles_prefix, a.ctrl, a.max_tiles, a.tiles_q, a.tiles_k, a.dboff, a.ds_blocks);
     return hipGetLastError();
 }
 

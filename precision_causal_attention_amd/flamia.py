@@ -23,7 +23,7 @@ STATUS = {0: "FLAMIA_OK", 1: "FLAMIA_ERR_NULL", 2: "FLAMIA_ERR_SHAPE", 3: "FLAMI
 class Dims(ctypes.Structure):
     _fields_ = [("ttot", ctypes.c_int32), ("ttot_cap", ctypes.c_int32), ("ndocs", ctypes.c_int32),
                 ("ndocs_cap", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
-                ("d", ctypes.c_int32)]
+                ("d", ctypes.c_int32), ("doclen_cap", ctypes.c_int32)]
 
 
 class Opts(ctypes.Structure):
@@ -160,10 +160,10 @@ class TrainingCall:
     (any integer view of the same bytes works); cu_seqlens int32 on device."""
 
     def __init__(self, ttot: int, hq: int, hkv: int, d: int, ndocs_cap: int, ttot_cap: int | None = None,
-                 opts: Opts | None = None, device="cuda"):
+                 opts: Opts | None = None, device="cuda", doclen_cap: int = 0):
         import torch
         self.torch = torch
-        self.dims = Dims(ttot, ttot_cap or ttot, 0, ndocs_cap, hq, hkv, d)
+        self.dims = Dims(ttot, ttot_cap or ttot, 0, ndocs_cap, hq, hkv, d, doclen_cap)
         self.opts = opts or flamia_default_opts()
         self.ws_bytes = flamia_workspace_bytes(self.dims, self.opts)
         if self.ws_bytes == 0:

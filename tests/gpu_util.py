@@ -21,12 +21,18 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_hip(inst: dict, opts: F.Opts | None = None, backward: bool = True, ndocs_cap: int | None = None):
+def run_hip(inst: dict, opts: F.Opts | None = None, backward: bool = True, ndocs_cap: int | None = None,
+            doclen_cap: int | None = None):
+    """doclen_cap: None = the longest document (the dS store path), 0 = no
+    store (the rebuilding dQ pass)."""
     q, k, v = (dev_bf16(inst[n]) for n in ("q", "k", "v"))
     cu = torch.from_numpy(inst["cu_seqlens"]).cuda()
     T, hq, d = inst["q"].shape
     hkv = inst["k"].shape[1]
-    call = F.TrainingCall(T, hq, hkv, d, ndocs_cap or len(inst["cu_seqlens"]) - 1, opts=opts)
+    if doclen_cap is None:
+        doclen_cap = int(np.max(np.diff(inst["cu_seqlens"]))) if len(inst["cu_seqlens"]) > 1 else 0
+    call = F.TrainingCall(T, hq, hkv, d, ndocs_cap or len(inst["cu_seqlens"]) - 1, opts=opts,
+                          doclen_cap=doclen_cap)
     call.forward(q, k, v, cu)
     out = {"o": host_bits(call.o), "lse2": call.lse2.cpu().numpy(),
            "q_codes": call.q_mx[0].cpu().numpy(), "q_scales": call.q_mx[1].cpu().numpy(),

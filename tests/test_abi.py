@@ -26,16 +26,16 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_defaults(L):
-    assert F.flamia_abi_version() == 1
+    assert F.flamia_abi_version() == 2
     o = F.flamia_default_opts()
     assert (o.c_log2, o.tau, o.key_tile, o.rowsum) == (4, 4, 128, 0)
     assert F.flamia_status_str(0) == "ok"
 
 
 def dims(**kw):
-    base = dict(ttot=1024, ttot_cap=1024, ndocs=3, ndocs_cap=8, hq=8, hkv=2, d=64)
+    base = dict(ttot=1024, ttot_cap=1024, ndocs=3, ndocs_cap=8, hq=8, hkv=2, d=64, doclen_cap=0)
     base.update(kw)
-    return F.Dims(*[base[k] for k in ("ttot", "ttot_cap", "ndocs", "ndocs_cap", "hq", "hkv", "d")])
+    return F.Dims(*[base[k] for k in ("ttot", "ttot_cap", "ndocs", "ndocs_cap", "hq", "hkv", "d", "doclen_cap")])
 
 
 def test_workspace_depends_on_capacity_only():
@@ -44,6 +44,18 @@ def test_workspace_depends_on_capacity_only():
     assert a == b > 0
     assert F.flamia_workspace_bytes(dims(ttot_cap=2048)) > a
     assert F.flamia_workspace_bytes(dims(d=96)) == 0
+
+
+def test_ds_store_sizing():
+    # the dS store adds hq * B * (1024 + 1) bytes (plus alignment), with
+    # B = (ttot_cap / 32 + ndocs_cap) * (ceil(doclen_cap / 32) + 1) / 2
+    base = F.flamia_workspace_bytes(dims())
+    with_store = F.flamia_workspace_bytes(dims(doclen_cap=1000))
+    B = (1024 // 32 + 8) * (-(-1000 // 32) + 1) // 2
+    assert with_store - base >= 8 * B * 1025
+    assert with_store - base < 8 * B * 1025 + 2048
+    assert F.flamia_workspace_bytes(dims(doclen_cap=2048)) == 0      # longer than ttot_cap
+    assert F.flamia_workspace_bytes(dims(doclen_cap=-1)) == 0
 
 
 FAKE = 1 << 20   # aligned non-null host integer, never dereferenced: validation fails first

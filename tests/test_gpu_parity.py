@@ -63,7 +63,7 @@ def test_quantize_bitexact(orc, case):
     say(f"[quantize] {case} T={inst['q'].shape[0]}")
     cu = inst["cu_seqlens"]
     T, hq, d = inst["q"].shape
-    dims = F.Dims(T, T, len(cu) - 1, len(cu) - 1, hq, inst["k"].shape[1], d)
+    dims = F.Dims(T, T, len(cu) - 1, len(cu) - 1, hq, inst["k"].shape[1], d, 0)
     cu_d = torch.from_numpy(cu).cuda()
     for name in ("q", "k", "v", "do"):
         x = inst[name]
@@ -106,11 +106,35 @@ def test_full_size_gqa_sampled_group(orc):
     for every document, and those outputs are compared element by element."""
     inst = W.generate("gqa-4x8k", 0)
     say(f"[full] gqa-4x8k docs={len(inst['lengths'])} sumL2={inst['sum_L2']}")
-    g = run_hip(inst)
+    g = run_hip(inst, doclen_cap=8192)     # the benchmark's store capacity (row length)
     km = np.zeros(8, np.uint8)
     km[0] = 1
     r = _oracle(orc, inst, kv_mask=km)
     _check_all(g, r, heads=slice(0, 4), kvheads=slice(0, 1))
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_ds_store_equals_rebuild(case):
+    """The dQ pass from the stored dS-hat blocks and the pass that rebuilds
+    them consume the same operand bytes in the same order: every output is
+    bitwise the same."""
+    inst = SMALL[case]()
+    say(f"[dS store vs rebuild] {case}")
+    a = run_hip(inst)                       # store sized for the longest document
+    b = run_hip(inst, doclen_cap=0)         # no store
+    for key in ("o", "lse2", "dq", "dk", "dv"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_ds_store_too_small_falls_back():
+    """A store sized for shorter documents than the call's: the device sees
+    that the blocks do not fit and the rebuilding pass produces dQ."""
+    inst = SMALL["ragged-gqa-d64"]()
+    say("[dS store overflow] ragged-gqa-d64 with doclen_cap=32")
+    a = run_hip(inst, doclen_cap=32)
+    b = run_hip(inst, doclen_cap=0)
+    for key in ("dq", "dk", "dv"):
+        assert np.array_equal(a[key], b[key]), key
 
 
 def test_deterministic_and_document_isolation():
