@@ -19,7 +19,9 @@ Prints ONE JSON line:
             products x 2d x L^2/2 causal pairs, backward 2.5x the forward;
             the recomputed score products of the dQ pass earn no credit)
   roofline  the dominant kernel's algorithmic FLOP per launch divided by its
-            average duration in the timed pass
+            average duration in the timed pass; traffic = its HBM bytes per
+            launch from the committed counter summary of the workload, while
+            the kernel's sources still match the digest recorded there
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 """
 import argparse
@@ -37,6 +39,10 @@ METRIC = "fwd+bwd causal attention TFLOP/s incl. quant (MXFP8, packed docs), % o
 MXFP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8/MXFP8 MFMA peak (AMD specification)
 FWD_PHASES = ["quantize_qkv", "worklist_fwd", "fwd_kernel"]
 BWD_PHASES = ["quantize_do", "worklist_bwd", "dkv_kernel", "dq_kernel"]
+CSRC = os.path.join(ROOT, "precision_causal_attention_amd", "csrc")
+# sources whose text decides each attention kernel's memory traffic
+KERNEL_SOURCES = {"fwd_kernel": ["fwd.hip"], "dkv_kernel": ["bwd.hip"], "dq_kernel": ["dq.hip", "dq_store.hip"]}
+COMMON_SOURCES = ["device.h", "kernels.h"]
 
 
 def log(*a):
@@ -72,6 +78,33 @@ class Hip:
         return float(ms.value)
 
 
+def source_digest(kernel):
+    """sha256 (16 hex digits) of the sources a kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + COMMON_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, kernel, doclen_cap):
+    """HBM bytes per launch of `kernel` from the committed counter summary of
+    `workload` (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by the copy-kernel
+    calibration written there), or None when there is none or the kernel's
+    sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    digest = source_digest(kernel)
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        # | kernel | source digest | doclen_cap | FETCH KiB | WRITE KiB | HBM bytes per launch |
+        if len(cells) == 6 and cells[0] == kernel and cells[1] == digest and cells[2] == str(doclen_cap):
+            return int(cells[5])
+    return None
+
+
 def cpu_baseline(inst, hkv):
     """The oracle as it stands, on key/value head 0 and its query heads (all
     documents), scaled to TFLOP/s of that sample."""
@@ -97,7 +130,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="gqa-4x8k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -232,7 +265,7 @@ def main():
         "phases_ms": {p: round(t, 4) for p, t in phases.items()},
         "roofline": {"kernel": dom, "kernel_ms": round(dom_ms, 4), "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MXFP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MXFP8_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": recorded_traffic(wl.name, dom, doclen_cap)},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")
