@@ -42,7 +42,7 @@ struct BwdSmem {
     uint8_t eo[kQStep];
 };
 
-template <int D>
+template <int D, bool STORE>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs a) {
     constexpr int KC = D / 64;
     constexpr int DT = D / 32;
@@ -56,7 +56,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     const int k0 = it.x, ds = it.y, de = it.z, doc = it.w;
     const int g = (int)blockIdx.x - ti * a.hkv;
     // the dS store holds this call's blocks: write each dS-hat block once
-    const bool use_store = a.ntiles[1] != 0;
+    const bool use_store = STORE && a.ntiles[1] != 0;
     const long doc_blk = use_store ? (long)a.dboff[doc] : 0;
     const int G = a.hq / a.hkv;
     const int L = de - ds;
@@ -327,8 +327,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
 
 hipError_t launch_bwd(const BwdArgs& a, int d, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
-    if (d == 64) hipLaunchKernelGGL(bwd_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(bwd_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    // the store variant only where the workspace has a dS store
+    const bool store = a.ds_blocks > 0;
+    if (d == 64) {
+        if (store) hipLaunchKernelGGL((bwd_kernel<64, true>), dim3((unsigned)grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((bwd_kernel<64, false>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    } else {
+        if (store) hipLaunchKernelGGL((bwd_kernel<128, true>), dim3((unsigned)grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((bwd_kernel<128, false>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
 

@@ -105,17 +105,14 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_floa
 // the smallest e with amax <= 448 * 2^e ("rounded up", so no element of the
 // block saturates), clamped to [lo, 127]; amax == 0 gives lo.
 __device__ __forceinline__ int block_exponent(float amax, int lo) {
-    // branch-free (selects only), so that callers stay one basic block
+    // Branch-free (a compare and two clamps), so that callers stay one basic
+    // block.  With amax = 1.f x 2^E, 448 = 1.75 x 2^8: the exponent is E - 8,
+    // plus one when the mantissa exceeds 1.75.  A subnormal or zero amax
+    // (biased exponent 0) gives at most -134 here and a true exponent below
+    // -133, so for lo >= -133 the clamp alone yields the right result.
     const uint32_t u = __float_as_uint(amax);
-    const uint32_t ef = u >> 23;
-    const int lz = __clz(u) - 8;               // fp32 subnormal: leading zeros inside the fraction + 1
-    const int E = ef ? (int)ef - 127 : -126 - lz;
-    const uint32_t frac = ef ? (u & 0x7FFFFFu) : ((u << (lz & 31)) & 0x7FFFFFu);   // fraction of 1.f
-    // mantissa 1.f > 1.75  <=>  frac > 0.75 * 2^23
-    int e = E - 8 + (frac > 0x600000u ? 1 : 0);
-    e = e < lo ? lo : e;
-    e = e > 127 ? 127 : e;
-    return u == 0u ? lo : e;
+    const int e = (int)(u >> 23) - 135 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    return min(max(e, lo), 127);
 }
 
 // block_exponent of a wave-uniform maximum, evaluated on the scalar unit
