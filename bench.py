@@ -6,13 +6,18 @@ dK/dV kernel, query-major dQ kernel) on one seeded synthetic batch already
 resident in HBM.
 
 Every HIP event recorded between two launches adds a few microseconds of
-dispatch gap, so the measurement runs in two passes:
-  1. phase pass: K steps with an event at every phase boundary (library-
-     recorded on the launch stream) -> phases_ms, and which attention kernel
-     dominates;
-  2. timed pass: K steps with only two events per step, around the dominant
-     kernel -> value / ms_per_step (bracketed by device synchronizations) and
-     the roofline's average kernel duration.
+dispatch gap, so the measurement runs in passes:
+  1. phase pass: K eager steps with an event at every phase boundary
+     (library-recorded on the launch stream) -> phases_ms, and which
+     attention kernel dominates;
+  2. timed pass: K eager steps with two events per step, around the dominant
+     kernel -> value / ms_per_step (bracketed by device synchronizations)
+     and the roofline's average kernel duration;
+  3. graph pass: one whole call captured as a HIP graph and replayed K times,
+     bracketed by device synchronizations -> graph_ms_per_step (the pages
+     time a replayed graph; on MI355X with ROCm 7 the replay adds about
+     10-15 us per kernel node over stream launches, so the eager time is the
+     one reported as value).
 
 Prints ONE JSON line:
   value     whole-call throughput, FLOP = 7 * Hq * d * sum(L^2) (forward 2
@@ -243,6 +248,33 @@ def main():
     ms_step = ms_total / args.steps
     dom_ms = sum(hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(args.steps)) / args.steps
 
+
+    # ---- pass 3: one whole call (fwd + bwd) captured as a HIP graph and
+    # replayed K times
+    def capture():
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        call.opts.phase_events, call.opts.n_events = None, 0
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                call.forward(q, k, v, cu, cs)
+                call.backward(do, cu, cs)
+        torch.cuda.synchronize()
+        return g
+
+    log(f"[bench] graph pass, {args.steps} replays")
+    graph = capture()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms_step = t0.elapsed_time(t1) / args.steps
+
     tflops = flop / (ms_step * 1e-3) / 1e12
     achieved = kflop[dom] / (dom_ms * 1e-3) / 1e12
     result = {
@@ -262,6 +294,7 @@ def main():
         "config": {"workload": wl.name, "rows": wl.rows, "row_len": wl.row_len, "tokens": T, "hq": hq,
                    "hkv": hkv, "d": d, "docs": ndocs, "sum_L2": sum_l2, "seed": args.seed,
                    "doc_law": wl.docs, "doclen_cap": doclen_cap, "parallelism": "single-gpu"},
+        "graph_ms_per_step": round(graph_ms_step, 4),
         "phases_ms": {p: round(t, 4) for p, t in phases.items()},
         "roofline": {"kernel": dom, "kernel_ms": round(dom_ms, 4), "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MXFP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MXFP8_PEAK_TFLOPS, 4),
