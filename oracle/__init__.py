@@ -49,6 +49,7 @@ class _Params(ctypes.Structure):
         ("tau", ctypes.c_int32), ("key_tile", ctypes.c_int32), ("quant", ctypes.c_int32),
         ("rowsum", ctypes.c_int32), ("softmax_scale", ctypes.c_double),
         ("unsafe_bound", ctypes.c_int32), ("score_rel_err", ctypes.c_double),
+        ("hadamard", ctypes.c_int32),
     ]
 
 
@@ -76,6 +77,7 @@ def _load():
         lib.orc_e4m3_value_array.argtypes = [P, ctypes.c_long, P]
         lib.orc_scale_exp_array.argtypes = [P, ctypes.c_long, ctypes.c_int, P]
         lib.orc_double_to_bf16_array.argtypes = [P, ctypes.c_long, P]
+        lib.orc_hadamard_f32_array.argtypes = [P, ctypes.c_long, ctypes.c_int, P]
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -95,11 +97,13 @@ class Opts:
     softmax_scale: float = 0.0
     unsafe_bound: int = 0
     score_rel_err: float = 0.0   # > 0 with want_tol: decision-sensitivity bounds
+    hadamard: int = 0            # 1: Hadamard rotation of Q and K (Section 3.4, Appendix A.2)
 
 
 def _params(ttot, ndocs, hq, hkv, d, opts: Opts) -> _Params:
     return _Params(ttot, ndocs, hq, hkv, d, opts.c_log2, opts.tau, opts.key_tile, opts.quant,
-                   opts.rowsum, float(opts.softmax_scale), opts.unsafe_bound, float(opts.score_rel_err))
+                   opts.rowsum, float(opts.softmax_scale), opts.unsafe_bound, float(opts.score_rel_err),
+                   opts.hadamard)
 
 
 def max_threads() -> int:
@@ -138,6 +142,16 @@ def to_bf16_bits(x) -> np.ndarray:
 def bf16_bits_to_f64(b) -> np.ndarray:
     b = np.asarray(b, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def hadamard_f32(x_bits) -> np.ndarray:
+    """Rows of bf16 patterns [..., d] -> their fp32 Hadamard rotation (the
+    quantizer's input when the rotation is on)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    d = x.shape[-1]
+    out = np.empty(x.shape, dtype=np.float32)
+    _load().orc_hadamard_f32_array(_ptr(x), x.size // d, d, _ptr(out))
+    return out
 
 
 # ---- token-block quantizer --------------------------------------------------

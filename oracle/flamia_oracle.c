@@ -29,7 +29,10 @@
  *     after accumulation;
  *   - D_i = dO~_i . O_i uses the bf16 output that the forward returns;
  *   - GQA: query head h reads key/value head h / (Hq/Hkv); dK and dV sum over
- *     the heads of the group before rounding.
+ *     the heads of the group before rounding;
+ *   - the optional Hadamard rotation of Q and K is computed in fp32 by the
+ *     butterfly in a fixed stage order (its values decide codes), and the
+ *     gradients are rotated back in binary64.
  *
  * Parity: every exported function is pinned by CPU tests against definitions
  * that do not go through this file (a library FP8 codec, brute-force nearest
@@ -68,6 +71,9 @@ typedef struct {
      * code, a running-maximum replacement) lies within that error band of its
      * rounding or comparison threshold. */
     double score_rel_err;
+    /* Hadamard rotation of Q and K before quantization (Section 3.4 and
+     * Appendix A.2): 0 off, 1 on. */
+    int32_t hadamard;
 } orc_params;
 
 /* ---------------------------------------------------------------------------
@@ -161,31 +167,85 @@ uint16_t orc_double_to_bf16(double x)
 }
 
 /* ---------------------------------------------------------------------------
+ * Hadamard rotation (Section 3.4 "a normalized Hadamard transform ... mixes
+ * the head channels of both Q and K before quantization"; Appendix A.2).
+ * The rotated values decide E4M3 codes, so their precision is part of the
+ * definition; the reading taken: the bf16 row is widened to fp32, transformed
+ * by the fast Walsh-Hadamard butterfly in fp32 (stages of stride 1, 2, 4, ...,
+ * d/2; each butterfly maps (a, b) at channels (j, j + h) to (a + b, a - b)),
+ * then multiplied by fp32(1/sqrt(d)) (exactly 2^-3 at d = 64, the nearest
+ * fp32 to 2^-3.5 at d = 128).  The butterfly computes x H with the Sylvester
+ * matrix H[i][j] = (-1)^popcount(i & j), so the rotation is x H / sqrt(d),
+ * orthogonal and its own inverse.
+ * ------------------------------------------------------------------------- */
+void orc_hadamard_f32(const uint16_t *x, int d, float *y)
+{
+    for (int i = 0; i < d; ++i) y[i] = (float)orc_bf16_to_double(x[i]);
+    for (int h = 1; h < d; h <<= 1)
+        for (int i = 0; i < d; i += 2 * h)
+            for (int j = i; j < i + h; ++j) {
+                float a = y[j], b = y[j + h];
+                y[j] = a + b;
+                y[j + h] = a - b;
+            }
+    const float rs = sqrtf(1.0f / (float)d);
+    for (int i = 0; i < d; ++i) y[i] = y[i] * rs;
+}
+
+/* The same rotation of a binary64 row, in binary64 (used to rotate the
+ * gradients back: dQ = dQ' H / sqrt(d), dK = dK' H / sqrt(d)). */
+static void hadamard_f64(double *y, int d)
+{
+    for (int h = 1; h < d; h <<= 1)
+        for (int i = 0; i < d; i += 2 * h)
+            for (int j = i; j < i + h; ++j) {
+                double a = y[j], b = y[j + h];
+                y[j] = a + b;
+                y[j + h] = a - b;
+            }
+    const double rs = 1.0 / sqrt((double)d);
+    for (int i = 0; i < d; ++i) y[i] *= rs;
+}
+
+/* ---------------------------------------------------------------------------
  * Token-block quantizer (Section 3.1 "token-block scaling"; Section 3.6.1,
  * blocks and statistics kept inside document boundaries).
- * One document slice of L tokens, d channels, rows `rstride` elements apart.
+ * One document slice of L tokens, d channels, rows `rstride` elements apart;
+ * rot = 1 quantizes the Hadamard-rotated rows instead of the bf16 rows.
  * Blocks are [32b, min(32b+32, L)) from the document start; one exponent per
  * block over all d channels; every token of the block stores it.
- * deq (L x d, dense) receives value(code) * 2^e, or x itself when quant is
- * QUANT_NONE.  codes/scales may be NULL.
+ * deq (L x d, dense) receives value(code) * 2^e, or the (rotated) values
+ * themselves when quant is QUANT_NONE.  codes/scales may be NULL.
+ * Returns 0, or ORC_ERR_NOMEM.
  * ------------------------------------------------------------------------- */
-static void tbq_slice(const uint16_t *x, long rstride, int L, int d, int quant,
-                      double *deq, uint8_t *codes, long cstride, uint8_t *scales)
+static int tbq_slice(const uint16_t *x, long rstride, int L, int d, int quant, int rot,
+                     double *deq, uint8_t *codes, long cstride, uint8_t *scales)
 {
+    double *xv = malloc(sizeof(double) * (size_t)L * d);
+    float *row = malloc(sizeof(float) * (size_t)d);
+    if (!xv || !row) { free(xv); free(row); return ORC_ERR_NOMEM; }
+    for (int t = 0; t < L; ++t) {
+        if (rot) {
+            orc_hadamard_f32(x + (long)t * rstride, d, row);
+            for (int k = 0; k < d; ++k) xv[(long)t * d + k] = (double)row[k];
+        } else {
+            for (int k = 0; k < d; ++k) xv[(long)t * d + k] = orc_bf16_to_double(x[(long)t * rstride + k]);
+        }
+    }
     for (int b0 = 0; b0 < L; b0 += 32) {
         int b1 = b0 + 32 < L ? b0 + 32 : L;
         double amax = 0.0;
         int e = 0;
         for (int t = b0; t < b1; ++t)
             for (int k = 0; k < d; ++k) {
-                double v = fabs(orc_bf16_to_double(x[(long)t * rstride + k]));
+                double v = fabs(xv[(long)t * d + k]);
                 if (v > amax) amax = v;
             }
         if (quant != QUANT_NONE) e = orc_scale_exp(amax, quant == QUANT_FLOOR ? 1 : 0);
         for (int t = b0; t < b1; ++t) {
             if (scales) scales[t] = (uint8_t)(e + 127);
             for (int k = 0; k < d; ++k) {
-                double v = orc_bf16_to_double(x[(long)t * rstride + k]);
+                double v = xv[(long)t * d + k];
                 if (quant == QUANT_NONE) {
                     deq[(long)t * d + k] = v;
                 } else {
@@ -196,6 +256,9 @@ static void tbq_slice(const uint16_t *x, long rstride, int L, int d, int quant,
             }
         }
     }
+    free(xv);
+    free(row);
+    return ORC_OK;
 }
 
 static int check_cu(const orc_params *p, const int32_t *cu)
@@ -223,9 +286,10 @@ int orc_quantize(const orc_params *p, int heads, const uint16_t *x, const int32_
         if (L == 0) continue;
         deq = (double *)malloc(sizeof(double) * (size_t)L * d);
         if (!deq) { err = ORC_ERR_NOMEM; continue; }
-        tbq_slice(x + ((long)base * heads + h) * d, (long)heads * d, L, d, p->quant, deq,
-                  codes + ((long)base * heads + h) * d, (long)heads * d,
-                  scales + (long)h * p->ttot + base);
+        if (tbq_slice(x + ((long)base * heads + h) * d, (long)heads * d, L, d, p->quant, p->hadamard != 0,
+                      deq, codes + ((long)base * heads + h) * d, (long)heads * d,
+                      scales + (long)h * p->ttot + base) != ORC_OK)
+            err = ORC_ERR_NOMEM;
         free(deq);
     }
     return err;
@@ -443,12 +507,20 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         goto done;
     }
     /* K~ and V~: token blocks of this document and this key/value head. */
-    tbq_slice(k + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, Kt, 0, 0, 0);
-    tbq_slice(v + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, Vt, 0, 0, 0);
+    /* K~ is quantized from the rotated rows when the Hadamard rotation is on
+     * (Section 3.4); V~ never is. */
+    if (tbq_slice(k + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, p->hadamard != 0, Kt, 0, 0, 0) ||
+        tbq_slice(v + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, 0, Vt, 0, 0, 0)) {
+        *err = ORC_ERR_NOMEM;
+        goto done;
+    }
 
     for (int hh = 0; hh < G; ++hh) {
         const int h = g * G + hh;
-        tbq_slice(q + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, Qt, 0, 0, 0);
+        if (tbq_slice(q + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, p->hadamard != 0, Qt, 0, 0, 0)) {
+            *err = ORC_ERR_NOMEM;
+            goto done;
+        }
         /* ---- forward, row by row ---- */
         for (int i = 0; i < L; ++i) {
             fwd_row(p, i, Qt + (long)i * d, Kt, Vt, c1, acc, xbuf, O + (long)i * d, &lse[i], &sat, rt);
@@ -475,7 +547,10 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         if (!need_bwd) continue;
 
         /* ---- backward (Section 2 equations; Section 3.3 consistency) ---- */
-        tbq_slice(dout + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, dOt, 0, 0, 0);
+        if (tbq_slice(dout + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, 0, dOt, 0, 0, 0)) {
+            *err = ORC_ERR_NOMEM;
+            goto done;
+        }
         for (int i = 0; i < L; ++i) {
             Dv[i] = dotd(dOt + (long)i * d, O + (long)i * d, d);
             if (out->dvec) out->dvec[(long)h * p->ttot + base + i] = Dv[i];
@@ -572,6 +647,20 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                     }
             }
         }
+        if (p->hadamard) {
+            /* dQ' is the gradient for the rotated Q' = Q H / sqrt(d): dQ = dQ' H / sqrt(d)
+             * (H / sqrt(d) is symmetric and its own inverse).  An output element
+             * is a +-1/sqrt(d) combination of the row, so the bound of each
+             * element is the row's bounds summed, over sqrt(d). */
+            for (int i = 0; i < L; ++i) {
+                hadamard_f64(dQa + (long)i * d, d);
+                if (tdq) {
+                    double t = 0.0;
+                    for (int c = 0; c < d; ++c) t += tdq[(long)i * d + c];
+                    for (int c = 0; c < d; ++c) tdq[(long)i * d + c] = t / sqrt((double)d);
+                }
+            }
+        }
         for (int i = 0; i < L; ++i)
             for (int c = 0; c < d; ++c) {
                 long gi = ((long)(base + i) * hq + h) * d + c;
@@ -582,6 +671,15 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
             }
     }
     if (need_bwd) {
+        if (p->hadamard)   /* dK = dK' H / sqrt(d), as for dQ */
+            for (int j = 0; j < L; ++j) {
+                hadamard_f64(dKa + (long)j * d, d);
+                if (tdk) {
+                    double t = 0.0;
+                    for (int c = 0; c < d; ++c) t += tdk[(long)j * d + c];
+                    for (int c = 0; c < d; ++c) tdk[(long)j * d + c] = t / sqrt((double)d);
+                }
+            }
         for (int j = 0; j < L; ++j)
             for (int c = 0; c < d; ++c) {
                 long gj = ((long)(base + j) * hkv + g) * d + c;
@@ -669,6 +767,12 @@ int orc_attention(const orc_params *p, const uint16_t *q, const uint16_t *k, con
     }
     free(units);
     return err;
+}
+
+/* rows x d bf16 patterns -> rows x d fp32 rotated values */
+void orc_hadamard_f32_array(const uint16_t *x, long rows, int d, float *y)
+{
+    for (long r = 0; r < rows; ++r) orc_hadamard_f32(x + r * d, d, y + r * d);
 }
 
 void orc_e4m3_encode_array(const double *y, long n, uint8_t *codes)
