@@ -110,7 +110,7 @@ def recorded_traffic(workload, kernel, doclen_cap):
     return None
 
 
-def cpu_baseline(inst, hkv):
+def cpu_baseline(inst, hkv, hadamard=0):
     """The oracle as it stands, on key/value head 0 and its query heads (all
     documents), scaled to TFLOP/s of that sample."""
     import numpy as np
@@ -120,8 +120,8 @@ def cpu_baseline(inst, hkv):
     km = np.zeros(hkv, np.uint8)
     km[0] = 1
     t0 = time.perf_counter()
-    oracle.attention(inst["q"], inst["k"], inst["v"], inst["do"], inst["cu_seqlens"], kv_mask=km,
-                     want_f64=False)
+    oracle.attention(inst["q"], inst["k"], inst["v"], inst["do"], inst["cu_seqlens"],
+                     oracle.Opts(hadamard=hadamard), kv_mask=km, want_f64=False)
     dt = time.perf_counter() - t0
     hq, d = inst["q"].shape[1], inst["q"].shape[2]
     G = hq // hkv
@@ -143,6 +143,8 @@ def main():
                     help="dS store capacity as the longest document; 0: no store, dQ rebuilds "
                          "dS-hat.  Default: the row length at d = 128, where reading the stored "
                          "blocks is faster on MI355X, and no store at d = 64, where rebuilding is")
+    ap.add_argument("--hadamard", type=int, default=0, choices=(0, 1),
+                    help="1: Hadamard rotation of Q and K before quantization (the pages' default at d = 128)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a fill and a widening copy of this many MiB (known-size "
                          "references for hardware byte counters collected over the same run)")
@@ -170,6 +172,7 @@ def main():
     # dS store sized for the longest possible document (a whole row), at d = 128
     doclen_cap = (wl.row_len if d == 128 else 0) if args.doclen_cap < 0 else args.doclen_cap
     call = F.TrainingCall(T, hq, hkv, d, ndocs_cap=ndocs, doclen_cap=doclen_cap)
+    call.opts.hadamard = args.hadamard
     hip = Hip()
     nf, nb = len(FWD_PHASES) + 1, len(BWD_PHASES) + 1
     stream = torch.cuda.current_stream()
@@ -293,7 +296,8 @@ def main():
         "frac_of_mxfp8_peak": round(tflops / MXFP8_PEAK_TFLOPS, 4),
         "config": {"workload": wl.name, "rows": wl.rows, "row_len": wl.row_len, "tokens": T, "hq": hq,
                    "hkv": hkv, "d": d, "docs": ndocs, "sum_L2": sum_l2, "seed": args.seed,
-                   "doc_law": wl.docs, "doclen_cap": doclen_cap, "parallelism": "single-gpu"},
+                   "doc_law": wl.docs, "doclen_cap": doclen_cap, "hadamard": args.hadamard,
+                   "parallelism": "single-gpu"},
         "graph_ms_per_step": round(graph_ms_step, 4),
         "phases_ms": {p: round(t, 4) for p, t in phases.items()},
         "roofline": {"kernel": dom, "kernel_ms": round(dom_ms, 4), "bound": "mfma", "achieved": round(achieved, 2),
@@ -302,7 +306,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")
-        result["cpu_baseline"] = cpu_baseline(inst, hkv)
+        result["cpu_baseline"] = cpu_baseline(inst, hkv, args.hadamard)
     print(json.dumps(result), flush=True)
 
 

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FLAMIA_ABI_VERSION 2
+#define FLAMIA_ABI_VERSION 3
 
 typedef enum {
     FLAMIA_OK = 0,
@@ -85,6 +85,12 @@ typedef struct {
     int32_t rowsum;        /* 0: the forward row sum accumulates the unquantized p;
                               1: it accumulates the represented value(P-hat)/2^c */
     float softmax_scale;   /* <= 0 selects 1/sqrt(d) */
+    int32_t hadamard;      /* 1: Q and K are rotated by the normalized d x d Hadamard
+                              transform before quantization (Section 3.4, Appendix A.2):
+                              the saved Q-hat / K-hat codes are those of the rotated rows
+                              (fp32 butterfly, strides 1, 2, ..., d/2, then x fp32(1/sqrt(d))),
+                              and flamia_bwd rotates dQ and dK back.  flamia_bwd must be
+                              given the value flamia_fwd had.  0 (default): off */
     /* Optional phase timing: when phase_events is non-NULL it points to
      * n_events hipEvent_t handles (created by the caller); the call records
      * event i on `stream` before its i-th internal launch and the next one

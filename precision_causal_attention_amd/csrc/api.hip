@@ -49,6 +49,7 @@ flamia_status_t check_opts(const flamia_opts_t* o) {
     if (o->c_log2 < 0 || o->tau < 0 || o->c_log2 + o->tau > 8) return FLAMIA_ERR_OPTS;
     if (o->key_tile != kTile) return FLAMIA_ERR_OPTS;
     if (o->rowsum != 0 && o->rowsum != 1) return FLAMIA_ERR_OPTS;
+    if (o->hadamard != 0 && o->hadamard != 1) return FLAMIA_ERR_OPTS;
     if (!(o->softmax_scale <= 0.f || isfinite(o->softmax_scale))) return FLAMIA_ERR_OPTS;
     if (o->n_events < 0 || (o->n_events > 0 && !o->phase_events)) return FLAMIA_ERR_OPTS;
     return FLAMIA_OK;
@@ -123,6 +124,7 @@ flamia_opts_t flamia_default_opts(void) {
     o.key_tile = kTile;
     o.rowsum = 0;
     o.softmax_scale = 0.f;
+    o.hadamard = 0;
     o.phase_events = nullptr;
     o.n_events = 0;
     return o;
@@ -160,7 +162,7 @@ flamia_status_t flamia_quantize(const flamia_dims_t* dims, int32_t heads, const 
     if (!aligned16(x) || !aligned16(out.codes)) return FLAMIA_ERR_ALIGN;
     QuantArgs a{};
     a.cu = cu_seqlens; a.ndocs = dims->ndocs; a.ttot = dims->ttot; a.d = dims->d;
-    a.t[0] = QuantTensor{x, out.codes, out.scales, heads};
+    a.t[0] = QuantTensor{x, out.codes, out.scales, heads, 0};
     a.ntensors = 1;
     hipError_t e = launch_quantize(a, (hipStream_t)stream);
     return e == hipSuccess ? FLAMIA_OK : hip_fail(e);
@@ -192,9 +194,11 @@ flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     // quantization of the three operands in one launch (Section 3.5.1)
     QuantArgs qa{};
     qa.cu = cu_seqlens; qa.ndocs = dims->ndocs; qa.ttot = dims->ttot; qa.d = d;
-    qa.t[0] = QuantTensor{q, q_mx.codes, q_mx.scales, dims->hq};
-    qa.t[1] = QuantTensor{k, k_mx.codes, k_mx.scales, dims->hkv};
-    qa.t[2] = QuantTensor{v, v_mx.codes, v_mx.scales, dims->hkv};
+    // with the Hadamard option Q and K are quantized from their rotated rows
+    // (Section 3.4: the rotation is fused into the quantizer), V never is
+    qa.t[0] = QuantTensor{q, q_mx.codes, q_mx.scales, dims->hq, opts.hadamard};
+    qa.t[1] = QuantTensor{k, k_mx.codes, k_mx.scales, dims->hkv, opts.hadamard};
+    qa.t[2] = QuantTensor{v, v_mx.codes, v_mx.scales, dims->hkv, 0};
     qa.ntensors = 3;
     PhaseMarks pm{opts, st};
     hipError_t e;
@@ -251,7 +255,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     // dO launch: codes + scales and D = dO~ . O (Section 3.5.1)
     QuantArgs qa{};
     qa.cu = cu_seqlens; qa.ndocs = dims->ndocs; qa.ttot = dims->ttot; qa.d = d;
-    qa.t[0] = QuantTensor{d_o, oc, os, dims->hq};
+    qa.t[0] = QuantTensor{d_o, oc, os, dims->hq, 0};
     qa.ntensors = 1;
     qa.o = o; qa.dvec = dvec;
     PhaseMarks pm{opts, st};
@@ -278,6 +282,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     ba.ttot = dims->ttot; ba.hq = dims->hq; ba.hkv = dims->hkv;
     ba.scale = scale;
     ba.c1 = scale * 1.4426950408889634f;
+    ba.hadamard = opts.hadamard;
     ba.ds_codes = ds_codes; ba.ds_scales = ds_scales; ba.dboff = dboff; ba.ds_blocks = w.ds_blocks;
     if ((e = pm.mark()) != hipSuccess || (e = launch_bwd(ba, d, w.max_tiles * dims->hkv, st)) != hipSuccess)
         return hip_fail(e);
@@ -292,6 +297,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     qd.ttot = dims->ttot; qd.hq = dims->hq; qd.hkv = dims->hkv;
     qd.scale = scale;
     qd.c1 = ba.c1;
+    qd.hadamard = opts.hadamard;
     qd.ds_codes = ds_codes; qd.ds_scales = ds_scales; qd.dboff = dboff; qd.ds_blocks = w.ds_blocks;
     // dQ: from the stored blocks when the call fits the store (decided on the
     // device; the other kernel returns at once), else by rebuilding dS-hat

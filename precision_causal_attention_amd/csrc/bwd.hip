@@ -306,7 +306,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
         while (more && q0 >= kt0 + kTile) more = step(std::false_type{});
     }
     flush_store();
-    // ---- epilogue: dK = softmax_scale * sum, dV; summed over the group's heads
+    // ---- epilogue: dK = softmax_scale * sum, dV; summed over the group's heads.
+    // With the Hadamard option the dK sum is the gradient of the rotated K and
+    // is rotated back first.
+    float sck = a.scale;
+    if (a.hadamard) {
+        hadamard_rows<DT>(dkt, lg);
+        sck *= inv_sqrt_d<D>();
+    }
     if (key_valid) {
         uint16_t* kp = a.dk + ((long)(ds + key_loc) * a.hkv + g) * D;
         uint16_t* vp = a.dv + ((long)(ds + key_loc) * a.hkv + g) * D;
@@ -316,8 +323,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             for (int j = 0; j < 4; ++j) {
                 const int dd = 32 * dt + 8 * j + 4 * lg;
                 *reinterpret_cast<uint2*>(kp + dd) = make_uint2(
-                    pack_bf16x2(dkt[dt][4 * j] * a.scale, dkt[dt][4 * j + 1] * a.scale),
-                    pack_bf16x2(dkt[dt][4 * j + 2] * a.scale, dkt[dt][4 * j + 3] * a.scale));
+                    pack_bf16x2(dkt[dt][4 * j] * sck, dkt[dt][4 * j + 1] * sck),
+                    pack_bf16x2(dkt[dt][4 * j + 2] * sck, dkt[dt][4 * j + 3] * sck));
                 *reinterpret_cast<uint2*>(vp + dd) = make_uint2(
                     pack_bf16x2(dvt[dt][4 * j], dvt[dt][4 * j + 1]),
                     pack_bf16x2(dvt[dt][4 * j + 2], dvt[dt][4 * j + 3]));

@@ -122,6 +122,60 @@ __device__ __forceinline__ int block_exponent_uniform(float amax, int lo) {
     return block_exponent(__uint_as_float(u), lo);
 }
 
+// fp32 nearest to 1/sqrt(d) for d = 64 (exact) and d = 128 (2^-3.5 rounded).
+template <int D>
+__device__ __forceinline__ constexpr float inv_sqrt_d() {
+    return D == 64 ? 0.125f : 0x1.6a09e6p-4f;
+}
+
+// Normalized Hadamard rotation over the d channels of a transposed gradient
+// accumulator (dQ^T or dK^T: register 4j + r of tile dt holds channel
+// 32 dt + 8 j + 4 lg + r of the lane's row, lg = lane / 32).  H / sqrt(d) is
+// symmetric and its own inverse, so this takes the gradient of a rotated
+// operand back to the unrotated one.  fp32 butterflies in the order of the
+// channel bits; the lane-half bit (channel bit 2) pairs lanes l and l ^ 32.
+template <int DT>
+__device__ __forceinline__ void hadamard_rows(v16f (&acc)[DT], int lg) {
+    // channel bits 0, 1 (r) and 3, 4 (j): register bits 0, 1, 2, 3
+    auto in_reg = [&](int rbit) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if ((i & rbit) == 0) {
+                    const float a = acc[dt][i], b = acc[dt][i + rbit];
+                    acc[dt][i] = a + b;
+                    acc[dt][i + rbit] = a - b;
+                }
+    };
+    in_reg(1);
+    in_reg(2);
+    // channel bit 2: the other lane half
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float v = acc[dt][i];
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+            const float p = __uint_as_float(lg ? r[0] : r[1]);
+            acc[dt][i] = lg ? p - v : v + p;
+        }
+    in_reg(4);
+    in_reg(8);
+    // channel bits 5, 6: the tiles
+#pragma unroll
+    for (int h = 1; h < DT; h <<= 1)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            if ((dt & h) == 0)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float a = acc[dt][i], b = acc[dt + h][i];
+                    acc[dt][i] = a + b;
+                    acc[dt + h][i] = a - b;
+                }
+}
+
 // Lane exchange without the LDS crossbar: DPP within 16-lane rows, then
 // v_permlane16_swap / v_permlane32_swap across rows.  Each swap returns the
 // pair {own value, partner value} (order depends on the lane), so a

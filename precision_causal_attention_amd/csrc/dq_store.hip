@@ -148,15 +148,21 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) dq_store_kernel(const Dq
         step(fa, t);
         if (t + 1 < ntiles) step(fb, t + 1);          // workgroup-uniform
     }
-    // ---- epilogue: dQ = softmax_scale * sum, bf16
+    // ---- epilogue: dQ = softmax_scale * sum, bf16; with the Hadamard option
+    // the sum is the gradient of the rotated Q and is rotated back first
+    float sc = a.scale;
+    if (a.hadamard) {
+        hadamard_rows<DT>(acc, lg);
+        sc *= inv_sqrt_d<D>();
+    }
     if (q_valid) {
         uint16_t* qp = a.dq + ((long)(ds + q_loc) * a.hq + h) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t b01 = pack_bf16x2(acc[dt][4 * j] * a.scale, acc[dt][4 * j + 1] * a.scale);
-                const uint32_t b23 = pack_bf16x2(acc[dt][4 * j + 2] * a.scale, acc[dt][4 * j + 3] * a.scale);
+                const uint32_t b01 = pack_bf16x2(acc[dt][4 * j] * sc, acc[dt][4 * j + 1] * sc);
+                const uint32_t b23 = pack_bf16x2(acc[dt][4 * j + 2] * sc, acc[dt][4 * j + 3] * sc);
                 *reinterpret_cast<uint2*>(qp + 32 * dt + 8 * j + 4 * lg) = make_uint2(b01, b23);
             }
     }

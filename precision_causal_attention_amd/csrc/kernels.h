@@ -15,6 +15,7 @@ struct QuantTensor {
     uint8_t* codes;
     uint8_t* scales;
     int heads;
+    int rot;                  // 1: quantize the Hadamard-rotated rows
 };
 
 struct QuantArgs {
@@ -72,6 +73,7 @@ struct BwdArgs {
     const int32_t* ntiles;    // ntiles[1] != 0: store dS-hat blocks
     int ttot, hq, hkv;
     float c1, scale;
+    int hadamard;             // 1: rotate dK back (Q and K were rotated)
     uint8_t* ds_codes;        // dS store (see PlanArgs)
     uint8_t* ds_scales;
     const int32_t* dboff;
@@ -88,6 +90,7 @@ struct DqArgs {
                               // pass runs when it is 0, the store pass when it is 1)
     int ttot, hq, hkv;
     float c1, scale;
+    int hadamard;             // 1: rotate dQ back (Q and K were rotated)
     const uint8_t* ds_codes;  // dS store (see PlanArgs)
     const uint8_t* ds_scales;
     const int32_t* dboff;

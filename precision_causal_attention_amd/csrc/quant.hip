@@ -15,6 +15,8 @@
 // piece c % (d/8) of token c / (d/8), so each load instruction of the wave
 // reads whole 2d-byte rows.
 // HBM-bound: the input is read once, codes and scales are written once.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -32,6 +34,52 @@ __device__ __forceinline__ float token_sum(float v) {
     if constexpr (CPT == 16)
         v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // other 8 of 16
     return v;
+}
+
+// Normalized Hadamard rotation of the token rows (Section 3.4, Appendix A.2):
+// fp32 butterflies (a, b) -> (a + b, a - b) on channel pairs (j, j + h) for
+// h = 1, 2, ..., d/2 in that order, then x fp32(1/sqrt(d)).  Lane chunk ch
+// holds channels 8 ch .. 8 ch + 7 of its token, so h = 1, 2, 4 pair values of
+// one lane and h = 8, 16, 32, 64 pair lanes ch ^ 1, ^ 2, ^ 4, ^ 8 of the
+// same token (one 16-lane DPP row at most).
+template <int CPT, int R>
+__device__ __forceinline__ void rotate_rows(float (&v)[R][8], int ch) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if ((i & h) == 0) {
+                    const float a = v[r][i], b = v[r][i + h];
+                    v[r][i] = a + b;
+                    v[r][i + h] = a - b;
+                }
+    auto stage = [&](auto down, auto up, int bit) {   // partner lane ch ^ bit
+        const bool hi = (ch & bit) != 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int x = __float_as_int(v[r][i]);
+                const float from_up = __int_as_float(__builtin_amdgcn_mov_dpp(x, decltype(up)::value, 0xF, 0xF, true));
+                const float from_down = __int_as_float(__builtin_amdgcn_mov_dpp(x, decltype(down)::value, 0xF, 0xF, true));
+                const float p = hi ? from_down : from_up;
+                v[r][i] = hi ? p - v[r][i] : v[r][i] + p;
+            }
+    };
+    // quad_perm [1,0,3,2] and [2,3,0,1] serve both lanes of a pair
+    stage(std::integral_constant<int, 0xB1>{}, std::integral_constant<int, 0xB1>{}, 1);
+    stage(std::integral_constant<int, 0x4E>{}, std::integral_constant<int, 0x4E>{}, 2);
+    // row_shr:4 brings lane - 4, row_shl:4 brings lane + 4 (same for 8)
+    stage(std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0x104>{}, 4);
+    if constexpr (CPT == 16)
+        stage(std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0x108>{}, 8);
+    constexpr float rs = CPT == 8 ? 0.125f : 0x1.6a09e6p-4f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[r][i] = v[r][i] * rs;
 }
 
 }  // namespace
@@ -66,7 +114,6 @@ __global__ void __launch_bounds__(256) quantize_kernel(const QuantArgs a) {
         const int nt = min(kBlock, de - bs);
 
         float v[R][8];
-        float amax = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int tok = tok0 + r * (64 / CPT);
@@ -78,9 +125,13 @@ __global__ void __launch_bounds__(256) quantize_kernel(const QuantArgs a) {
                 v[r][2 * k] = bf16_to_f32(w[k] & 0xFFFFu);
                 v[r][2 * k + 1] = bf16_to_f32(w[k] >> 16);
             }
+        }
+        if (tz.rot) rotate_rows<CPT, R>(v, ch);
+        float amax = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[r][k]));
-        }
         amax = wave_max_nonneg(amax);
         const int e = block_exponent_uniform(amax, -127);
         // codes = E4M3(x * 2^-e): the power-of-two scaling is exact, the

@@ -26,9 +26,9 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_defaults(L):
-    assert F.flamia_abi_version() == 2
+    assert F.flamia_abi_version() == 3
     o = F.flamia_default_opts()
-    assert (o.c_log2, o.tau, o.key_tile, o.rowsum) == (4, 4, 128, 0)
+    assert (o.c_log2, o.tau, o.key_tile, o.rowsum, o.hadamard) == (4, 4, 128, 0, 0)
     assert F.flamia_status_str(0) == "ok"
 
 
@@ -85,12 +85,15 @@ def test_invalid_arguments_return_status(call):
     bad_opts.c_log2, bad_opts.tau = 8, 2          # 2^(c+tau) = 1024 > 448
     tile_opts = F.flamia_default_opts()
     tile_opts.key_tile = 64
+    rot_opts = F.flamia_default_opts()
+    rot_opts.hadamard = 2
     assert call(dims(d=96)) == 2                  # FLAMIA_ERR_SHAPE
     assert call(dims(hq=6, hkv=4)) == 2
     assert call(dims(ttot=4096)) == 2             # beyond capacity
     assert call(dims(ndocs=0)) == 2
     assert call(dims(), opts=bad_opts) == 4       # FLAMIA_ERR_OPTS
     assert call(dims(), opts=tile_opts) == 4
+    assert call(dims(), opts=rot_opts) == 4
     assert call(dims(), ws_bytes=100) == 5        # FLAMIA_ERR_WORKSPACE
     assert call(dims(), ws=0) == 5                # NULL workspace is a workspace error (flamia.h)
     assert call(dims(), cu=0) == 1                # FLAMIA_ERR_NULL

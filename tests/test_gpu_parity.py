@@ -100,6 +100,26 @@ def test_represented_rowsum_mode(orc):
     _check_all(g, r)
 
 
+@pytest.mark.parametrize("case,doclen_cap", [("ragged-gqa-d64", None), ("ragged-gqa-d64", 0),
+                                             ("ragged-d128", None), ("ragged-d128", 0),
+                                             ("gqa-outliers", 0), ("packed-2k", None)])
+def test_hadamard_rotation_matches_oracle(orc, case, doclen_cap):
+    """Section 3.4 / Appendix A.2 option: Q and K are quantized from their
+    Hadamard-rotated rows (codes bit-exact against the oracle, which rotates
+    in the same fp32 butterfly order), V is not; dQ and dK are rotated back
+    (by the dQ pass that rebuilds dS-hat and by the one that reads the store)."""
+    inst = SMALL[case]()
+    say(f"[hadamard] {case} doclen_cap={doclen_cap}")
+    opts = F.flamia_default_opts()
+    opts.hadamard = 1
+    g = run_hip(inst, opts, doclen_cap=doclen_cap)
+    r = _oracle(orc, inst, orc.Opts(hadamard=1))
+    for name, rot in (("q", 1), ("k", 1), ("v", 0)):
+        rc, rs = orc.quantize(inst[name], inst["cu_seqlens"], orc.Opts(hadamard=rot))
+        assert np.array_equal(g[f"{name}_codes"], rc) and np.array_equal(g[f"{name}_scales"], rs), name
+    _check_all(g, r)
+
+
 def test_full_size_gqa_sampled_group(orc):
     """The full 4 x 8192, 32/8-head, d = 64 workload in the benchmark's launch
     configuration; the oracle computes key/value head 0 and its 4 query heads
