@@ -49,7 +49,7 @@ class _Params(ctypes.Structure):
         ("tau", ctypes.c_int32), ("key_tile", ctypes.c_int32), ("quant", ctypes.c_int32),
         ("rowsum", ctypes.c_int32), ("softmax_scale", ctypes.c_double),
         ("unsafe_bound", ctypes.c_int32), ("score_rel_err", ctypes.c_double),
-        ("hadamard", ctypes.c_int32),
+        ("hadamard", ctypes.c_int32), ("fast_exp", ctypes.c_int32),
     ]
 
 
@@ -78,6 +78,8 @@ def _load():
         lib.orc_scale_exp_array.argtypes = [P, ctypes.c_long, ctypes.c_int, P]
         lib.orc_double_to_bf16_array.argtypes = [P, ctypes.c_long, P]
         lib.orc_hadamard_f32_array.argtypes = [P, ctypes.c_long, ctypes.c_int, P]
+        lib.orc_schraudolph_exp2.restype = ctypes.c_float
+        lib.orc_schraudolph_exp2.argtypes = [ctypes.c_float]
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -98,12 +100,13 @@ class Opts:
     unsafe_bound: int = 0
     score_rel_err: float = 0.0   # > 0 with want_tol: decision-sensitivity bounds
     hadamard: int = 0            # 1: Hadamard rotation of Q and K (Section 3.4, Appendix A.2)
+    fast_exp: int = 0            # k of 8 key-pair classes use Schraudolph's exponential (forward only)
 
 
 def _params(ttot, ndocs, hq, hkv, d, opts: Opts) -> _Params:
     return _Params(ttot, ndocs, hq, hkv, d, opts.c_log2, opts.tau, opts.key_tile, opts.quant,
                    opts.rowsum, float(opts.softmax_scale), opts.unsafe_bound, float(opts.score_rel_err),
-                   opts.hadamard)
+                   opts.hadamard, opts.fast_exp)
 
 
 def max_threads() -> int:
@@ -152,6 +155,13 @@ def hadamard_f32(x_bits) -> np.ndarray:
     out = np.empty(x.shape, dtype=np.float32)
     _load().orc_hadamard_f32_array(_ptr(x), x.size // d, d, _ptr(out))
     return out
+
+
+def schraudolph_exp2(y) -> np.ndarray:
+    """Schraudolph's approximation of 2^y (Appendix C.2) of fp32 arguments."""
+    f = _load().orc_schraudolph_exp2
+    y = np.asarray(y, dtype=np.float32)
+    return np.array([f(float(v)) for v in y.ravel()], dtype=np.float32).reshape(y.shape)
 
 
 # ---- token-block quantizer --------------------------------------------------

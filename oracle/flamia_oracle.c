@@ -32,7 +32,9 @@
  *     the heads of the group before rounding;
  *   - the optional Hadamard rotation of Q and K is computed in fp32 by the
  *     butterfly in a fixed stage order (its values decide codes), and the
- *     gradients are rotated back in binary64.
+ *     gradients are rotated back in binary64;
+ *   - the optional inference exponential (Schraudolph) is evaluated bit for
+ *     bit on the fp32 argument, for the keys of k of every 8 key-pair classes.
  *
  * Parity: every exported function is pinned by CPU tests against definitions
  * that do not go through this file (a library FP8 codec, brute-force nearest
@@ -74,6 +76,11 @@ typedef struct {
     /* Hadamard rotation of Q and K before quantization (Section 3.4 and
      * Appendix A.2): 0 off, 1 on. */
     int32_t hadamard;
+    /* Inference-only exponential (Section 3.7, Appendix C.2): 0 = exact;
+     * k in 1..8 = Schraudolph's approximation for the forward's p' of keys
+     * whose pair class (bits 1, 3, 4 of the document-local key index) is
+     * below k, i.e. k of every 8 key pairs.  Forward only. */
+    int32_t fast_exp;
 } orc_params;
 
 /* ---------------------------------------------------------------------------
@@ -367,6 +374,36 @@ typedef struct {
     double *tol_o;  /* out: [d] */
 } row_tol;
 
+/* ---------------------------------------------------------------------------
+ * Schraudolph's exponential (Section 3.7; Appendix C.2).  One fp32 fused
+ * multiply-add t = 2^7 y + K, K = fp32(1.5 * 2^23 + 2^7 (127 - sigma)),
+ * sigma = 0.0573: adding 1.5 * 2^23 rounds 2^7 y to an integer held in the
+ * low mantissa bits of t, and those low 16 bits, read as a bf16 pattern,
+ * are 2^floor(z) (1 + {z}) with z = y - sigma' (7 fraction bits; K is an
+ * integer, so the offset in effect is sigma' = 7/128).  The pattern is
+ * moved to the high half of a float and clamped at zero.  The argument y is
+ * the fp32 value the kernel exponentiates.
+ * ------------------------------------------------------------------------- */
+float orc_schraudolph_exp2(float y)
+{
+    const float K = (float)(12582912.0 + 128.0 * (127.0 - 0.0573));
+    float t = fmaf(128.0f, y, K);
+    uint32_t bits;
+    int32_t hi;
+    float v;
+    memcpy(&bits, &t, 4);
+    hi = (int32_t)(bits << 16);
+    if (hi < 0) hi = 0;
+    memcpy(&v, &hi, 4);
+    return v;
+}
+
+/* pair class of a document-local key: bits 1, 3 and 4 of its index */
+static int key_pair_class(int j)
+{
+    return ((j >> 1) & 1) | (((j >> 3) & 1) << 1) | (((j >> 4) & 1) << 2);
+}
+
 static void fwd_row(const orc_params *p, int i, const double *qi, const double *Kt,
                     const double *Vt, double c1, double *acc, double *x,
                     double *o_out, double *lse_out, int64_t *sat, row_tol *rt)
@@ -407,7 +444,10 @@ static void fwd_row(const orc_params *p, int i, const double *qi, const double *
             }
         }
         for (int j = j0; j < j1; ++j) {
-            double pj = exp2(x[j - j0] - m), w;
+            const int approx = p->fast_exp > 0 && quant != QUANT_NONE && key_pair_class(j) < p->fast_exp;
+            /* approximated: p' = 2^c p is formed from the fp32 argument x - m + c */
+            double pj = approx ? (double)orc_schraudolph_exp2((float)(x[j - j0] - m + p->c_log2)) / two_c
+                               : exp2(x[j - j0] - m), w;
             const double *vj = Vt + (long)j * d;
             if (quant == QUANT_NONE) {
                 w = pj;
@@ -420,7 +460,11 @@ static void fwd_row(const orc_params *p, int i, const double *qi, const double *
                 w = orc_e4m3_value(code);
                 l += (p->rowsum == 1) ? w / two_c : pj;
                 if (track) {
-                    double sw = code_swing(y, rt->delta[j - j0] + dm, loose);
+                    /* the approximation's log2 slope is at most 1/ln 2, and the
+                     * kernel may land one 1/128 step away */
+                    double band = rt->delta[j - j0] + dm;
+                    if (approx) band = band / log(2.0) + log2(1.0 + 1.0 / 128.0);
+                    double sw = code_swing(y, band, loose);
                     if (sw > 0.0) {
                         for (int k = 0; k < d; ++k) rt->tacc[k] += sw * fabs(vj[k]);
                         if (p->rowsum == 1) tl += sw / two_c;
@@ -436,10 +480,12 @@ static void fwd_row(const orc_params *p, int i, const double *qi, const double *
         *lse_out = m + log2(l);
         if (track) {
             /* codes that may move, plus the smooth movement of the row sum */
-            double rel_l = log(2.0) * (dmax + dm);
+            double band2 = dmax + dm;                 /* log2 band of one p */
+            if (p->fast_exp > 0) band2 = band2 / log(2.0) + log2(1.0 + 1.0 / 128.0);
+            double rel_l = log(2.0) * band2;
             for (int k = 0; k < d; ++k)
                 rt->tol_o[k] = rt->tacc[k] / den + fabs(o_out[k]) * (tl / l + rel_l);
-            rt->tol_lse = dmax + dm + log2(1.0 + tl / l) + 0x1p-20 * (1.0 + fabs(*lse_out));
+            rt->tol_lse = band2 + log2(1.0 + tl / l) + 0x1p-20 * (1.0 + fabs(*lse_out));
         }
     }
 }
@@ -739,6 +785,8 @@ int orc_attention(const orc_params *p, const uint16_t *q, const uint16_t *k, con
     int err = ORC_OK;
     if (!p || !q || !k || !v || p->d <= 0 || p->hq <= 0 || p->hkv <= 0 || p->hq % p->hkv)
         return ORC_ERR_ARG;
+    /* the approximate exponential is for the forward only (Section 3.7) */
+    if (p->fast_exp < 0 || p->fast_exp > 8 || (p->fast_exp > 0 && dout)) return ORC_ERR_ARG;
     if (p->key_tile <= 0 || p->quant < 0 || p->quant > 2 || !check_cu(p, cu)) return ORC_ERR_ARG;
     /* Section 3.4 / Appendix B.1: c + tau <= log2(448) keeps 2^c p below the
      * largest E4M3 value; anything else is rejected. */
