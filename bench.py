@@ -131,6 +131,51 @@ def cpu_baseline(inst, hkv, hadamard=0):
                       f"documents, forward + backward incl. quantization; {dt:.1f} s wall"}
 
 
+def inference_bench(args, call, q, k, v, cu, stream, hip, wl, inst, doclen_cap):
+    """Inference call: flamia_fwd alone (quantize Q/K/V, work list, forward)
+    with fast_exp key-pair classes on Schraudolph's exponential (Section 3.7,
+    Appendix C.2).  FLOP = 2 * Hq * d * sum(L^2) (S and PV, causal)."""
+    import torch
+    call.opts.fast_exp = args.inference
+    T, hq, d = inst["q"].shape
+    for _ in range(args.warmup):
+        call.forward(q, k, v, cu, stream)
+    torch.cuda.synchronize()
+    nf = len(FWD_PHASES) + 1
+    ev = hip.events(nf * args.steps)
+    for i in range(args.steps):
+        fe = (ctypes.c_void_p * nf)(*ev[i * nf:(i + 1) * nf])
+        call.opts.phase_events, call.opts.n_events = ctypes.cast(fe, ctypes.POINTER(ctypes.c_void_p)), nf
+        call.forward(q, k, v, cu, stream)
+    call.opts.phase_events, call.opts.n_events = None, 0
+    torch.cuda.synchronize()
+    phases = {p: sum(hip.elapsed_ms(ev[i * nf + j], ev[i * nf + j + 1]) for i in range(args.steps)) / args.steps
+              for j, p in enumerate(FWD_PHASES)}
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        call.forward(q, k, v, cu, stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    flop = 2.0 * hq * d * inst["sum_L2"]
+    kern = phases["fwd_kernel"]
+    print(json.dumps({
+        "metric": "inference forward TFLOP/s incl. quant (MXFP8, packed docs)",
+        "value": round(flop / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "dtype": "fp8e4m3", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "hq": hq, "hkv": inst["k"].shape[1], "d": d,
+                   "sum_L2": inst["sum_L2"], "seed": args.seed, "fast_exp": args.inference,
+                   "hadamard": args.hadamard},
+        "phases_ms": {p: round(t, 4) for p, t in phases.items()},
+        "roofline": {"kernel": "fwd_kernel", "kernel_ms": round(kern, 4), "bound": "mfma",
+                     "achieved": round(flop / (kern * 1e-3) / 1e12, 2), "peak": MXFP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flop / (kern * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +190,10 @@ def main():
                          "blocks is faster on MI355X, and no store at d = 64, where rebuilding is")
     ap.add_argument("--hadamard", type=int, default=0, choices=(0, 1),
                     help="1: Hadamard rotation of Q and K before quantization (the pages' default at d = 128)")
+    ap.add_argument("--inference", type=int, default=-1, choices=(-1, 0, 5, 8),
+                    help="time the inference call (quantization + forward only) with the "
+                         "approximate exponential on 0, 5 or 8 of the 8 key-pair classes "
+                         "(a separate metric; -1, the default: the training call)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a fill and a widening copy of this many MiB (known-size "
                          "references for hardware byte counters collected over the same run)")
@@ -197,6 +246,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.inference >= 0:
+        inference_bench(args, call, q, k, v, cu, stream, hip, wl, inst, doclen_cap)
+        return
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):

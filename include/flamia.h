@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FLAMIA_ABI_VERSION 3
+#define FLAMIA_ABI_VERSION 4
 
 typedef enum {
     FLAMIA_OK = 0,
@@ -91,6 +91,13 @@ typedef struct {
                               (fp32 butterfly, strides 1, 2, ..., d/2, then x fp32(1/sqrt(d))),
                               and flamia_bwd rotates dQ and dK back.  flamia_bwd must be
                               given the value flamia_fwd had.  0 (default): off */
+    int32_t fast_exp;      /* inference only (Section 3.7, Appendix C.2): 0 (default) = exact
+                              exponential; 5 or 8 = Schraudolph's approximation of
+                              p' = 2^(x - m + c) for the keys of 5 (the paper's split) or all 8
+                              of the 8 key-pair classes (class = bits 1, 3, 4 of the
+                              document-local key index).  The forward's O and lse2 then come from
+                              the approximate values; flamia_bwd returns FLAMIA_ERR_OPTS for a
+                              non-zero value (the backward rebuilds P with the exact exponential) */
     /* Optional phase timing: when phase_events is non-NULL it points to
      * n_events hipEvent_t handles (created by the caller); the call records
      * event i on `stream` before its i-th internal launch and the next one

@@ -50,6 +50,7 @@ flamia_status_t check_opts(const flamia_opts_t* o) {
     if (o->key_tile != kTile) return FLAMIA_ERR_OPTS;
     if (o->rowsum != 0 && o->rowsum != 1) return FLAMIA_ERR_OPTS;
     if (o->hadamard != 0 && o->hadamard != 1) return FLAMIA_ERR_OPTS;
+    if (o->fast_exp != 0 && o->fast_exp != 5 && o->fast_exp != 8) return FLAMIA_ERR_OPTS;
     if (!(o->softmax_scale <= 0.f || isfinite(o->softmax_scale))) return FLAMIA_ERR_OPTS;
     if (o->n_events < 0 || (o->n_events > 0 && !o->phase_events)) return FLAMIA_ERR_OPTS;
     return FLAMIA_OK;
@@ -125,6 +126,7 @@ flamia_opts_t flamia_default_opts(void) {
     o.rowsum = 0;
     o.softmax_scale = 0.f;
     o.hadamard = 0;
+    o.fast_exp = 0;
     o.phase_events = nullptr;
     o.n_events = 0;
     return o;
@@ -219,6 +221,7 @@ flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     fa.c_log2 = (float)opts.c_log2;
     fa.tau = (float)opts.tau;
     fa.rowsum = opts.rowsum;
+    fa.fast_exp = opts.fast_exp;
     if ((e = pm.mark()) != hipSuccess || (e = launch_fwd(fa, d, w.max_tiles * dims->hq, st)) != hipSuccess)
         return hip_fail(e);
     e = pm.mark();
@@ -235,6 +238,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     if (s != FLAMIA_OK) return s;
     const flamia_opts_t opts = resolve(opts_in);
     if ((s = check_opts(&opts)) != FLAMIA_OK) return s;
+    if (opts.fast_exp != 0) return FLAMIA_ERR_OPTS;     // inference-only exponential (Section 3.7)
     if (!d_o || !o || !lse2 || !cu_seqlens || !dq || !dk || !dv || !q_mx.codes || !q_mx.scales ||
         !k_mx.codes || !k_mx.scales || !v_mx.codes || !v_mx.scales)
         return FLAMIA_ERR_NULL;

@@ -34,7 +34,23 @@ struct FwdSmem {
     uint8_t ev[kTile];
 };
 
-template <int D, int ROWSUM>
+// Schraudolph's exponential (inference only; paper Section 3.7, Appendix
+// C.2): t = 2^7 y + K in one fp32 FMA, K = 1.5 * 2^23 + 2^7 (127 - 0.0573)
+// rounded to fp32 (an integer), so 2^7 y is rounded to an integer in the low
+// mantissa bits of t; those low 16 bits are the bf16 pattern of
+// 2^floor(z) (1 + {z}), z = y - 7/128, moved to the high half of a float and
+// clamped at zero.  Here y = x c1 + (c - m) and the per-row part is folded
+// into the constant: t = s * (2^7 c1) + (2^7 (c - m) + K), one FMA per score.
+constexpr float kSchraudolphK = (float)(12582912.0 + 128.0 * (127.0 - 0.0573));
+
+// Key-pair class of accumulator register i (key bits 1, 3, 4; see the key
+// layout of the S^T tiles): registers of classes below FAST take the
+// approximation.
+__device__ __forceinline__ constexpr int pair_class(int i) {
+    return ((i >> 1) & 1) | (((i >> 2) & 1) << 1) | (((i >> 3) & 1) << 2);
+}
+
+template <int D, int ROWSUM, int FAST>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs a) {
     constexpr int KC = D / 64;                    // 64-channel contraction steps of S
     constexpr int DT = D / 32;                    // 32-row channel tiles of O^T
@@ -159,6 +175,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
         }
         m = m_new;
         const float nmc = a.c_log2 - m;                 // p' = 2^(x - m + c)
+        const float c1x128 = a.c1 * 128.f;              // exact (power of two)
+        const float kofs = fmaf(128.f, nmc, kSchraudolphK);
+        auto pexp = [&](float sv, int i) -> float {
+            if (FAST > 0 && pair_class(i) < FAST) {
+                const int b = max(__float_as_int(fmaf(sv, c1x128, kofs)) << 16, 0);
+                return __int_as_float(b);
+            }
+            return exp2_fast(fmaf(sv, a.c1, nmc));
+        };
         // ---- p' = 2^c p and P-hat codes in operand byte order (byte i of a
         // sub-tile = accumulator register i)
         int pc[4][4];
@@ -170,10 +195,10 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
                     pc[kk][j] = 0;
                     continue;
                 }
-                const float p0 = exp2_fast(fmaf(s[kk][4 * j], a.c1, nmc));
-                const float p1 = exp2_fast(fmaf(s[kk][4 * j + 1], a.c1, nmc));
-                const float p2 = exp2_fast(fmaf(s[kk][4 * j + 2], a.c1, nmc));
-                const float p3 = exp2_fast(fmaf(s[kk][4 * j + 3], a.c1, nmc));
+                const float p0 = pexp(s[kk][4 * j], 4 * j);
+                const float p1 = pexp(s[kk][4 * j + 1], 4 * j + 1);
+                const float p2 = pexp(s[kk][4 * j + 2], 4 * j + 2);
+                const float p3 = pexp(s[kk][4 * j + 3], 4 * j + 3);
                 const int w = pack_fp8x4(p0, p1, p2, p3);
                 pc[kk][j] = w;
                 if constexpr (ROWSUM == 0) l += (p0 + p1) + (p2 + p3);
@@ -216,15 +241,22 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
     }
 }
 
+template <int D, int ROWSUM>
+static void launch_fwd_fast(const FwdArgs& a, dim3 g, dim3 b, hipStream_t st) {
+    if (a.fast_exp == 8) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 8>), g, b, 0, st, a);
+    else if (a.fast_exp == 5) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 5>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 0>), g, b, 0, st, a);
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int d, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), b(256);
     if (d == 64) {
-        if (a.rowsum) hipLaunchKernelGGL((fwd_kernel<64, 1>), g, b, 0, st, a);
-        else hipLaunchKernelGGL((fwd_kernel<64, 0>), g, b, 0, st, a);
+        if (a.rowsum) launch_fwd_fast<64, 1>(a, g, b, st);
+        else launch_fwd_fast<64, 0>(a, g, b, st);
     } else {
-        if (a.rowsum) hipLaunchKernelGGL((fwd_kernel<128, 1>), g, b, 0, st, a);
-        else hipLaunchKernelGGL((fwd_kernel<128, 0>), g, b, 0, st, a);
+        if (a.rowsum) launch_fwd_fast<128, 1>(a, g, b, st);
+        else launch_fwd_fast<128, 0>(a, g, b, st);
     }
     return hipGetLastError();
 }

@@ -62,6 +62,7 @@ struct FwdArgs {
     float c1;              // softmax_scale * log2(e)
     float c_log2, tau;
     int rowsum;
+    int fast_exp;          // 0, or 5 / 8 key-pair classes of 8 with the approximate exponential
 };
 
 struct BwdArgs {

@@ -26,9 +26,9 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_defaults(L):
-    assert F.flamia_abi_version() == 3
+    assert F.flamia_abi_version() == 4
     o = F.flamia_default_opts()
-    assert (o.c_log2, o.tau, o.key_tile, o.rowsum, o.hadamard) == (4, 4, 128, 0, 0)
+    assert (o.c_log2, o.tau, o.key_tile, o.rowsum, o.hadamard, o.fast_exp) == (4, 4, 128, 0, 0, 0)
     assert F.flamia_status_str(0) == "ok"
 
 
@@ -87,6 +87,8 @@ def test_invalid_arguments_return_status(call):
     tile_opts.key_tile = 64
     rot_opts = F.flamia_default_opts()
     rot_opts.hadamard = 2
+    fast_bad = F.flamia_default_opts()
+    fast_bad.fast_exp = 3                         # only 0, 5 or 8 key-pair classes
     assert call(dims(d=96)) == 2                  # FLAMIA_ERR_SHAPE
     assert call(dims(hq=6, hkv=4)) == 2
     assert call(dims(ttot=4096)) == 2             # beyond capacity
@@ -94,10 +96,21 @@ def test_invalid_arguments_return_status(call):
     assert call(dims(), opts=bad_opts) == 4       # FLAMIA_ERR_OPTS
     assert call(dims(), opts=tile_opts) == 4
     assert call(dims(), opts=rot_opts) == 4
+    assert call(dims(), opts=fast_bad) == 4
     assert call(dims(), ws_bytes=100) == 5        # FLAMIA_ERR_WORKSPACE
     assert call(dims(), ws=0) == 5                # NULL workspace is a workspace error (flamia.h)
     assert call(dims(), cu=0) == 1                # FLAMIA_ERR_NULL
     assert call(dims(), o=FAKE + 4) == 3          # FLAMIA_ERR_ALIGN
+
+
+def test_backward_refuses_inference_exponential():
+    """Section 3.7: the approximate exponential is for inference only; the
+    backward rebuilds P with the exact one."""
+    o = F.flamia_default_opts()
+    o.fast_exp = 5
+    assert call_bwd(dims(), opts=o) == 4          # FLAMIA_ERR_OPTS
+    o.fast_exp = 0
+    assert call_bwd(dims(), opts=o) != 4
 
 
 def test_quantize_validation():

@@ -120,6 +120,26 @@ def test_hadamard_rotation_matches_oracle(orc, case, doclen_cap):
     _check_all(g, r)
 
 
+@pytest.mark.parametrize("k", [5, 8])
+@pytest.mark.parametrize("case", ["ragged-gqa-d64", "ragged-d128", "gqa-outliers", "packed-2k"])
+def test_inference_exponential_forward_matches_oracle(orc, case, k):
+    """Section 3.7 / Appendix C.2 inference forward: Schraudolph's exponential
+    for the keys of k of 8 key-pair classes; O and lse2 against the oracle's
+    bit-level model of the same approximation."""
+    inst = SMALL[case]()
+    say(f"[fast_exp={k}] {case}")
+    opts = F.flamia_default_opts()
+    opts.fast_exp = k
+    g = run_hip(inst, opts, backward=False)
+    fwd = {n: inst[n] for n in ("q", "k", "v", "cu_seqlens")}
+    fwd["do"] = None
+    r = _oracle(orc, fwd, orc.Opts(fast_exp=k))
+    assert_close("O", g["o"], r["o64"], r["tol_o"])
+    lse_err = np.abs(g["lse2"] - r["lse2"])
+    say(f"  lse2: max abs err {lse_err.max():.3e}")
+    assert (lse_err <= r["tol_lse"] + 1e-5).all()
+
+
 def test_full_size_gqa_sampled_group(orc):
     """The full 4 x 8192, 32/8-head, d = 64 workload in the benchmark's launch
     configuration; the oracle computes key/value head 0 and its 4 query heads
