@@ -1,0 +1,112 @@
+"""Edge cases of the HIP path against the oracle (through the C ABI).
+
+- degenerate documents in one call: Q = K = 0 (every score 0: uniform
+  attention, all-zero token blocks with the lowest exponent), V = 0 (O = 0,
+  dS = 0), dO = 0 (every gradient 0), keys all equal (sum_j dS_ij = 0, so
+  dQ is only what quantizing dS leaves), next to an ordinary document;
+- the largest call the library accepts: 2^20 tokens (the token capacity),
+  thousands of documents from 1 token up, compared on a sample of documents
+  that includes the first, the last and the longest;
+- the long-document d = 128 workload (1 x 32768, 16 heads) in the benchmark's
+  launch configuration (dS store), compared on one head over every document
+  but the longest.
+"""
+import numpy as np
+import pytest
+
+from precision_causal_attention_amd import workloads as W
+
+from gpu_util import SCORE_REL_ERR, assert_close, run_hip, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.build(force=False)
+    return oracle
+
+
+def _oracle(orc, inst, **kw):
+    return orc.attention(inst["q"], inst["k"], inst["v"], inst["do"], inst["cu_seqlens"],
+                         orc.Opts(score_rel_err=SCORE_REL_ERR), want_tol=True, **kw)
+
+
+def _check_rows(g, r, rows, heads=slice(None), kvheads=slice(None)):
+    assert_close("O", g["o"][rows][:, heads], r["o64"][rows][:, heads], r["tol_o"][rows][:, heads])
+    lse_err = np.abs(g["lse2"][heads][:, rows] - r["lse2"][heads][:, rows])
+    say(f"  lse2: max abs err {lse_err.max():.3e}")
+    assert (lse_err <= r["tol_lse"][heads][:, rows] + 1e-5).all()
+    assert_close("dQ", g["dq"][rows][:, heads], r["dq64"][rows][:, heads], r["tol_dq"][rows][:, heads])
+    assert_close("dK", g["dk"][rows][:, kvheads], r["dk64"][rows][:, kvheads], r["tol_dk"][rows][:, kvheads])
+    assert_close("dV", g["dv"][rows][:, kvheads], r["dv64"][rows][:, kvheads], r["tol_dv"][rows][:, kvheads])
+
+
+@pytest.mark.parametrize("doclen_cap", [0, None])
+def test_degenerate_documents(orc, doclen_cap):
+    lens = [200, 150, 130, 180, 170]
+    inst = W.generate(W.custom("degenerate", lens, 4, 2, 64), 5, lens=lens)
+    cu = inst["cu_seqlens"]
+    zero = W.bf16_bits(np.zeros(1, np.float32))[0]
+    a0, a1 = cu[0], cu[1]                                  # Q = K = 0
+    inst["q"][a0:a1] = zero
+    inst["k"][a0:a1] = zero
+    inst["v"][cu[1]:cu[2]] = zero                          # V = 0
+    inst["do"][cu[2]:cu[3]] = zero                         # dO = 0
+    inst["k"][cu[3]:cu[4]] = inst["k"][cu[3]]              # every key of the document equal
+    say(f"[degenerate] doclen_cap={doclen_cap}")
+    g = run_hip(inst, doclen_cap=doclen_cap)
+    r = _oracle(orc, inst)
+    _check_rows(g, r, slice(None))
+    # exact zeros where the method gives exact zeros
+    for key, rng in (("dq", (cu[2], cu[3])), ("dk", (cu[2], cu[3])), ("dv", (cu[2], cu[3])),
+                     ("o", (cu[1], cu[2])), ("dq", (cu[1], cu[2])), ("dk", (cu[1], cu[2]))):
+        vals = W.bits_to_f32(g[key][rng[0]:rng[1]])
+        assert not np.any(vals), key
+    # Q = K = 0: uniform attention, the scale tables hold the lowest exponent
+    assert not np.any(g["q_codes"][a0:a1]) and np.all(g["q_scales"][:, a0:a1] == 0)
+
+
+def _max_size_lengths(total, rng):
+    lens = []
+    while sum(lens) < total:
+        L = int(np.clip(np.rint(np.exp(rng.normal(np.log(200.0), 1.5))), 1, 4096))
+        lens.append(min(L, total - sum(lens)))
+    lens[0] = 1                                            # a one-token document first
+    lens[-1] += total - sum(lens)
+    return lens
+
+
+def test_maximum_size_call(orc):
+    total = 1 << 20                                        # the library's token capacity
+    lens = _max_size_lengths(total, np.random.default_rng(91))
+    inst = W.generate(W.custom("max", lens, 1, 1, 64), 7, lens=lens)
+    cu = inst["cu_seqlens"]
+    nd = len(lens)
+    pick = sorted({0, 1, nd - 1, int(np.argmax(lens)), nd // 3, (2 * nd) // 3})
+    say(f"[max size] T={total} docs={nd} longest={max(lens)} checked docs={pick}")
+    g = run_hip(inst, doclen_cap=0)
+    mask = np.zeros(nd, np.uint8)
+    mask[pick] = 1
+    r = _oracle(orc, inst, doc_mask=mask)
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in pick])
+    _check_rows(g, r, rows)
+
+
+def test_long_32k_d128_sampled_head(orc):
+    """Head 0 of every document but the longest (a single binary64 unit of
+    6225 tokens would take the oracle about a minute on one thread)."""
+    inst = W.generate("long-32k", 0)
+    lens = inst["lengths"]
+    cu = inst["cu_seqlens"]
+    skip = int(np.argmax(lens))
+    say(f"[full] long-32k docs={len(lens)} longest={max(lens)} (not compared)")
+    g = run_hip(inst, doclen_cap=32768)                    # the benchmark's store capacity
+    km = np.zeros(16, np.uint8)
+    km[0] = 1
+    dm = np.ones(len(lens), np.uint8)
+    dm[skip] = 0
+    r = _oracle(orc, inst, kv_mask=km, doc_mask=dm)
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in range(len(lens)) if i != skip])
+    _check_rows(g, r, rows, heads=slice(0, 1), kvheads=slice(0, 1))
