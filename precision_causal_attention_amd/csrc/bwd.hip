@@ -32,7 +32,7 @@ namespace flamia {
 constexpr int kQStep = 64;
 
 template <int D>
-struct BwdSmem {
+struct BwdStep {
     static constexpr int kStride = D + 16;       // row pitch of code tiles
     uint8_t q[kQStep * kStride];
     uint8_t o[kQStep * kStride];                 // quantized dO
@@ -40,6 +40,15 @@ struct BwdSmem {
     alignas(16) float dv[kQStep];                // -D
     uint8_t eq[kQStep];
     uint8_t eo[kQStep];
+};
+
+// Step buffers: with the software pipeline (d = 64) the products of step i
+// read buffer i % 2 while the dV/dK products of step i - 1 still read the
+// other one.
+template <int D>
+struct BwdSmem {
+    static constexpr int kStride = BwdStep<D>::kStride;
+    BwdStep<D> buf[D == 64 ? 2 : 1];
 };
 
 template <int D, bool STORE>
@@ -94,19 +103,19 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             p_dv = a.dvec[(long)h * a.ttot + qr];
         }
     };
-    auto store_step = [&]() {
+    auto store_step = [&](BwdStep<D>& b) {
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
             const int c = tid + 256 * r;
             const int row = c / (D / 16), col = (c % (D / 16)) * 16;
-            *reinterpret_cast<u32x4*>(&sm.q[row * STR + col]) = pq[r];
-            *reinterpret_cast<u32x4*>(&sm.o[row * STR + col]) = po[r];
+            *reinterpret_cast<u32x4*>(&b.q[row * STR + col]) = pq[r];
+            *reinterpret_cast<u32x4*>(&b.o[row * STR + col]) = po[r];
         }
         if (tid < kQStep) {
-            sm.eq[tid] = (uint8_t)p_eq;
-            sm.eo[tid] = (uint8_t)p_eo;
-            sm.lse[tid] = p_in ? p_lse : INFINITY;   // +inf: row outside the document
-            sm.dv[tid] = -p_dv;                       // -D: accumulator input of dP
+            b.eq[tid] = (uint8_t)p_eq;
+            b.eo[tid] = (uint8_t)p_eo;
+            b.lse[tid] = p_in ? p_lse : INFINITY;   // +inf: row outside the document
+            b.dv[tid] = -p_dv;                       // -D: accumulator input of dP
         }
     };
     load_step(g * G, kt0);
@@ -138,6 +147,38 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     const int tr_col = 16 * grp + 8 * (s16 & 1);
     const float inv256 = 1.f / 256.f;
 
+    // dV^T += dO^T P-hat_b and dK^T += Q^T dS-hat of one step (contraction
+    // over its 64 queries), from its codes and its step buffer
+    auto dvdk = [&](const BwdStep<D>& b, const int (&pbc)[2][4], const int (&dsc)[2][4], const int (&es)[2]) {
+        const v8i pb = v8i{pbc[0][0], pbc[0][1], pbc[0][2], pbc[0][3], pbc[1][0], pbc[1][1], pbc[1][2], pbc[1][3]};
+        const v8i db = v8i{dsc[0][0], dsc[0][1], dsc[0][2], dsc[0][3], dsc[1][0], dsc[1][1], dsc[1][2], dsc[1][3]};
+        const int so = b.eo[32 * lg], sq = b.eq[32 * lg];
+        const int sd = lg ? es[1] : es[0];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            v2i r[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                r[rr] = lds_read_tr8(&b.o[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+            const v8i oa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+            dvt[dt] = mfma_mx(oa, pb, dvt[dt], so, 127 - 8);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                r[rr] = lds_read_tr8(&b.q[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+            const v8i qa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+            dkt[dt] = mfma_mx(qa, db, dkt[dt], sq, sd);
+        }
+    };
+    // Software pipeline (d = 64, no dS store): the dV/dK products of a step are issued in
+    // the next step, right after its S and dP products, so that they run on
+    // the matrix cores while the wave computes the next softmax.  At d = 128
+    // the extra live codes cost an occupancy step, and with the store they
+    // spill, so the products follow their own step there.
+    constexpr bool PIPE = D == 64 && !STORE;
+    int cur = 0;                           // step buffer of the current step
+    bool dvdk_due = false;                 // the previous step's dV/dK products are pending
+    int ppbc[2][4], pdsc[2][4], pes[2];
+
     int hh = 0, q0 = kt0;
     // dS blocks of the previous step, stored at the start of the next one
     u32x4 pend_w[2];
@@ -160,8 +201,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     auto step = [&](auto mask_tag) -> bool {
         constexpr bool MASK = decltype(mask_tag)::value;
         // ---- publish the prefetched step in LDS, start fetching the next one
-        __syncthreads();
-        store_step();
+        BwdStep<D>& B = sm.buf[cur];
+        __syncthreads();                   // buffer cur: its last readers were two steps ago
+        store_step(B);
         __syncthreads();
         const int h = g * G + hh;
         const int qs0 = q0;
@@ -192,7 +234,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             // the same error as a separate fp32 subtraction
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float4 d4 = *reinterpret_cast<const float4*>(&sm.dv[32 * st + 8 * j + 4 * lg]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&B.dv[32 * st + 8 * j + 4 * lg]);
                 pacc[st][4 * j] = d4.x;
                 pacc[st][4 * j + 1] = d4.y;
                 pacc[st][4 * j + 2] = d4.z;
@@ -200,16 +242,18 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             }
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                uint4 lo = *reinterpret_cast<const uint4*>(&sm.q[row * STR + 64 * kc + 16 * lg]);
-                uint4 hi = *reinterpret_cast<const uint4*>(&sm.q[row * STR + 64 * kc + 32 + 16 * lg]);
+                uint4 lo = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 16 * lg]);
+                uint4 hi = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 32 + 16 * lg]);
                 const v8i qa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                sacc[st] = mfma_mx(qa, kb[kc], sacc[st], sm.eq[row], ek);
-                lo = *reinterpret_cast<const uint4*>(&sm.o[row * STR + 64 * kc + 16 * lg]);
-                hi = *reinterpret_cast<const uint4*>(&sm.o[row * STR + 64 * kc + 32 + 16 * lg]);
+                sacc[st] = mfma_mx(qa, kb[kc], sacc[st], B.eq[row], ek);
+                lo = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 16 * lg]);
+                hi = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 32 + 16 * lg]);
                 const v8i oa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                pacc[st] = mfma_mx(oa, vb[kc], pacc[st], sm.eo[row], ev);
+                pacc[st] = mfma_mx(oa, vb[kc], pacc[st], B.eo[row], ev);
             }
         }
+        // ---- the previous step's dV/dK products, under this step's softmax
+        if (PIPE && dvdk_due) dvdk(sm.buf[cur ^ 1], ppbc, pdsc, pes);
         // ---- P, P-hat_b, dS, dS-hat (one 32x32 block per accumulator tile)
         // accumulator register i = 4j + r of query block st holds query
         // qs0 + 32st + 8j + 4lg + r; masked while the wave's key lies after it
@@ -228,7 +272,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int q4 = 32 * st + 8 * j + 4 * lg;            // 4 consecutive query rows
-                const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse[q4]);
+                const float4 l4 = *reinterpret_cast<const float4*>(&B.lse[q4]);
                 const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -276,25 +320,22 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
                 pend_e[st] = es[st];
             }
         }
-        // ---- dV^T += dO^T P-hat_b and dK^T += Q^T dS-hat (contraction over the 64 queries)
-        if (!skipped(1)) {                     // (block 1 skipped implies block 0 skipped)
-            const v8i pb = v8i{pbc[0][0], pbc[0][1], pbc[0][2], pbc[0][3], pbc[1][0], pbc[1][1], pbc[1][2], pbc[1][3]};
-            const v8i db = v8i{dsc[0][0], dsc[0][1], dsc[0][2], dsc[0][3], dsc[1][0], dsc[1][1], dsc[1][2], dsc[1][3]};
-            const int so = sm.eo[32 * lg], sq = sm.eq[32 * lg];
+        // ---- this step's dV/dK products (block 1 skipped implies block 0
+        // skipped: nothing to add), in the next step when pipelined
+        if constexpr (PIPE) {
+            dvdk_due = !skipped(1);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                v2i r[4];
+            for (int st = 0; st < 2; ++st) {
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    r[rr] = lds_read_tr8(&sm.o[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
-                const v8i oa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
-                dvt[dt] = mfma_mx(oa, pb, dvt[dt], so, 127 - 8);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    r[rr] = lds_read_tr8(&sm.q[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
-                const v8i qa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
-                dkt[dt] = mfma_mx(qa, db, dkt[dt], sq, es[lg]);
+                for (int j = 0; j < 4; ++j) {
+                    ppbc[st][j] = pbc[st][j];
+                    pdsc[st][j] = dsc[st][j];
+                }
+                pes[st] = es[st];
             }
+            cur ^= 1;
+        } else if (!skipped(1)) {
+            dvdk(B, pbc, dsc, es);
         }
         return more;
     };
@@ -305,6 +346,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
         while (more && q0 < kt0 + kTile) more = step(std::true_type{});
         while (more && q0 >= kt0 + kTile) more = step(std::false_type{});
     }
+    if (PIPE && dvdk_due) dvdk(sm.buf[cur ^ 1], ppbc, pdsc, pes);
     flush_store();
     // ---- epilogue: dK = softmax_scale * sum, dV; summed over the group's heads.
     // With the Hadamard option the dK sum is the gradient of the rotated K and
