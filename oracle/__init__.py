@@ -49,7 +49,7 @@ class _Params(ctypes.Structure):
         ("tau", ctypes.c_int32), ("key_tile", ctypes.c_int32), ("quant", ctypes.c_int32),
         ("rowsum", ctypes.c_int32), ("softmax_scale", ctypes.c_double),
         ("unsafe_bound", ctypes.c_int32), ("score_rel_err", ctypes.c_double),
-        ("hadamard", ctypes.c_int32), ("fast_exp", ctypes.c_int32),
+        ("hadamard", ctypes.c_int32), ("fast_exp", ctypes.c_int32), ("mixed", ctypes.c_int32),
     ]
 
 
@@ -78,6 +78,13 @@ def _load():
         lib.orc_scale_exp_array.argtypes = [P, ctypes.c_long, ctypes.c_int, P]
         lib.orc_double_to_bf16_array.argtypes = [P, ctypes.c_long, P]
         lib.orc_hadamard_f32_array.argtypes = [P, ctypes.c_long, ctypes.c_int, P]
+        lib.orc_e2m1_value.restype = ctypes.c_double
+        lib.orc_e2m1_value.argtypes = [ctypes.c_uint8]
+        lib.orc_e2m1_encode.restype = ctypes.c_uint8
+        lib.orc_e2m1_encode.argtypes = [ctypes.c_double]
+        lib.orc_nvfp4_scale.restype = ctypes.c_uint8
+        lib.orc_nvfp4_scale.argtypes = [ctypes.c_double]
+        lib.orc_nvfp4_rows.argtypes = [P, ctypes.c_long, ctypes.c_int, ctypes.c_int, P]
         lib.orc_schraudolph_exp2.restype = ctypes.c_float
         lib.orc_schraudolph_exp2.argtypes = [ctypes.c_float]
         lib.orc_max_threads.restype = ctypes.c_int
@@ -101,12 +108,13 @@ class Opts:
     score_rel_err: float = 0.0   # > 0 with want_tol: decision-sensitivity bounds
     hadamard: int = 0            # 1: Hadamard rotation of Q and K (Section 3.4, Appendix A.2)
     fast_exp: int = 0            # k of 8 key-pair classes use Schraudolph's exponential (forward only)
+    mixed: int = 0               # 1: scores from NVFP4 Q and K (Section 3.4 mixed path)
 
 
 def _params(ttot, ndocs, hq, hkv, d, opts: Opts) -> _Params:
     return _Params(ttot, ndocs, hq, hkv, d, opts.c_log2, opts.tau, opts.key_tile, opts.quant,
                    opts.rowsum, float(opts.softmax_scale), opts.unsafe_bound, float(opts.score_rel_err),
-                   opts.hadamard, opts.fast_exp)
+                   opts.hadamard, opts.fast_exp, opts.mixed)
 
 
 def max_threads() -> int:
@@ -154,6 +162,28 @@ def hadamard_f32(x_bits) -> np.ndarray:
     d = x.shape[-1]
     out = np.empty(x.shape, dtype=np.float32)
     _load().orc_hadamard_f32_array(_ptr(x), x.size // d, d, _ptr(out))
+    return out
+
+
+def e2m1_value(code) -> float:
+    return float(_load().orc_e2m1_value(int(code)))
+
+
+def e2m1_encode(y) -> int:
+    return int(_load().orc_e2m1_encode(float(y)))
+
+
+def nvfp4_scale(amax) -> int:
+    """E4M3 code of the NVFP4 scale of a 16-group with largest magnitude amax."""
+    return int(_load().orc_nvfp4_scale(float(amax)))
+
+
+def nvfp4_values(x_bits, hadamard: int = 0) -> np.ndarray:
+    """NVFP4 values (binary64) of bf16 rows [..., d] (the mixed path's Q and K)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    d = x.shape[-1]
+    out = np.empty(x.shape, dtype=np.float64)
+    _load().orc_nvfp4_rows(_ptr(x), x.size // d, d, int(hadamard), _ptr(out))
     return out
 
 

@@ -34,12 +34,17 @@
  *     butterfly in a fixed stage order (its values decide codes), and the
  *     gradients are rotated back in binary64;
  *   - the optional inference exponential (Schraudolph) is evaluated bit for
- *     bit on the fp32 argument, for the keys of k of every 8 key-pair classes.
+ *     bit on the fp32 argument, for the keys of k of every 8 key-pair classes;
+ *   - the mixed path's NVFP4 Q and K: one E4M3 scale per 16 channels of each
+ *     token, rounded up (the smallest with 6 s >= the group maximum), tensor
+ *     scale 1 (a constant: no statistic over the sequence), E2M1 codes to
+ *     nearest even; they serve the scores only.
  *
  * Parity: every exported function is pinned by CPU tests against definitions
  * that do not go through this file (a library FP8 codec, brute-force nearest
  * search, exact attention written as dense matrix algebra, finite differences,
- * and the causal and document-isolation invariants).
+ * closed forms of single-document calls, and the causal and
+ * document-isolation invariants).
  */
 #include <math.h>
 #include <stdint.h>
@@ -81,6 +86,11 @@ typedef struct {
      * whose pair class (bits 1, 3, 4 of the document-local key index) is
      * below k, i.e. k of every 8 key pairs.  Forward only. */
     int32_t fast_exp;
+    /* Mixed NVFP4/FP8 path (Section 3.4): 1 = the scores S = Q K^T (forward
+     * and backward) use NVFP4 Q and K (E2M1 codes, one E4M3 scale per 16
+     * channels of each token, tensor scale 1); dQ = dS K and dK = dS^T Q use
+     * the E4M3 token-block Q and K as in the MXFP8 path. */
+    int32_t mixed;
 } orc_params;
 
 /* ---------------------------------------------------------------------------
@@ -121,6 +131,58 @@ uint8_t orc_e4m3_encode(double y)
     if (n == 16.0) { n = 8.0; ef += 1; }
     if (ef > 8 || (ef == 8 && n > 14.0)) return (uint8_t)(sign | 0x7E);
     return (uint8_t)(sign | ((ef + 7) << 3) | ((int)n - 8));
+}
+
+/* E2M1 (OCP FP4, the 4-bit element of NVFP4, Section 2 "Microscaling
+ * floating-point formats"): 1 sign, 2 exponent bits, 1 mantissa bit; the
+ * magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+static const double e2m1_mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_value(uint8_t code)
+{
+    double v = e2m1_mag[code & 7];
+    return (code & 8) ? -v : v;
+}
+
+/* Round to the nearest E2M1 magnitude, ties to the even code (the one whose
+ * mantissa bit is 0); magnitudes above 6 saturate to 6. */
+uint8_t orc_e2m1_encode(double y)
+{
+    uint8_t sign = signbit(y) ? 8 : 0;
+    double a = fabs(y);
+    int best = 0;
+    for (int k = 1; k < 8; ++k) {
+        double dk = fabs(a - e2m1_mag[k]), db = fabs(a - e2m1_mag[best]);
+        if (dk < db || (dk == db && (k & 1) == 0)) best = k;
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* NVFP4 scale of a group of 16 whose largest magnitude is amax: the smallest
+ * E4M3 value s with 6 s >= amax (rounded up, like the MX exponents of
+ * Section 3.2, so that no element is clamped), 0 for an all-zero group; a
+ * group above 6 x 448 gets 448 and saturates.  Returns the E4M3 code. */
+uint8_t orc_nvfp4_scale(double amax)
+{
+    for (int c = 0; c <= 0x7E; ++c)
+        if (6.0 * orc_e4m3_value((uint8_t)c) >= amax) return (uint8_t)c;
+    return 0x7E;
+}
+
+/* NVFP4 values of one row of d channels (d a multiple of 16): groups of 16
+ * consecutive channels, one E4M3 scale each, tensor scale 1; each element
+ * becomes value(E2M1(x / s)) * s.  The row never shares a statistic with
+ * another token. */
+static void nvfp4_row(const double *x, int d, double *out)
+{
+    for (int g0 = 0; g0 < d; g0 += 16) {
+        double amax = 0.0, s;
+        for (int k = g0; k < g0 + 16; ++k)
+            if (fabs(x[k]) > amax) amax = fabs(x[k]);
+        s = orc_e4m3_value(orc_nvfp4_scale(amax));
+        for (int k = g0; k < g0 + 16; ++k)
+            out[k] = s == 0.0 ? 0.0 : orc_e2m1_value(orc_e2m1_encode(x[k] / s)) * s;
+    }
 }
 
 /* Shared block exponent for a block whose largest magnitude is amax.
@@ -226,7 +288,7 @@ static void hadamard_f64(double *y, int d)
  * Returns 0, or ORC_ERR_NOMEM.
  * ------------------------------------------------------------------------- */
 static int tbq_slice(const uint16_t *x, long rstride, int L, int d, int quant, int rot,
-                     double *deq, uint8_t *codes, long cstride, uint8_t *scales)
+                     double *deq, uint8_t *codes, long cstride, uint8_t *scales, double *nv)
 {
     double *xv = malloc(sizeof(double) * (size_t)L * d);
     float *row = malloc(sizeof(float) * (size_t)d);
@@ -239,6 +301,9 @@ static int tbq_slice(const uint16_t *x, long rstride, int L, int d, int quant, i
             for (int k = 0; k < d; ++k) xv[(long)t * d + k] = orc_bf16_to_double(x[(long)t * rstride + k]);
         }
     }
+    /* the NVFP4 values of the same (rotated) rows, for the mixed path */
+    if (nv)
+        for (int t = 0; t < L; ++t) nvfp4_row(xv + (long)t * d, d, nv + (long)t * d);
     for (int b0 = 0; b0 < L; b0 += 32) {
         int b1 = b0 + 32 < L ? b0 + 32 : L;
         double amax = 0.0;
@@ -295,7 +360,7 @@ int orc_quantize(const orc_params *p, int heads, const uint16_t *x, const int32_
         if (!deq) { err = ORC_ERR_NOMEM; continue; }
         if (tbq_slice(x + ((long)base * heads + h) * d, (long)heads * d, L, d, p->quant, p->hadamard != 0,
                       deq, codes + ((long)base * heads + h) * d, (long)heads * d,
-                      scales + (long)h * p->ttot + base) != ORC_OK)
+                      scales + (long)h * p->ttot + base, 0) != ORC_OK)
             err = ORC_ERR_NOMEM;
         free(deq);
     }
@@ -500,6 +565,10 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
     const double c1 = s * (1.0 / log(2.0));     /* s * log2(e) */
     const int need_bwd = dout != NULL;
     double *Kt = 0, *Vt = 0, *Qt = 0, *dOt = 0, *O = 0, *lse = 0, *Dv = 0;
+    /* mixed path: NVFP4 values of K and Q for the scores (Section 3.4) */
+    const int mixed = p->mixed != 0 && quant != QUANT_NONE;
+    double *Kn = 0, *Qn = 0;
+    const double *Ks, *Qs;
     double *acc = 0, *xbuf = 0, *dS = 0, *dQa = 0, *dKa = 0, *dVa = 0;
     float *lsef = 0;
     int64_t sat = 0, nds = 0, nds0 = 0;
@@ -513,6 +582,11 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
 
     if (L == 0) return;
     Kt = malloc(sizeof(double) * Ld);
+    if (mixed) {
+        Kn = malloc(sizeof(double) * Ld);
+        Qn = malloc(sizeof(double) * Ld);
+        if (!Kn || !Qn) { *err = ORC_ERR_NOMEM; goto done; }
+    }
     Vt = malloc(sizeof(double) * Ld);
     Qt = malloc(sizeof(double) * Ld);
     O = malloc(sizeof(double) * Ld);
@@ -555,21 +629,23 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
     /* K~ and V~: token blocks of this document and this key/value head. */
     /* K~ is quantized from the rotated rows when the Hadamard rotation is on
      * (Section 3.4); V~ never is. */
-    if (tbq_slice(k + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, p->hadamard != 0, Kt, 0, 0, 0) ||
-        tbq_slice(v + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, 0, Vt, 0, 0, 0)) {
+    if (tbq_slice(k + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, p->hadamard != 0, Kt, 0, 0, 0, Kn) ||
+        tbq_slice(v + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, 0, Vt, 0, 0, 0, 0)) {
         *err = ORC_ERR_NOMEM;
         goto done;
     }
 
+    Ks = mixed ? Kn : Kt;     /* score operands; the gradient products keep Kt and Qt */
+    Qs = mixed ? Qn : Qt;
     for (int hh = 0; hh < G; ++hh) {
         const int h = g * G + hh;
-        if (tbq_slice(q + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, p->hadamard != 0, Qt, 0, 0, 0)) {
+        if (tbq_slice(q + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, p->hadamard != 0, Qt, 0, 0, 0, Qn)) {
             *err = ORC_ERR_NOMEM;
             goto done;
         }
         /* ---- forward, row by row ---- */
         for (int i = 0; i < L; ++i) {
-            fwd_row(p, i, Qt + (long)i * d, Kt, Vt, c1, acc, xbuf, O + (long)i * d, &lse[i], &sat, rt);
+            fwd_row(p, i, Qs + (long)i * d, Ks, Vt, c1, acc, xbuf, O + (long)i * d, &lse[i], &sat, rt);
             lsef[i] = (float)lse[i];
             if (track) {
                 tlse[i] = rt->tol_lse;
@@ -593,7 +669,7 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         if (!need_bwd) continue;
 
         /* ---- backward (Section 2 equations; Section 3.3 consistency) ---- */
-        if (tbq_slice(dout + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, 0, dOt, 0, 0, 0)) {
+        if (tbq_slice(dout + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, 0, dOt, 0, 0, 0, 0)) {
             *err = ORC_ERR_NOMEM;
             goto done;
         }
@@ -608,11 +684,11 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
             /* dS for the 32 query rows of this block, every visible key. */
             for (int i = i0; i < i1; ++i) {
                 double li = (quant == QUANT_NONE) ? lse[i] : (double)lsef[i];
-                const double *qi = Qt + (long)i * d, *doi = dOt + (long)i * d;
+                const double *qi = Qs + (long)i * d, *doi = dOt + (long)i * d;
                 double *row = dS + (size_t)(i - i0) * L;
                 for (int j = 0; j < L; ++j) row[j] = 0.0;
                 for (int j = 0; j <= i; ++j) {
-                    double xij = dotd(qi, Kt + (long)j * d, d) * c1;
+                    double xij = dotd(qi, Ks + (long)j * d, d) * c1;
                     double P = exp2(xij - li), wb;
                     double dP = dotd(doi, Vt + (long)j * d, d);
                     if (quant == QUANT_NONE) {
@@ -621,7 +697,7 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                         /* Appendix B.1: the dV operand is E4M3(2^8 P), no scale. */
                         wb = ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(P, 8))), -8);
                         if (track && tdv) {   /* tolerance bookkeeping */
-                            double r = score_delta(p, qi, Kt + (long)j * d, d, c1, xij, li) + tlse[i];
+                            double r = score_delta(p, qi, Ks + (long)j * d, d, c1, xij, li) + tlse[i];
                             double sw = ldexp(code_swing(ldexp(P, 8), r, 0), -8);
                             if (sw > 0.0)
                                 for (int c = 0; c < d; ++c) tdv[(long)j * d + c] += sw * fabs(doi[c]);
@@ -630,7 +706,7 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                     for (int c = 0; c < d; ++c) dVa[(long)j * d + c] += wb * doi[c];
                     row[j] = P * (dP - Dv[i]);
                     if (dSd) {   /* tolerance bookkeeping: error band of dS */
-                        double dx = score_delta(p, qi, Kt + (long)j * d, d, c1, xij, li) + tlse[i];
+                        double dx = score_delta(p, qi, Ks + (long)j * d, d, c1, xij, li) + tlse[i];
                         double ddp = score_delta(p, doi, Vt + (long)j * d, d, 1.0, dP, 0.0);
                         double dD = 0x1p-20 * fabs(Dv[i]);
                         for (int c = 0; c < d; ++c) dD += fabs(doi[c]) * tOall[(long)i * d + c];
@@ -748,6 +824,7 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
     }
 done:
     free(Kt); free(Vt); free(Qt); free(O); free(lse); free(lsef); free(acc); free(xbuf);
+    free(Kn); free(Qn);
     free(dOt); free(Dv); free(dS); free(dQa); free(dKa); free(dVa);
     free(tacc); free(tdel); free(tolo); free(tlse); free(tdv);
     free(tOall); free(dSd); free(tdq); free(tdk);
@@ -815,6 +892,25 @@ int orc_attention(const orc_params *p, const uint16_t *q, const uint16_t *k, con
     }
     free(units);
     return err;
+}
+
+/* rows x d bf16 patterns -> their NVFP4 values (rot = 1: of the rotated rows) */
+void orc_nvfp4_rows(const uint16_t *x, long rows, int d, int rot, double *out)
+{
+    double *xv = malloc(sizeof(double) * (size_t)d);
+    float *row = malloc(sizeof(float) * (size_t)d);
+    if (!xv || !row) { free(xv); free(row); return; }
+    for (long r = 0; r < rows; ++r) {
+        if (rot) {
+            orc_hadamard_f32(x + r * d, d, row);
+            for (int k = 0; k < d; ++k) xv[k] = (double)row[k];
+        } else {
+            for (int k = 0; k < d; ++k) xv[k] = orc_bf16_to_double(x[r * d + k]);
+        }
+        nvfp4_row(xv, d, out + r * d);
+    }
+    free(xv);
+    free(row);
 }
 
 /* rows x d bf16 patterns -> rows x d fp32 rotated values */
