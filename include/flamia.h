@@ -1,7 +1,8 @@
 /*
- * flamia.h -- C ABI of an MI355X (gfx950) library for microscaled (MXFP8)
- * causal flash attention over packed variable-length documents: the
- * training call (forward and backward) with the operand quantization fused in.
+ * flamia.h -- C ABI of an MI355X (gfx950) library for microscaled (MXFP8, and
+ * mixed NVFP4/FP8) causal flash attention over packed variable-length
+ * documents: the training call (forward and backward) with the operand
+ * quantization fused in.
  *
  * Method: "FLAMIA: FLAsh MIcroscaling Attention for Fast and Causally Safe
  * Training on Blackwell".  Section numbers below refer to that paper.
@@ -25,6 +26,15 @@
  *    stores the block's exponent (Section 3.1 token-block scaling, Section
  *    3.6.1 dense per-token metadata).  The exponent is the smallest e with
  *    max|x| <= 448 * 2^e (Section 3.2), so no code saturates.
+ *    On the mixed NVFP4/FP8 path (opts.mixed = 1, Section 3.4) Q and K also
+ *    carry their NVFP4 form (Section 2, "Microscaling floating-point
+ *    formats"): per token, one E4M3 scale s per 16 consecutive channels, the
+ *    smallest E4M3 value with 6 s >= the group's largest magnitude (0 for an
+ *    all-zero group), tensor scale 1, and each element the nearest E2M1 value
+ *    of x / s (ties to the even code, saturating at 6).  The library stores
+ *    each element's value E2M1 x s, which is exact in bf16, as bf16
+ *    [T][heads][d] (`nv`); the score products read these, the gradient
+ *    products the E4M3 token-block codes.
  *  - lse2 is the saved row statistic, [hq][T] fp32, base 2, in the domain of
  *    the scaled scores x = (q.k) * softmax_scale * log2(e):
  *    lse2_i = log2(sum_j 2^(x_ij)).  Natural-log LSE = lse2 * ln 2.
@@ -49,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FLAMIA_ABI_VERSION 4
+#define FLAMIA_ABI_VERSION 5
 
 typedef enum {
     FLAMIA_OK = 0,
@@ -97,7 +107,14 @@ typedef struct {
                               of the 8 key-pair classes (class = bits 1, 3, 4 of the
                               document-local key index).  The forward's O and lse2 then come from
                               the approximate values; flamia_bwd returns FLAMIA_ERR_OPTS for a
-                              non-zero value (the backward rebuilds P with the exact exponential) */
+                              non-zero value (the backward rebuilds P with the exact exponential);
+                              it is offered on the MXFP8 path only (FLAMIA_ERR_OPTS with mixed) */
+    int32_t mixed;         /* 1: the mixed NVFP4/FP8 path (Section 3.4): the scores (forward and
+                              backward recomputation) come from the NVFP4 values of Q and K,
+                              which flamia_fwd writes to q_mx.nv and k_mx.nv and flamia_bwd
+                              reads from there (both must be non-NULL); every other product
+                              is unchanged.  flamia_bwd must be given the value flamia_fwd had.
+                              0 (default): the MXFP8 path */
     /* Optional phase timing: when phase_events is non-NULL it points to
      * n_events hipEvent_t handles (created by the caller); the call records
      * event i on `stream` before its i-th internal launch and the next one
@@ -113,6 +130,8 @@ typedef struct {
 typedef struct {
     uint8_t *codes;        /* [T][heads][d] E4M3 */
     uint8_t *scales;       /* [heads][T] UE8M0 */
+    uint16_t *nv;          /* [T][heads][d] bf16 NVFP4 values (mixed path, Q and K only);
+                              ignored (may be NULL) elsewhere */
 } flamia_mx_t;
 
 flamia_opts_t flamia_default_opts(void);
@@ -134,7 +153,9 @@ size_t flamia_workspace_bytes(const flamia_dims_t *dims, const flamia_opts_t *op
  * (Section 3.1, Section 3.2 rounded-up exponent, Section 3.6.1 document-local
  * blocks).
  *   x      : bf16 [ttot][heads][d] (input)
- *   out    : codes [ttot][heads][d] and scales [heads][ttot] (outputs)
+ *   out    : codes [ttot][heads][d] and scales [heads][ttot] (outputs); when
+ *            out.nv is non-NULL also the NVFP4 values of the same rows (the
+ *            mixed path's form, see the conventions above)
  * No workspace.  heads must be >= 1; only dims->ttot, ndocs and d are read.
  */
 flamia_status_t flamia_quantize(const flamia_dims_t *dims, int32_t heads, const uint16_t *x,
@@ -148,7 +169,8 @@ flamia_status_t flamia_quantize(const flamia_dims_t *dims, int32_t heads, const 
  *   q, k, v            : bf16 inputs
  *   q_mx, k_mx, v_mx   : outputs -- the quantized operands, which the caller
  *                        keeps for flamia_bwd (the backward rebuilds the scores
- *                        from exactly these codes, Section 3.3)
+ *                        from exactly these codes, Section 3.3); with
+ *                        opts.mixed = 1 also q_mx.nv and k_mx.nv
  *   o                  : bf16 output [ttot][hq][d]
  *   lse2               : fp32 output [hq][ttot]
  *   ws / ws_bytes      : workspace of at least flamia_workspace_bytes()

@@ -51,6 +51,8 @@ flamia_status_t check_opts(const flamia_opts_t* o) {
     if (o->rowsum != 0 && o->rowsum != 1) return FLAMIA_ERR_OPTS;
     if (o->hadamard != 0 && o->hadamard != 1) return FLAMIA_ERR_OPTS;
     if (o->fast_exp != 0 && o->fast_exp != 5 && o->fast_exp != 8) return FLAMIA_ERR_OPTS;
+    if (o->mixed != 0 && o->mixed != 1) return FLAMIA_ERR_OPTS;
+    if (o->mixed && o->fast_exp) return FLAMIA_ERR_OPTS;   // the inference exponential is MXFP8-only
     if (!(o->softmax_scale <= 0.f || isfinite(o->softmax_scale))) return FLAMIA_ERR_OPTS;
     if (o->n_events < 0 || (o->n_events > 0 && !o->phase_events)) return FLAMIA_ERR_OPTS;
     return FLAMIA_OK;
@@ -114,6 +116,14 @@ float scale_of(const flamia_opts_t& o, int d) {
 
 bool mx_ok(flamia_mx_t m) { return m.codes && m.scales && aligned16(m.codes); }
 
+// Mixed path: Q and K must carry their NVFP4 values.
+flamia_status_t check_nv(const flamia_opts_t& o, flamia_mx_t q, flamia_mx_t k) {
+    if (!o.mixed) return FLAMIA_OK;
+    if (!q.nv || !k.nv) return FLAMIA_ERR_NULL;
+    if (!aligned16(q.nv) || !aligned16(k.nv)) return FLAMIA_ERR_ALIGN;
+    return FLAMIA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,6 +137,7 @@ flamia_opts_t flamia_default_opts(void) {
     o.softmax_scale = 0.f;
     o.hadamard = 0;
     o.fast_exp = 0;
+    o.mixed = 0;
     o.phase_events = nullptr;
     o.n_events = 0;
     return o;
@@ -161,10 +172,10 @@ flamia_status_t flamia_quantize(const flamia_dims_t* dims, int32_t heads, const 
     if (s != FLAMIA_OK) return s;
     if (heads <= 0) return FLAMIA_ERR_SHAPE;
     if (!x || !cu_seqlens || !out.codes || !out.scales) return FLAMIA_ERR_NULL;
-    if (!aligned16(x) || !aligned16(out.codes)) return FLAMIA_ERR_ALIGN;
+    if (!aligned16(x) || !aligned16(out.codes) || !aligned16(out.nv)) return FLAMIA_ERR_ALIGN;
     QuantArgs a{};
     a.cu = cu_seqlens; a.ndocs = dims->ndocs; a.ttot = dims->ttot; a.d = dims->d;
-    a.t[0] = QuantTensor{x, out.codes, out.scales, heads, 0};
+    a.t[0] = QuantTensor{x, out.codes, out.scales, heads, 0, out.nv};
     a.ntensors = 1;
     hipError_t e = launch_quantize(a, (hipStream_t)stream);
     return e == hipSuccess ? FLAMIA_OK : hip_fail(e);
@@ -185,6 +196,7 @@ flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !mx_ok(q_mx) ||
         !mx_ok(k_mx) || !mx_ok(v_mx))
         return FLAMIA_ERR_ALIGN;
+    if ((s = check_nv(opts, q_mx, k_mx)) != FLAMIA_OK) return s;
     const Layout w = layout(dims);
     if (!ws || ws_bytes < w.total) return FLAMIA_ERR_WORKSPACE;
     if (!aligned16(ws)) return FLAMIA_ERR_ALIGN;
@@ -197,10 +209,13 @@ flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     QuantArgs qa{};
     qa.cu = cu_seqlens; qa.ndocs = dims->ndocs; qa.ttot = dims->ttot; qa.d = d;
     // with the Hadamard option Q and K are quantized from their rotated rows
-    // (Section 3.4: the rotation is fused into the quantizer), V never is
-    qa.t[0] = QuantTensor{q, q_mx.codes, q_mx.scales, dims->hq, opts.hadamard};
-    qa.t[1] = QuantTensor{k, k_mx.codes, k_mx.scales, dims->hkv, opts.hadamard};
-    qa.t[2] = QuantTensor{v, v_mx.codes, v_mx.scales, dims->hkv, 0};
+    // (Section 3.4: the rotation is fused into the quantizer), V never is;
+    // on the mixed path Q and K also get their NVFP4 values
+    uint16_t* qn = opts.mixed ? q_mx.nv : nullptr;
+    uint16_t* kn = opts.mixed ? k_mx.nv : nullptr;
+    qa.t[0] = QuantTensor{q, q_mx.codes, q_mx.scales, dims->hq, opts.hadamard, qn};
+    qa.t[1] = QuantTensor{k, k_mx.codes, k_mx.scales, dims->hkv, opts.hadamard, kn};
+    qa.t[2] = QuantTensor{v, v_mx.codes, v_mx.scales, dims->hkv, 0, nullptr};
     qa.ntensors = 3;
     PhaseMarks pm{opts, st};
     hipError_t e;
@@ -222,6 +237,7 @@ flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     fa.tau = (float)opts.tau;
     fa.rowsum = opts.rowsum;
     fa.fast_exp = opts.fast_exp;
+    fa.qn = qn; fa.kn = kn;
     if ((e = pm.mark()) != hipSuccess || (e = launch_fwd(fa, d, w.max_tiles * dims->hq, st)) != hipSuccess)
         return hip_fail(e);
     e = pm.mark();
@@ -245,6 +261,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     if (!aligned16(d_o) || !aligned16(o) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
         !mx_ok(q_mx) || !mx_ok(k_mx) || !mx_ok(v_mx))
         return FLAMIA_ERR_ALIGN;
+    if ((s = check_nv(opts, q_mx, k_mx)) != FLAMIA_OK) return s;
     const Layout w = layout(dims);
     if (!ws || ws_bytes < w.total) return FLAMIA_ERR_WORKSPACE;
     if (!aligned16(ws)) return FLAMIA_ERR_ALIGN;
@@ -259,7 +276,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     // dO launch: codes + scales and D = dO~ . O (Section 3.5.1)
     QuantArgs qa{};
     qa.cu = cu_seqlens; qa.ndocs = dims->ndocs; qa.ttot = dims->ttot; qa.d = d;
-    qa.t[0] = QuantTensor{d_o, oc, os, dims->hq, 0};
+    qa.t[0] = QuantTensor{d_o, oc, os, dims->hq, 0, nullptr};
     qa.ntensors = 1;
     qa.o = o; qa.dvec = dvec;
     PhaseMarks pm{opts, st};
@@ -287,6 +304,8 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     ba.scale = scale;
     ba.c1 = scale * 1.4426950408889634f;
     ba.hadamard = opts.hadamard;
+    ba.qn = opts.mixed ? q_mx.nv : nullptr;
+    ba.kn = opts.mixed ? k_mx.nv : nullptr;
     ba.ds_codes = ds_codes; ba.ds_scales = ds_scales; ba.dboff = dboff; ba.ds_blocks = w.ds_blocks;
     if ((e = pm.mark()) != hipSuccess || (e = launch_bwd(ba, d, w.max_tiles * dims->hkv, st)) != hipSuccess)
         return hip_fail(e);
@@ -302,6 +321,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     qd.scale = scale;
     qd.c1 = ba.c1;
     qd.hadamard = opts.hadamard;
+    qd.qn = ba.qn; qd.kn = ba.kn;
     qd.ds_codes = ds_codes; qd.ds_scales = ds_scales; qd.dboff = dboff; qd.ds_blocks = w.ds_blocks;
     // dQ: from the stored blocks when the call fits the store (decided on the
     // device; the other kernel returns at once), else by rebuilding dS-hat

@@ -22,6 +22,10 @@
 // dK and dV accumulate in registers across the query heads of the group
 // (GQA sum in fp32) and are written once.  dQ is the query-major pass
 // (dq.hip), which rebuilds the same dS-hat bit for bit.
+// Mixed NVFP4/FP8 path (Section 3.4): S is rebuilt from the NVFP4 values of Q
+// and K (bf16, D/16 bf16 MFMAs per 32x32 tile, the forward's instruction with
+// the roles swapped, which gives the same bits); dK still contracts over the
+// E4M3 token-block Q^, so a step stages both forms of its query rows.
 #include <type_traits>
 
 #include "device.h"
@@ -31,33 +35,38 @@ namespace flamia {
 
 constexpr int kQStep = 64;
 
-template <int D>
+template <int D, int MIX>
 struct BwdStep {
     static constexpr int kStride = D + 16;       // row pitch of code tiles
+    static constexpr int kNStride = 2 * D + 16;  // row pitch of the bf16 NVFP4 rows (mixed path)
     uint8_t q[kQStep * kStride];
     uint8_t o[kQStep * kStride];                 // quantized dO
     alignas(16) float lse[kQStep];
     alignas(16) float dv[kQStep];                // -D
     uint8_t eq[kQStep];
     uint8_t eo[kQStep];
+    alignas(16) uint8_t qn[MIX ? kQStep * kNStride : 16];   // NVFP4 values of Q (mixed path)
 };
 
-// Step buffers: with the software pipeline (d = 64) the products of step i
-// read buffer i % 2 while the dV/dK products of step i - 1 still read the
-// other one.
-template <int D>
+// Step buffers: with the software pipeline (d = 64, MXFP8) the products of
+// step i read buffer i % 2 while the dV/dK products of step i - 1 still read
+// the other one.
+template <int D, int MIX>
 struct BwdSmem {
-    static constexpr int kStride = BwdStep<D>::kStride;
-    BwdStep<D> buf[D == 64 ? 2 : 1];
+    static constexpr int kStride = BwdStep<D, MIX>::kStride;
+    BwdStep<D, MIX> buf[D == 64 && !MIX ? 2 : 1];
 };
 
-template <int D, bool STORE>
+template <int D, bool STORE, int MIX>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs a) {
     constexpr int KC = D / 64;
+    constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;
-    constexpr int STR = BwdSmem<D>::kStride;
+    constexpr int STR = BwdSmem<D, MIX>::kStride;
+    constexpr int NSTR = BwdStep<D, MIX>::kNStride;
     constexpr int NQ = kQStep * D / 16 / 256;     // 16-byte chunks per thread of a 64-row code tile
-    __shared__ BwdSmem<D> sm;
+    constexpr int NQN = MIX ? 2 * NQ : 1;         // same for the bf16 NVFP4 rows
+    __shared__ BwdSmem<D, MIX> sm;
 
     const int ti = (int)blockIdx.x / a.hkv;
     if (ti >= *a.ntiles) return;
@@ -78,7 +87,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     const int key_row = ds + min(key_loc, L - 1);
 
     // ---- staging of one 64-query step (prefetched into registers one step ahead)
-    u32x4 pq[NQ], po[NQ];
+    u32x4 pq[NQ], po[NQ], pqn[NQN];
     uint32_t p_eq = 0, p_eo = 0;
     float p_lse = 0.f, p_dv = 0.f;
     bool p_in = true;
@@ -90,6 +99,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             const long qr = ds + min(q0 + row, L - 1);
             pq[r] = *reinterpret_cast<const u32x4*>(a.qc + (qr * a.hq + h) * D + col);
             po[r] = *reinterpret_cast<const u32x4*>(a.oc + (qr * a.hq + h) * D + col);
+        }
+        if constexpr (MIX) {
+#pragma unroll
+            for (int r = 0; r < NQN; ++r) {
+                const int c = tid + 256 * r;
+                const int row = c / (D / 8), col = (c % (D / 8)) * 8;   // col in bf16 elements
+                const long qr = ds + min(q0 + row, L - 1);
+                pqn[r] = *reinterpret_cast<const u32x4*>(a.qn + (qr * a.hq + h) * D + col);
+            }
         }
         // Every thread issues the same loads (rows clamped into the document),
         // so the number of outstanding memory operations is static.
@@ -103,13 +121,21 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             p_dv = a.dvec[(long)h * a.ttot + qr];
         }
     };
-    auto store_step = [&](BwdStep<D>& b) {
+    auto store_step = [&](BwdStep<D, MIX>& b) {
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
             const int c = tid + 256 * r;
             const int row = c / (D / 16), col = (c % (D / 16)) * 16;
             *reinterpret_cast<u32x4*>(&b.q[row * STR + col]) = pq[r];
             *reinterpret_cast<u32x4*>(&b.o[row * STR + col]) = po[r];
+        }
+        if constexpr (MIX) {
+#pragma unroll
+            for (int r = 0; r < NQN; ++r) {
+                const int c = tid + 256 * r;
+                const int row = c / (D / 8), col = (c % (D / 8)) * 16;   // col in bytes
+                *reinterpret_cast<u32x4*>(&b.qn[row * NSTR + col]) = pqn[r];
+            }
         }
         if (tid < kQStep) {
             b.eq[tid] = (uint8_t)p_eq;
@@ -120,22 +146,32 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     };
     load_step(g * G, kt0);
 
-    // The wave's key rows as B operands of S and dP (column = key, k = channel).
-    v8i kb[KC], vb[KC];
+    // The wave's key rows as B operands of S and dP (column = key, k = channel);
+    // mixed path: channels 16 kc + 8 lg .. + 8 of the key's NVFP4 values for S
+    v8i kb[MIX ? 1 : KC], vb[KC];
+    u32x4 kn[MIX ? NC : 1];
     {
         const uint8_t* kp = a.kc + ((long)key_row * a.hkv + g) * D;
         const uint8_t* vp = a.vc + ((long)key_row * a.hkv + g) * D;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            uint4 lo = *reinterpret_cast<const uint4*>(kp + 64 * kc + 16 * lg);
-            uint4 hi = *reinterpret_cast<const uint4*>(kp + 64 * kc + 32 + 16 * lg);
-            kb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            uint4 lo, hi;
+            if constexpr (!MIX) {
+                lo = *reinterpret_cast<const uint4*>(kp + 64 * kc + 16 * lg);
+                hi = *reinterpret_cast<const uint4*>(kp + 64 * kc + 32 + 16 * lg);
+                kb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
             lo = *reinterpret_cast<const uint4*>(vp + 64 * kc + 16 * lg);
             hi = *reinterpret_cast<const uint4*>(vp + 64 * kc + 32 + 16 * lg);
             vb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
+        if constexpr (MIX) {
+            const uint16_t* np = a.kn + ((long)key_row * a.hkv + g) * D;
+#pragma unroll
+            for (int kc = 0; kc < NC; ++kc) kn[kc] = *reinterpret_cast<const u32x4*>(np + 16 * kc + 8 * lg);
+        }
     }
-    const int ek = a.ks[(long)g * a.ttot + key_row];
+    const int ek = MIX ? 127 : a.ks[(long)g * a.ttot + key_row];
     const int ev = a.vs[(long)g * a.ttot + key_row];
 
     v16f dvt[DT], dkt[DT];
@@ -149,7 +185,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
 
     // dV^T += dO^T P-hat_b and dK^T += Q^T dS-hat of one step (contraction
     // over its 64 queries), from its codes and its step buffer
-    auto dvdk = [&](const BwdStep<D>& b, const int (&pbc)[2][4], const int (&dsc)[2][4], const int (&es)[2]) {
+    auto dvdk = [&](const BwdStep<D, MIX>& b, const int (&pbc)[2][4], const int (&dsc)[2][4], const int (&es)[2]) {
         const v8i pb = v8i{pbc[0][0], pbc[0][1], pbc[0][2], pbc[0][3], pbc[1][0], pbc[1][1], pbc[1][2], pbc[1][3]};
         const v8i db = v8i{dsc[0][0], dsc[0][1], dsc[0][2], dsc[0][3], dsc[1][0], dsc[1][1], dsc[1][2], dsc[1][3]};
         const int so = b.eo[32 * lg], sq = b.eq[32 * lg];
@@ -174,7 +210,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     // the matrix cores while the wave computes the next softmax.  At d = 128
     // the extra live codes cost an occupancy step, and with the store they
     // spill, so the products follow their own step there.
-    constexpr bool PIPE = D == 64 && !STORE;
+    // The mixed path's bf16 operands take the registers the pipeline needs.
+    constexpr bool PIPE = D == 64 && !STORE && !MIX;
     int cur = 0;                           // step buffer of the current step
     bool dvdk_due = false;                 // the previous step's dV/dK products are pending
     int ppbc[2][4], pdsc[2][4], pes[2];
@@ -201,7 +238,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     auto step = [&](auto mask_tag) -> bool {
         constexpr bool MASK = decltype(mask_tag)::value;
         // ---- publish the prefetched step in LDS, start fetching the next one
-        BwdStep<D>& B = sm.buf[cur];
+        BwdStep<D, MIX>& B = sm.buf[cur];
         __syncthreads();                   // buffer cur: its last readers were two steps ago
         store_step(B);
         __syncthreads();
@@ -242,12 +279,20 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             }
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                uint4 lo = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 16 * lg]);
-                uint4 hi = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 32 + 16 * lg]);
-                const v8i qa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                sacc[st] = mfma_mx(qa, kb[kc], sacc[st], B.eq[row], ek);
-                lo = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 16 * lg]);
-                hi = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 32 + 16 * lg]);
+                if constexpr (MIX) {
+#pragma unroll
+                    for (int n = 4 * kc; n < 4 * kc + 4; ++n) {
+                        const u32x4 qa = *reinterpret_cast<const u32x4*>(&B.qn[row * NSTR + 32 * n + 16 * lg]);
+                        sacc[st] = mfma_bf16(qa, kn[n], sacc[st]);
+                    }
+                } else {
+                    const uint4 lo = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 16 * lg]);
+                    const uint4 hi = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 32 + 16 * lg]);
+                    const v8i qa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    sacc[st] = mfma_mx(qa, kb[kc], sacc[st], B.eq[row], ek);
+                }
+                const uint4 lo = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 16 * lg]);
+                const uint4 hi = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 32 + 16 * lg]);
                 const v8i oa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 pacc[st] = mfma_mx(oa, vb[kc], pacc[st], B.eo[row], ev);
             }
@@ -374,16 +419,23 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     }
 }
 
+template <int D, bool STORE>
+static void launch_bwd_mix(const BwdArgs& a, dim3 g, hipStream_t st) {
+    if (a.qn) hipLaunchKernelGGL((bwd_kernel<D, STORE, 1>), g, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((bwd_kernel<D, STORE, 0>), g, dim3(256), 0, st, a);
+}
+
 hipError_t launch_bwd(const BwdArgs& a, int d, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
     // the store variant only where the workspace has a dS store
     const bool store = a.ds_blocks > 0;
+    const dim3 g((unsigned)grid);
     if (d == 64) {
-        if (store) hipLaunchKernelGGL((bwd_kernel<64, true>), dim3((unsigned)grid), dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((bwd_kernel<64, false>), dim3((unsigned)grid), dim3(256), 0, st, a);
+        if (store) launch_bwd_mix<64, true>(a, g, st);
+        else launch_bwd_mix<64, false>(a, g, st);
     } else {
-        if (store) hipLaunchKernelGGL((bwd_kernel<128, true>), dim3((unsigned)grid), dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((bwd_kernel<128, false>), dim3((unsigned)grid), dim3(256), 0, st, a);
+        if (store) launch_bwd_mix<128, true>(a, g, st);
+        else launch_bwd_mix<128, false>(a, g, st);
     }
     return hipGetLastError();
 }

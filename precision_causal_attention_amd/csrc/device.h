@@ -27,6 +27,21 @@ __device__ __forceinline__ v16f mfma_mx(v8i a, v8i b, v16f c, int scale_a, int s
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
 }
 
+// bf16 MFMA 32x32x16 -> fp32 (the score product of the mixed NVFP4 path,
+// whose values are exact in bf16).  Lane l carries row (A) / column (B)
+// l % 32 and eight contraction elements; A and B use the same (lane / 32,
+// element) -> k assignment (measured on gfx950), so any channel order that
+// both operands share gives the dot product.  Swapping the A and B roles
+// gives bitwise the transposed result (measured).  Accumulator layout as
+// mfma_mx.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v16f mfma_bf16(u32x4 a, u32x4 b, v16f c) {
+    bf16x8_t x, y;
+    __builtin_memcpy(&x, &a, 16);
+    __builtin_memcpy(&y, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+}
+
 // Transposed LDS read of 8-bit elements (ds_read_b64_tr_b8).  Within each
 // group of 16 lanes, lane s supplies the address of an 8-byte row R_s; lane j
 // receives byte i = R_{2i + (j%16)/8}[j % 8] for i = 0..7.

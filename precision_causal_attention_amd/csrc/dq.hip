@@ -18,6 +18,9 @@
 // the key-major pass (role-swapped MFMA operands give identical bits), so
 // dS-hat here is bitwise the payload the key-major pass feeds to dK.  dQ is
 // owned by one workgroup: no atomics, deterministic, written once as bf16.
+// Mixed NVFP4/FP8 path (Section 3.4): S^T comes from the NVFP4 values of K
+// and Q (bf16 MFMAs, as in the forward), while dQ still contracts over the
+// E4M3 token-block K^, so a key tile stages both forms of its rows.
 #include <type_traits>
 
 #include "device.h"
@@ -25,22 +28,27 @@
 
 namespace flamia {
 
-template <int D>
+template <int D, int MIX>
 struct DqSmem {
     static constexpr int kStride = D + 16;
+    static constexpr int kNStride = 2 * D + 16;   // bf16 NVFP4 rows of K (mixed path)
     uint8_t k[kTile * kStride];
     uint8_t v[kTile * kStride];
     uint8_t ek[kTile];
     uint8_t ev[kTile];
+    alignas(16) uint8_t kn[MIX ? kTile * kNStride : 16];
 };
 
-template <int D>
+template <int D, int MIX>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a) {
     constexpr int KC = D / 64;
+    constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;
-    constexpr int STR = DqSmem<D>::kStride;
+    constexpr int STR = DqSmem<D, MIX>::kStride;
+    constexpr int NSTR = DqSmem<D, MIX>::kNStride;
     constexpr int CHUNKS = kTile * D / 16;
-    __shared__ DqSmem<D> sm;
+    constexpr int NCH = MIX ? 2 * CHUNKS / 256 : 1;   // 16-byte chunks per thread of a bf16 K tile
+    __shared__ DqSmem<D, MIX> sm;
 
     if (a.ntiles[1] != 0) return;                    // the dS store is in use: dq_store.hip runs
     const int ti = (int)blockIdx.x / a.hq;
@@ -59,22 +67,32 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
     const bool q_valid = q_loc < L;
     const int q_row = ds + min(q_loc, L - 1);
 
-    // query rows of Q^ and dO^ as B operands (column = query, k = channel)
-    v8i qb[KC], ob[KC];
+    // query rows of Q^ and dO^ as B operands (column = query, k = channel);
+    // mixed path: channels 16 kc + 8 lg .. + 8 of the query's NVFP4 values for S
+    v8i qb[MIX ? 1 : KC], ob[KC];
+    u32x4 qn[MIX ? NC : 1];
     {
         const uint8_t* qp = a.qc + ((long)q_row * a.hq + h) * D;
         const uint8_t* op = a.oc + ((long)q_row * a.hq + h) * D;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * kc + 16 * lg);
-            uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * kc + 32 + 16 * lg);
-            qb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            uint4 lo, hi;
+            if constexpr (!MIX) {
+                lo = *reinterpret_cast<const uint4*>(qp + 64 * kc + 16 * lg);
+                hi = *reinterpret_cast<const uint4*>(qp + 64 * kc + 32 + 16 * lg);
+                qb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
             lo = *reinterpret_cast<const uint4*>(op + 64 * kc + 16 * lg);
             hi = *reinterpret_cast<const uint4*>(op + 64 * kc + 32 + 16 * lg);
             ob[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
+        if constexpr (MIX) {
+            const uint16_t* np = a.qn + ((long)q_row * a.hq + h) * D;
+#pragma unroll
+            for (int kc = 0; kc < NC; ++kc) qn[kc] = *reinterpret_cast<const u32x4*>(np + 16 * kc + 8 * lg);
+        }
     }
-    const int eq = a.qs[(long)h * a.ttot + q_row];
+    const int eq = MIX ? 127 : a.qs[(long)h * a.ttot + q_row];
     const int eo = a.os[(long)h * a.ttot + q_row];
     const float lse_raw = a.lse2[(long)h * a.ttot + q_row];
     const float lse = q_valid ? lse_raw : INFINITY;      // P = 0 on rows outside the document
@@ -94,9 +112,21 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
     const int tr_key = 8 * ((s16 >> 1) >> 2) + 4 * lg + ((s16 >> 1) & 3);
     const int tr_col = 16 * grp + 8 * (s16 & 1);
 
-    u32x4 kr[CHUNKS / 256], vr[CHUNKS / 256];
+    u32x4 kr[CHUNKS / 256], vr[CHUNKS / 256], knr[NCH];
     uint32_t ekr, evr;
-    fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds, a.ttot, a.hkv, g, tid);
+    auto fetch = [&](const int k0) {
+        fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, k0, a.ttot, a.hkv, g, tid);
+        if constexpr (MIX) {
+#pragma unroll
+            for (int r = 0; r < NCH; ++r) {
+                const int c = tid + 256 * r;
+                const int row = c / (D / 8), col = (c % (D / 8)) * 8;   // col in bf16 elements
+                const long krow = min(k0 + row, a.ttot - 1);
+                knr[r] = *reinterpret_cast<const u32x4*>(a.kn + (krow * a.hkv + g) * D + col);
+            }
+        }
+    };
+    fetch(ds);
 
     // One 128-key tile; DIAG marks the last (diagonal) tile, the only one that
     // needs the causal mask and the only one with nothing left to prefetch.
@@ -110,13 +140,20 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
             *reinterpret_cast<u32x4*>(&sm.k[row * STR + col]) = kr[r];
             *reinterpret_cast<u32x4*>(&sm.v[row * STR + col]) = vr[r];
         }
+        if constexpr (MIX) {
+#pragma unroll
+            for (int r = 0; r < NCH; ++r) {
+                const int c = tid + 256 * r;
+                const int row = c / (D / 8), col = (c % (D / 8)) * 16;   // col in bytes
+                *reinterpret_cast<u32x4*>(&sm.kn[row * NSTR + col]) = knr[r];
+            }
+        }
         if (tid < kTile) {
             sm.ek[tid] = (uint8_t)ekr;
             sm.ev[tid] = (uint8_t)evr;
         }
         __syncthreads();
-        if constexpr (!DIAG)
-            fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds + kTile * (t + 1), a.ttot, a.hkv, g, tid);
+        if constexpr (!DIAG) fetch(ds + kTile * (t + 1));
 
         // accumulator register i of sub-tile kk holds key 128t + 32kk + 8(i/4)
         // + 4lg + i%4; on the diagonal tile it is masked past the lane's query
@@ -131,12 +168,20 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
             dpb = negD;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                uint4 lo = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 16 * lg]);
-                uint4 hi = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 32 + 16 * lg]);
-                const v8i ka = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                sb = mfma_mx(ka, qb[kc], sb, sm.ek[row], eq);
-                lo = *reinterpret_cast<const uint4*>(&sm.v[row * STR + 64 * kc + 16 * lg]);
-                hi = *reinterpret_cast<const uint4*>(&sm.v[row * STR + 64 * kc + 32 + 16 * lg]);
+                if constexpr (MIX) {
+#pragma unroll
+                    for (int n = 4 * kc; n < 4 * kc + 4; ++n) {
+                        const u32x4 ka = *reinterpret_cast<const u32x4*>(&sm.kn[row * NSTR + 32 * n + 16 * lg]);
+                        sb = mfma_bf16(ka, qn[n], sb);
+                    }
+                } else {
+                    const uint4 lo = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 16 * lg]);
+                    const uint4 hi = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 32 + 16 * lg]);
+                    const v8i ka = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    sb = mfma_mx(ka, qb[kc], sb, sm.ek[row], eq);
+                }
+                const uint4 lo = *reinterpret_cast<const uint4*>(&sm.v[row * STR + 64 * kc + 16 * lg]);
+                const uint4 hi = *reinterpret_cast<const uint4*>(&sm.v[row * STR + 64 * kc + 32 + 16 * lg]);
                 const v8i va = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 dpb = mfma_mx(va, ob[kc], dpb, sm.ev[row], eo);
             }
@@ -236,8 +281,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
 
 hipError_t launch_dq(const DqArgs& a, int d, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
-    if (d == 64) hipLaunchKernelGGL(dq_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(dq_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, a);
+    const dim3 g((unsigned)grid), b(256);
+    if (d == 64) {
+        if (a.qn) hipLaunchKernelGGL((dq_kernel<64, 1>), g, b, 0, st, a);
+        else hipLaunchKernelGGL((dq_kernel<64, 0>), g, b, 0, st, a);
+    } else {
+        if (a.qn) hipLaunchKernelGGL((dq_kernel<128, 1>), g, b, 0, st, a);
+        else hipLaunchKernelGGL((dq_kernel<128, 0>), g, b, 0, st, a);
+    }
     return hipGetLastError();
 }
 

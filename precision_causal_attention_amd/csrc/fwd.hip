@@ -18,6 +18,12 @@
 //                                 layout), scale of each 32-key block of V.
 // The accumulator layout puts one query per lane column, so the online-softmax
 // statistics are per-lane scalars (plus one exchange between lane halves).
+// Mixed NVFP4/FP8 path (Section 3.4): S^T comes from the NVFP4 values of K and
+// Q instead, expanded to bf16 by the quantizer (an E2M1 element times an E4M3
+// scale has at most 6 significant bits, so bf16 holds it exactly; the
+// block-scaled MFMA cannot apply one E4M3 scale per 16 channels): D/16 bf16
+// MFMAs 32x32x16 per sub-tile, no scale operands; everything after S is the
+// same.
 #include <type_traits>
 
 #include "device.h"
@@ -25,10 +31,11 @@
 
 namespace flamia {
 
-template <int D>
+template <int D, int MIX>
 struct FwdSmem {
     static constexpr int kStride = D + 16;        // row pitch of a code tile in LDS (bank spread)
-    uint8_t k[kTile * kStride];
+    static constexpr int kKStride = MIX ? 2 * D + 16 : kStride;   // K: bf16 NVFP4 values when mixed
+    uint8_t k[kTile * kKStride];
     uint8_t v[kTile * kStride];
     uint8_t ek[kTile];
     uint8_t ev[kTile];
@@ -50,13 +57,17 @@ __device__ __forceinline__ constexpr int pair_class(int i) {
     return ((i >> 1) & 1) | (((i >> 2) & 1) << 1) | (((i >> 3) & 1) << 2);
 }
 
-template <int D, int ROWSUM, int FAST>
+template <int D, int ROWSUM, int FAST, int MIX>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs a) {
     constexpr int KC = D / 64;                    // 64-channel contraction steps of S
+    constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;                    // 32-row channel tiles of O^T
-    constexpr int STR = FwdSmem<D>::kStride;
+    constexpr int STR = FwdSmem<D, MIX>::kStride;
+    constexpr int KSTR = FwdSmem<D, MIX>::kKStride;
     constexpr int CHUNKS = kTile * D / 16;        // 16-byte chunks of one code tile
-    __shared__ FwdSmem<D> sm;
+    constexpr int KCHUNKS = MIX ? 2 * CHUNKS : CHUNKS;   // 16-byte chunks of one K tile
+    constexpr int KRB = MIX ? 2 * D / 16 : D / 16;       // 16-byte chunks of one K row
+    __shared__ FwdSmem<D, MIX> sm;
 
     const int ti = (int)blockIdx.x / a.hq;
     if (ti >= *a.ntiles) return;
@@ -76,8 +87,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
 
     // The wave's 32 query rows as the B operand (column = query, k = channel):
     // bytes 0..15 = channels 64kc + 16lg .. +16, bytes 16..31 = 64kc + 32 + 16lg .. +16.
-    v8i qb[KC];
-    {
+    v8i qb[MIX ? 1 : KC];
+    // mixed path: channels 16 kc + 8 lg .. + 8 of the query's NVFP4 values
+    // (the K rows use the same assignment)
+    u32x4 qn[MIX ? NC : 1];
+    if constexpr (MIX) {
+        const uint16_t* qp = a.qn + ((long)q_row * a.hq + h) * D;
+#pragma unroll
+        for (int kc = 0; kc < NC; ++kc) qn[kc] = *reinterpret_cast<const u32x4*>(qp + 16 * kc + 8 * lg);
+    } else {
         const uint8_t* qp = a.qc + ((long)q_row * a.hq + h) * D;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
@@ -86,7 +104,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
             qb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
     }
-    const int eq = a.qs[(long)h * a.ttot + q_row];
+    const int eq = MIX ? 127 : a.qs[(long)h * a.ttot + q_row];
 
     v16f acc[DT];
 #pragma unroll
@@ -100,10 +118,33 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
     const int tr_key = 8 * ((s16 >> 1) >> 2) + 4 * lg + ((s16 >> 1) & 3);
     const int tr_col = 16 * grp + 8 * (s16 & 1);
 
-    // ---- K^/V^ code tiles and scales, prefetched into registers one tile ahead
-    u32x4 kr[CHUNKS / 256], vr[CHUNKS / 256];
+    // ---- K^/V^ code tiles and scales (mixed: K's NVFP4 values), prefetched
+    // into registers one tile ahead
+    u32x4 kr[KCHUNKS / 256], vr[CHUNKS / 256];
     uint32_t ekr, evr;
-    fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds, a.ttot, a.hkv, g, tid);
+    auto fetch = [&](const int k0) {
+        if constexpr (MIX) {
+#pragma unroll
+            for (int r = 0; r < CHUNKS / 256; ++r) {
+                const int c = tid + 256 * r;
+                const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+                const long krow = min(k0 + row, a.ttot - 1);
+                vr[r] = *reinterpret_cast<const u32x4*>(a.vc + (krow * a.hkv + g) * D + col);
+            }
+            ekr = 127;
+            evr = a.vs[(long)g * a.ttot + min(k0 + (tid & 127), a.ttot - 1)];
+#pragma unroll
+            for (int r = 0; r < KCHUNKS / 256; ++r) {
+                const int c = tid + 256 * r;
+                const int row = c / KRB, col = (c % KRB) * 8;      // col in bf16 elements
+                const long krow = min(k0 + row, a.ttot - 1);
+                kr[r] = *reinterpret_cast<const u32x4*>(a.kn + (krow * a.hkv + g) * D + col);
+            }
+        } else {
+            fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, k0, a.ttot, a.hkv, g, tid);
+        }
+    };
+    fetch(ds);
 
     // One 128-key tile; DIAG marks the last (diagonal) tile, the only one that
     // needs the causal mask and the only one with nothing left to prefetch.
@@ -111,10 +152,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
         constexpr bool DIAG = decltype(diag_tag)::value;
         __syncthreads();
 #pragma unroll
+        for (int r = 0; r < KCHUNKS / 256; ++r) {
+            const int c = tid + 256 * r;
+            const int row = c / KRB, col = (c % KRB) * 16;
+            *reinterpret_cast<u32x4*>(&sm.k[row * KSTR + col]) = kr[r];
+        }
+#pragma unroll
         for (int r = 0; r < CHUNKS / 256; ++r) {
             const int c = tid + 256 * r;
             const int row = c / (D / 16), col = (c % (D / 16)) * 16;
-            *reinterpret_cast<u32x4*>(&sm.k[row * STR + col]) = kr[r];
             *reinterpret_cast<u32x4*>(&sm.v[row * STR + col]) = vr[r];
         }
         if (tid < kTile) {
@@ -122,8 +168,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
             sm.ev[tid] = (uint8_t)evr;
         }
         __syncthreads();
-        if constexpr (!DIAG)
-            fetch_kv_tile<D>(kr, vr, ekr, evr, a.kc, a.ks, a.vc, a.vs, ds + kTile * (t + 1), a.ttot, a.hkv, g, tid);
+        if constexpr (!DIAG) fetch(ds + kTile * (t + 1));
 
         // On the diagonal tile, sub-tiles kk > wave lie entirely after every
         // query of the wave: they contribute p = 0, so they are skipped (no
@@ -136,12 +181,20 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
             if (DIAG && kk > wave_u) continue;
             const int row = 32 * kk + lr;
             s[kk] = v16f{0};
+            if constexpr (MIX) {
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const uint4 lo = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 16 * lg]);
-                const uint4 hi = *reinterpret_cast<const uint4*>(&sm.k[row * STR + 64 * kc + 32 + 16 * lg]);
-                const v8i ka = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                s[kk] = mfma_mx(ka, qb[kc], s[kk], sm.ek[row], eq);
+                for (int kc = 0; kc < NC; ++kc) {
+                    const u32x4 ka = *reinterpret_cast<const u32x4*>(&sm.k[row * KSTR + 32 * kc + 16 * lg]);
+                    s[kk] = mfma_bf16(ka, qn[kc], s[kk]);
+                }
+            } else {
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    const uint4 lo = *reinterpret_cast<const uint4*>(&sm.k[row * KSTR + 64 * kc + 16 * lg]);
+                    const uint4 hi = *reinterpret_cast<const uint4*>(&sm.k[row * KSTR + 64 * kc + 32 + 16 * lg]);
+                    const v8i ka = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    s[kk] = mfma_mx(ka, qb[kc], s[kk], sm.ek[row], eq);
+                }
             }
         }
         // ---- causal mask (sub-tile kk == wave of the diagonal tile):
@@ -243,9 +296,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs
 
 template <int D, int ROWSUM>
 static void launch_fwd_fast(const FwdArgs& a, dim3 g, dim3 b, hipStream_t st) {
-    if (a.fast_exp == 8) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 8>), g, b, 0, st, a);
-    else if (a.fast_exp == 5) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 5>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 0>), g, b, 0, st, a);
+    // the inference exponential is offered on the MXFP8 path only
+    if (a.qn) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 0, 1>), g, b, 0, st, a);
+    else if (a.fast_exp == 8) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 8, 0>), g, b, 0, st, a);
+    else if (a.fast_exp == 5) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 5, 0>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 0, 0>), g, b, 0, st, a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, long grid, hipStream_t st) {

@@ -9,13 +9,16 @@ constexpr int kTile = 128;     // query and key tile (B_r = B_c = 128)
 constexpr int kBlock = 32;     // token block of the operand scales and of the dS blocks
 
 // One tensor of a quantization launch: bf16 [T][heads][d] in, E4M3 codes
-// [T][heads][d] and UE8M0 scales [heads][T] out.
+// [T][heads][d] and UE8M0 scales [heads][T] out; optionally the NVFP4 values
+// of the same rows (one E4M3 scale per 16 channels of a token, E2M1
+// elements) expanded to bf16 [T][heads][d].
 struct QuantTensor {
     const uint16_t* x;
     uint8_t* codes;
     uint8_t* scales;
     int heads;
     int rot;                  // 1: quantize the Hadamard-rotated rows
+    uint16_t* nv;             // NVFP4 values (nullptr: not written)
 };
 
 struct QuantArgs {
@@ -63,6 +66,7 @@ struct FwdArgs {
     float c_log2, tau;
     int rowsum;
     int fast_exp;          // 0, or 5 / 8 key-pair classes of 8 with the approximate exponential
+    const uint16_t *qn, *kn;   // mixed path: NVFP4 values of Q and K (bf16) for the scores; else nullptr
 };
 
 struct BwdArgs {
@@ -75,6 +79,7 @@ struct BwdArgs {
     int ttot, hq, hkv;
     float c1, scale;
     int hadamard;             // 1: rotate dK back (Q and K were rotated)
+    const uint16_t *qn, *kn;  // mixed path: NVFP4 values of Q and K for the scores; else nullptr
     uint8_t* ds_codes;        // dS store (see PlanArgs)
     uint8_t* ds_scales;
     const int32_t* dboff;
@@ -92,6 +97,7 @@ struct DqArgs {
     int ttot, hq, hkv;
     float c1, scale;
     int hadamard;             // 1: rotate dQ back (Q and K were rotated)
+    const uint16_t *qn, *kn;  // mixed path: NVFP4 values of Q and K for the scores; else nullptr
     const uint8_t* ds_codes;  // dS store (see PlanArgs)
     const uint8_t* ds_scales;
     const int32_t* dboff;

@@ -14,7 +14,8 @@
 // loads and stores coalesced: chunk c = lane + 64 r (r < d/16) is the 16-byte
 // piece c % (d/8) of token c / (d/8), so each load instruction of the wave
 // reads whole 2d-byte rows.
-// HBM-bound: the input is read once, codes and scales are written once.
+// HBM-bound: the input is read once, codes and scales are written once (and,
+// for Q and K on the mixed path, their NVFP4 values).
 #include <type_traits>
 
 #include "device.h"
@@ -80,6 +81,42 @@ __device__ __forceinline__ void rotate_rows(float (&v)[R][8], int ch) {
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[r][i] = v[r][i] * rs;
+}
+
+// NVFP4 scale of a 16-channel group with largest magnitude amax (Section 2
+// "Microscaling floating-point formats": E4M3 scale per 16 elements; rounded
+// up like the MX exponents of Section 3.2): the smallest E4M3 value s with
+// 6 s >= amax, 448 above 6 x 448, 0 for amax = 0.  The converted quotient
+// lands within one code of the answer; exact comparisons settle it (6 s has
+// at most 6 significant bits, so it is exact in fp32).
+__device__ __forceinline__ float nvfp4_scale(float amax) {
+    const float t = fminf(amax * (1.f / 6.f), 448.f);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, t, 0, false) & 0x7Fu;
+    const float s = fp8_to_f32(c);
+    const float up = fp8_to_f32(min(c + 1u, 0x7Eu));
+    const float dn = fp8_to_f32(c > 0u ? c - 1u : 0u);
+    const float r = (6.f * s < amax) ? up : s;
+    return (c > 0u && 6.f * dn >= amax) ? dn : r;
+}
+
+// value(E2M1(x / s)) * s as a bf16 pattern (s > 0): the nearest of
+// s x {0, 0.5, 1, 1.5, 2, 3, 4, 6}, ties to the even code, saturating at 6 s.
+// |x| is compared with the exact midpoints m s (at most 7 significant bits),
+// so no rounded quotient decides a code; the value is exact in bf16.  Ties at
+// 0.25, 1.25, 2.5 and 5 go down (to codes 0, 2, 4, 6), those at 0.75, 1.75
+// and 3.5 go up (to codes 2, 4, 6).  s = 0 (an all-zero group) gives +0.
+__device__ __forceinline__ uint32_t nvfp4_bf16(float x, float s) {
+    const float a = fabsf(x);
+    float v = 0.f;
+    v = a > 0.25f * s ? 0.5f * s : v;
+    v = a >= 0.75f * s ? s : v;
+    v = a > 1.25f * s ? 1.5f * s : v;
+    v = a >= 1.75f * s ? 2.f * s : v;
+    v = a > 2.5f * s ? 3.f * s : v;
+    v = a >= 3.5f * s ? 4.f * s : v;
+    v = a > 5.f * s ? 6.f * s : v;
+    const uint32_t b = (__float_as_uint(v) >> 16) | ((__float_as_uint(x) >> 16) & 0x8000u);
+    return s > 0.f ? b : 0u;
 }
 
 }  // namespace
@@ -149,6 +186,28 @@ __global__ void __launch_bounds__(256) quantize_kernel(const QuantArgs a) {
                     make_uint2(packed[r][0], packed[r][1]);
         }
         if (lane < nt) tz.scales[(long)h * a.ttot + bs + lane] = (uint8_t)(e + 127);
+
+        // mixed path (Section 3.4): the NVFP4 values of the same rows, one
+        // scale per 16 channels of each token (lanes ch and ch ^ 1 hold the
+        // two halves of a group), expanded to bf16
+        if (tz.nv) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int tok = tok0 + r * (64 / CPT);
+                float gm = 0.f;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) gm = fmaxf(gm, fabsf(v[r][k]));
+                gm = fmaxf(gm, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(gm), 0xB1, 0xF, 0xF, true)));
+                const float sg = nvfp4_scale(gm);
+                uint32_t w[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    w[k] = nvfp4_bf16(v[r][2 * k], sg) | (nvfp4_bf16(v[r][2 * k + 1], sg) << 16);
+                if (tok < nt)
+                    *reinterpret_cast<uint4*>(tz.nv + ((long)(bs + tok) * H + h) * D + 8 * ch) =
+                        make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
 
         if constexpr (kDO) {
             // D_i = dO~_i . O_i with the dequantized dO and the bf16 output

@@ -29,11 +29,12 @@ class Dims(ctypes.Structure):
 class Opts(ctypes.Structure):
     _fields_ = [("c_log2", ctypes.c_int32), ("tau", ctypes.c_int32), ("key_tile", ctypes.c_int32),
                 ("rowsum", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("hadamard", ctypes.c_int32), ("fast_exp", ctypes.c_int32), ("phase_events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32)]
+                ("hadamard", ctypes.c_int32), ("fast_exp", ctypes.c_int32), ("mixed", ctypes.c_int32),
+                ("phase_events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32)]
 
 
 class Mx(ctypes.Structure):
-    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("nv", ctypes.c_void_p)]
 
 
 class FlamiaError(RuntimeError):
@@ -100,8 +101,9 @@ def _stream(stream):
     return stream if isinstance(stream, int) else stream.cuda_stream
 
 
-def _mx(pair) -> Mx:
-    return Mx(_ptr(pair[0]), _ptr(pair[1]))
+def _mx(t) -> Mx:
+    """(codes, scales) or (codes, scales, nv); nv = the mixed path's NVFP4 values."""
+    return Mx(_ptr(t[0]), _ptr(t[1]), _ptr(t[2]) if len(t) > 2 else None)
 
 
 # ---- the C ABI under the same names -----------------------------------------
@@ -173,6 +175,9 @@ class TrainingCall:
         self.ws = torch.empty(self.ws_bytes, dtype=u8, device=dev)
         self.q_mx = (torch.empty((ttot, hq, d), dtype=u8, device=dev), torch.empty((hq, ttot), dtype=u8, device=dev))
         self.k_mx = (torch.empty((ttot, hkv, d), dtype=u8, device=dev), torch.empty((hkv, ttot), dtype=u8, device=dev))
+        if self.opts.mixed:   # NVFP4 values of Q and K (bf16), read by the score products
+            self.q_mx += (torch.empty((ttot, hq, d), dtype=bf, device=dev),)
+            self.k_mx += (torch.empty((ttot, hkv, d), dtype=bf, device=dev),)
         self.v_mx = (torch.empty((ttot, hkv, d), dtype=u8, device=dev), torch.empty((hkv, ttot), dtype=u8, device=dev))
         self.o = torch.empty((ttot, hq, d), dtype=bf, device=dev)
         self.lse2 = torch.empty((hq, ttot), dtype=torch.float32, device=dev)

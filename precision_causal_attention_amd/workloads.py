@@ -50,6 +50,9 @@ WORKLOADS = {
     # long context: one row of 32768, 16 heads, d = 128, lognormal documents
     # (median 2048, sigma 1.5) clipped to [16, 32768]
     "long-32k": Workload("long-32k", 1, 32768, 16, 16, 128, "lognormal:2048:1.5:16"),
+    # the mixed NVFP4/FP8 path's workload: one row of 8192, 16 heads, d = 128,
+    # lognormal documents (median 1024, sigma 1) clipped to [32, 8192]
+    "mixed-8k": Workload("mixed-8k", 1, 8192, 16, 16, 128, "lognormal:1024:1.0:32"),
 }
 
 

@@ -26,9 +26,9 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_defaults(L):
-    assert F.flamia_abi_version() == 4
+    assert F.flamia_abi_version() == 5
     o = F.flamia_default_opts()
-    assert (o.c_log2, o.tau, o.key_tile, o.rowsum, o.hadamard, o.fast_exp) == (4, 4, 128, 0, 0, 0)
+    assert (o.c_log2, o.tau, o.key_tile, o.rowsum, o.hadamard, o.fast_exp, o.mixed) == (4, 4, 128, 0, 0, 0, 0)
     assert F.flamia_status_str(0) == "ok"
 
 
@@ -61,21 +61,21 @@ def test_ds_store_sizing():
 FAKE = 1 << 20   # aligned non-null host integer, never dereferenced: validation fails first
 
 
-def call_fwd(dm, opts=None, ws_bytes=None, **over):
+def call_fwd(dm, opts=None, ws_bytes=None, q_mx=(FAKE, FAKE), k_mx=(FAKE, FAKE), **over):
     args = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, o=FAKE, lse=FAKE, ws=FAKE)
     args.update(over)
     mx = (FAKE, FAKE)
     wsb = F.flamia_workspace_bytes(dims()) if ws_bytes is None else ws_bytes
-    return F.flamia_fwd(dm, opts, args["q"], args["k"], args["v"], args["cu"], mx, mx, mx,
+    return F.flamia_fwd(dm, opts, args["q"], args["k"], args["v"], args["cu"], q_mx, k_mx, mx,
                         args["o"], args["lse"], args["ws"], wsb, stream=0, check=False)
 
 
-def call_bwd(dm, opts=None, ws_bytes=None, **over):
+def call_bwd(dm, opts=None, ws_bytes=None, q_mx=(FAKE, FAKE), k_mx=(FAKE, FAKE), **over):
     args = dict(do=FAKE, o=FAKE, lse=FAKE, cu=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE)
     args.update(over)
     mx = (FAKE, FAKE)
     wsb = F.flamia_workspace_bytes(dims()) if ws_bytes is None else ws_bytes
-    return F.flamia_bwd(dm, opts, args["do"], args["o"], args["lse"], args["cu"], mx, mx, mx,
+    return F.flamia_bwd(dm, opts, args["do"], args["o"], args["lse"], args["cu"], q_mx, k_mx, mx,
                         args["dq"], args["dk"], args["dv"], args["ws"], wsb, stream=0, check=False)
 
 
@@ -110,7 +110,28 @@ def test_backward_refuses_inference_exponential():
     o.fast_exp = 5
     assert call_bwd(dims(), opts=o) == 4          # FLAMIA_ERR_OPTS
     o.fast_exp = 0
-    assert call_bwd(dims(), opts=o) != 4
+    # accepted options: the call then stops at the next check (a workspace
+    # that is too small), so nothing is launched on the fake pointers
+    assert call_bwd(dims(), opts=o, ws_bytes=100) == 5
+
+
+@pytest.mark.parametrize("call", [call_fwd, call_bwd])
+def test_mixed_path_validation(call):
+    """Section 3.4 mixed path: opts.mixed is 0 or 1, excludes the inference
+    exponential, and needs the NVFP4 value buffers of Q and K."""
+    o = F.flamia_default_opts()
+    o.mixed = 2
+    assert call(dims(), opts=o) == 4
+    o.mixed = 1
+    o.fast_exp = 5
+    assert call(dims(), opts=o) == 4
+    o.fast_exp = 0
+    assert call(dims(), opts=o) == 1                                   # no nv buffers
+    assert call(dims(), opts=o, q_mx=(FAKE, FAKE, FAKE)) == 1          # K's missing
+    assert call(dims(), opts=o, q_mx=(FAKE, FAKE, FAKE), k_mx=(FAKE, FAKE, FAKE + 2)) == 3
+    assert call(dims(), opts=o, q_mx=(FAKE, FAKE, FAKE), k_mx=(FAKE, FAKE, FAKE), ws_bytes=100) == 5
+    o.mixed = 0                                                         # nv is ignored off the mixed path
+    assert call(dims(), opts=o, q_mx=(FAKE, FAKE, FAKE + 2), ws_bytes=100) == 5
 
 
 def test_quantize_validation():
@@ -120,3 +141,4 @@ def test_quantize_validation():
     assert F.flamia_quantize(dm, 2, 0, FAKE, mx, stream=0, check=False) == 1
     assert F.flamia_quantize(dm, 2, FAKE + 2, FAKE, mx, stream=0, check=False) == 3
     assert F.flamia_quantize(dims(d=32), 2, FAKE, FAKE, mx, stream=0, check=False) == 2
+    assert F.flamia_quantize(dm, 2, FAKE, FAKE, (FAKE, FAKE, FAKE + 2), stream=0, check=False) == 3
