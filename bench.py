@@ -28,6 +28,11 @@ Prints ONE JSON line:
             launch from the committed counter summary of the workload, while
             the kernel's sources still match the digest recorded there
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+
+--mixed 1 times the mixed NVFP4/FP8 path instead (a metric of its own): the
+score products (forward S and its recomputation in both backward kernels)
+run on the bf16 MFMA, the other products on the FP8 one, so each kernel's
+roofline peak is the FLOP-weighted harmonic mean of the two dense peaks.
 """
 import argparse
 import ctypes
@@ -41,7 +46,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fwd+bwd causal attention TFLOP/s incl. quant (MXFP8, packed docs), % of roofline"
+METRIC_MIXED = "fwd+bwd causal attention TFLOP/s incl. quant (mixed NVFP4/FP8, packed docs), % of roofline"
 MXFP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8/MXFP8 MFMA peak (AMD specification)
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA peak (AMD specification)
+# products per kernel (each 2d x L^2/2 causal pairs per head): score products
+# (bf16 on the mixed path) and the others (FP8)
+KERNEL_PRODUCTS = {"fwd_kernel": (1, 1), "dkv_kernel": (1, 3), "dq_kernel": (1, 2), "call": (2, 5)}
+
+
+def mixed_peak(kernel):
+    """Peak of a kernel whose score products run on the bf16 MFMA and the
+    rest on the FP8 one: total FLOP over the time each part takes at its peak."""
+    s, f = KERNEL_PRODUCTS[kernel]
+    return (s + f) / (s / BF16_PEAK_TFLOPS + f / MXFP8_PEAK_TFLOPS)
 FWD_PHASES = ["quantize_qkv", "worklist_fwd", "fwd_kernel"]
 BWD_PHASES = ["quantize_do", "worklist_bwd", "dkv_kernel", "dq_kernel"]
 CSRC = os.path.join(ROOT, "precision_causal_attention_amd", "csrc")
@@ -110,25 +127,38 @@ def recorded_traffic(workload, kernel, doclen_cap):
     return None
 
 
-def cpu_baseline(inst, hkv, hadamard=0):
-    """The oracle as it stands, on key/value head 0 and its query heads (all
-    documents), scaled to TFLOP/s of that sample."""
+def cpu_baseline(inst, hkv, hadamard=0, mixed=0, target_s=10.0):
+    """The oracle as it stands on a sample of the workload: key/value head 0
+    and its query heads (all documents) is timed first; while a call takes
+    less than target_s, the sample grows to the first n key/value heads (one
+    call, n scaled from the last time; at most two more calls) and the last
+    call is reported.  Scaled to TFLOP/s."""
     import numpy as np
 
     import oracle
     oracle.build(force=False)
-    km = np.zeros(hkv, np.uint8)
-    km[0] = 1
-    t0 = time.perf_counter()
-    oracle.attention(inst["q"], inst["k"], inst["v"], inst["do"], inst["cu_seqlens"],
-                     oracle.Opts(hadamard=hadamard), kv_mask=km, want_f64=False)
-    dt = time.perf_counter() - t0
+
+    def run(n):
+        km = np.zeros(hkv, np.uint8)
+        km[:n] = 1
+        t0 = time.perf_counter()
+        oracle.attention(inst["q"], inst["k"], inst["v"], inst["do"], inst["cu_seqlens"],
+                         oracle.Opts(hadamard=hadamard, mixed=mixed), kv_mask=km, want_f64=False)
+        return time.perf_counter() - t0
+
+    n, dt = 1, run(1)
+    for _ in range(2):   # more heads also parallelize better: at most two more calls
+        if dt >= target_s or n >= hkv:
+            break
+        n = min(hkv, max(n + 1, math.ceil(n * target_s / max(dt, 1e-3))))
+        dt = run(n)
     hq, d = inst["q"].shape[1], inst["q"].shape[2]
     G = hq // hkv
-    flop = 7.0 * G * d * inst["sum_L2"]
+    flop = 7.0 * n * G * d * inst["sum_L2"]
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"key/value head 0 of {hkv} ({G} of {hq} query heads), all {len(inst['lengths'])} "
-                      f"documents, forward + backward incl. quantization; {dt:.1f} s wall"}
+            "sample": f"key/value head{'s 0-' + str(n - 1) if n > 1 else ' 0'} of {hkv} ({n * G} of {hq} query heads), all "
+                      f"{len(inst['lengths'])} documents, forward + backward incl. quantization"
+                      f"{' (mixed NVFP4/FP8 path)' if mixed else ''}; {dt:.1f} s wall"}
 
 
 def inference_bench(args, call, q, k, v, cu, stream, hip, wl, inst, doclen_cap):
@@ -161,18 +191,20 @@ def inference_bench(args, call, q, k, v, cu, stream, hip, wl, inst, doclen_cap):
     ms = t0.elapsed_time(t1) / args.steps
     flop = 2.0 * hq * d * inst["sum_L2"]
     kern = phases["fwd_kernel"]
+    peak = mixed_peak("fwd_kernel") if args.mixed else MXFP8_PEAK_TFLOPS
     print(json.dumps({
-        "metric": "inference forward TFLOP/s incl. quant (MXFP8, packed docs)",
+        "metric": "inference forward TFLOP/s incl. quant (%s, packed docs)"
+                  % ("mixed NVFP4/FP8" if args.mixed else "MXFP8"),
         "value": round(flop / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "dtype": "fp8e4m3", "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "hq": hq, "hkv": inst["k"].shape[1], "d": d,
                    "sum_L2": inst["sum_L2"], "seed": args.seed, "fast_exp": args.inference,
-                   "hadamard": args.hadamard},
+                   "hadamard": args.hadamard, "mixed": args.mixed},
         "phases_ms": {p: round(t, 4) for p, t in phases.items()},
         "roofline": {"kernel": "fwd_kernel", "kernel_ms": round(kern, 4), "bound": "mfma",
-                     "achieved": round(flop / (kern * 1e-3) / 1e12, 2), "peak": MXFP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(flop / (kern * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4)},
+                     "achieved": round(flop / (kern * 1e-3) / 1e12, 2), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(flop / (kern * 1e-3) / 1e12 / peak, 4)},
     }), flush=True)
 
 
@@ -194,10 +226,16 @@ def main():
                     help="time the inference call (quantization + forward only) with the "
                          "approximate exponential on 0, 5 or 8 of the 8 key-pair classes "
                          "(a separate metric; -1, the default: the training call)")
+    ap.add_argument("--mixed", type=int, default=0, choices=(0, 1),
+                    help="1: the mixed NVFP4/FP8 path (NVFP4 Q and K for the scores; a separate "
+                         "metric, measured on the workload mixed-8k)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a fill and a widening copy of this many MiB (known-size "
                          "references for hardware byte counters collected over the same run)")
     args = ap.parse_args()
+    if args.mixed and args.inference > 0:
+        print("the approximate exponential is offered on the MXFP8 path only", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build runs the attention call on a single "
               f"MI355X); --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -220,8 +258,10 @@ def main():
     cu = torch.from_numpy(inst["cu_seqlens"]).cuda()
     # dS store sized for the longest possible document (a whole row), at d = 128
     doclen_cap = (wl.row_len if d == 128 else 0) if args.doclen_cap < 0 else args.doclen_cap
-    call = F.TrainingCall(T, hq, hkv, d, ndocs_cap=ndocs, doclen_cap=doclen_cap)
-    call.opts.hadamard = args.hadamard
+    opts = F.flamia_default_opts()
+    opts.hadamard = args.hadamard
+    opts.mixed = args.mixed
+    call = F.TrainingCall(T, hq, hkv, d, ndocs_cap=ndocs, opts=opts, doclen_cap=doclen_cap)
     hip = Hip()
     nf, nb = len(FWD_PHASES) + 1, len(BWD_PHASES) + 1
     stream = torch.cuda.current_stream()
@@ -333,8 +373,9 @@ def main():
 
     tflops = flop / (ms_step * 1e-3) / 1e12
     achieved = kflop[dom] / (dom_ms * 1e-3) / 1e12
+    peak = mixed_peak(dom) if args.mixed else MXFP8_PEAK_TFLOPS
     result = {
-        "metric": METRIC,
+        "metric": METRIC_MIXED if args.mixed else METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -344,22 +385,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3",
+        "dtype": "fp8e4m3+bf16" if args.mixed else "fp8e4m3",
         "data": "synthetic",
         "frac_of_mxfp8_peak": round(tflops / MXFP8_PEAK_TFLOPS, 4),
+        "frac_of_path_peak": round(tflops / (mixed_peak("call") if args.mixed else MXFP8_PEAK_TFLOPS), 4),
         "config": {"workload": wl.name, "rows": wl.rows, "row_len": wl.row_len, "tokens": T, "hq": hq,
                    "hkv": hkv, "d": d, "docs": ndocs, "sum_L2": sum_l2, "seed": args.seed,
                    "doc_law": wl.docs, "doclen_cap": doclen_cap, "hadamard": args.hadamard,
-                   "parallelism": "single-gpu"},
+                   "mixed": args.mixed, "parallelism": "single-gpu"},
         "graph_ms_per_step": round(graph_ms_step, 4),
         "phases_ms": {p: round(t, 4) for p, t in phases.items()},
         "roofline": {"kernel": dom, "kernel_ms": round(dom_ms, 4), "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": MXFP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MXFP8_PEAK_TFLOPS, 4),
-                     "traffic": recorded_traffic(wl.name, dom, doclen_cap)},
+                     "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None if args.mixed else recorded_traffic(wl.name, dom, doclen_cap)},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")
-        result["cpu_baseline"] = cpu_baseline(inst, hkv, args.hadamard)
+        result["cpu_baseline"] = cpu_baseline(inst, hkv, args.hadamard, args.mixed)
     print(json.dumps(result), flush=True)
 
 
