@@ -48,13 +48,15 @@ struct BwdStep {
     alignas(16) uint8_t qn[MIX ? kQStep * kNStride : 16];   // NVFP4 values of Q (mixed path)
 };
 
-// Step buffers: with the software pipeline (d = 64, MXFP8) the products of
-// step i read buffer i % 2 while the dV/dK products of step i - 1 still read
-// the other one.
-template <int D, int MIX>
+// A ring of step buffers, so that a step fills its buffer without waiting:
+// step i writes buffer i % N, last read by the products of step i - N and,
+// with the software pipeline (d = 64, MXFP8, N = 3), by the dV/dK products
+// of that step issued in step i - N + 1; every wave is past both before it
+// reaches the barrier of step i - 1.
+template <int D, int MIX, int N>
 struct BwdSmem {
     static constexpr int kStride = BwdStep<D, MIX>::kStride;
-    BwdStep<D, MIX> buf[D == 64 && !MIX ? 2 : 1];
+    BwdStep<D, MIX> buf[N];
 };
 
 template <int D, bool STORE, int MIX>
@@ -62,11 +64,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     constexpr int KC = D / 64;
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;
-    constexpr int STR = BwdSmem<D, MIX>::kStride;
+    // The mixed path's bf16 operands take the registers the pipeline needs.
+    constexpr bool PIPE = D == 64 && !STORE && !MIX;
+    constexpr int NBUF = PIPE ? 3 : 2;
+    constexpr int STR = BwdStep<D, MIX>::kStride;
     constexpr int NSTR = BwdStep<D, MIX>::kNStride;
     constexpr int NQ = kQStep * D / 16 / 256;     // 16-byte chunks per thread of a 64-row code tile
     constexpr int NQN = MIX ? 2 * NQ : 1;         // same for the bf16 NVFP4 rows
-    __shared__ BwdSmem<D, MIX> sm;
+    __shared__ BwdSmem<D, MIX, NBUF> sm;
 
     const int ti = (int)blockIdx.x / a.hkv;
     if (ti >= *a.ntiles) return;
@@ -210,9 +215,8 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
     // the matrix cores while the wave computes the next softmax.  At d = 128
     // the extra live codes cost an occupancy step, and with the store they
     // spill, so the products follow their own step there.
-    // The mixed path's bf16 operands take the registers the pipeline needs.
-    constexpr bool PIPE = D == 64 && !STORE && !MIX;
     int cur = 0;                           // step buffer of the current step
+    int prv = 0;                           // step buffer of the previous step
     bool dvdk_due = false;                 // the previous step's dV/dK products are pending
     int ppbc[2][4], pdsc[2][4], pes[2];
 
@@ -239,7 +243,6 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
         constexpr bool MASK = decltype(mask_tag)::value;
         // ---- publish the prefetched step in LDS, start fetching the next one
         BwdStep<D, MIX>& B = sm.buf[cur];
-        __syncthreads();                   // buffer cur: its last readers were two steps ago
         store_step(B);
         __syncthreads();
         const int h = g * G + hh;
@@ -298,7 +301,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             }
         }
         // ---- the previous step's dV/dK products, under this step's softmax
-        if (PIPE && dvdk_due) dvdk(sm.buf[cur ^ 1], ppbc, pdsc, pes);
+        if (PIPE && dvdk_due) dvdk(sm.buf[prv], ppbc, pdsc, pes);
         // ---- P, P-hat_b, dS, dS-hat (one 32x32 block per accumulator tile)
         // accumulator register i = 4j + r of query block st holds query
         // qs0 + 32st + 8j + 4lg + r; masked while the wave's key lies after it
@@ -378,10 +381,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
                 }
                 pes[st] = es[st];
             }
-            cur ^= 1;
         } else if (!skipped(1)) {
             dvdk(B, pbc, dsc, es);
         }
+        prv = cur;
+        cur = cur + 1 == NBUF ? 0 : cur + 1;
         return more;
     };
     // two loops instead of a per-step choice, so that both bodies keep the
@@ -391,7 +395,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
         while (more && q0 < kt0 + kTile) more = step(std::true_type{});
         while (more && q0 >= kt0 + kTile) more = step(std::false_type{});
     }
-    if (PIPE && dvdk_due) dvdk(sm.buf[cur ^ 1], ppbc, pdsc, pes);
+    if (PIPE && dvdk_due) dvdk(sm.buf[prv], ppbc, pdsc, pes);
     flush_store();
     // ---- epilogue: dK = softmax_scale * sum, dV; summed over the group's heads.
     // With the Hadamard option the dK sum is the gradient of the rotated K and
