@@ -3,7 +3,8 @@
 One step = flamia_fwd (quantize Q/K/V in one launch, work list, forward
 kernel) followed by flamia_bwd (quantize dO with D, work lists, key-major
 dK/dV kernel, query-major dQ kernel) on one seeded synthetic batch already
-resident in HBM.
+resident in HBM (without a dS store the backward's dQ pass runs first and
+quantizes dO itself: work lists, dQ, dK/dV).
 
 Every HIP event recorded between two launches adds a few microseconds of
 dispatch gap, so the measurement runs in passes:
@@ -60,7 +61,11 @@ def mixed_peak(kernel):
     s, f = KERNEL_PRODUCTS[kernel]
     return (s + f) / (s / BF16_PEAK_TFLOPS + f / MXFP8_PEAK_TFLOPS)
 FWD_PHASES = ["quantize_qkv", "worklist_fwd", "fwd_kernel"]
-BWD_PHASES = ["quantize_do", "worklist_bwd", "dkv_kernel", "dq_kernel"]
+# the backward's launches: with a dS store (doclen_cap > 0) dO is quantized
+# by its own launch before the key-major pass; without one the query-major
+# dQ pass runs first and quantizes dO itself
+BWD_PHASES_STORE = ["quantize_do", "worklist_bwd", "dkv_kernel", "dq_kernel"]
+BWD_PHASES_FUSED = ["worklist_bwd", "dq_kernel", "dkv_kernel"]
 CSRC = os.path.join(ROOT, "precision_causal_attention_amd", "csrc")
 # sources whose text decides each attention kernel's memory traffic
 KERNEL_SOURCES = {"fwd_kernel": ["fwd.hip"], "dkv_kernel": ["bwd.hip"], "dq_kernel": ["dq.hip", "dq_store.hip"]}
@@ -263,6 +268,7 @@ def main():
     opts.mixed = args.mixed
     call = F.TrainingCall(T, hq, hkv, d, ndocs_cap=ndocs, opts=opts, doclen_cap=doclen_cap)
     hip = Hip()
+    BWD_PHASES = BWD_PHASES_FUSED if doclen_cap == 0 else BWD_PHASES_STORE
     nf, nb = len(FWD_PHASES) + 1, len(BWD_PHASES) + 1
     stream = torch.cuda.current_stream()
 

@@ -120,9 +120,11 @@ typedef struct {
      * event i on `stream` before its i-th internal launch and the next one
      * after its last launch, as far as n_events allows; NULL entries are
      * skipped (no event recorded there).  flamia_fwd has 3 phases (quantize
-     * Q, K and V in one launch; work list; forward kernel), flamia_bwd 4
-     * (quantize dO with D; work lists; key-major dK/dV kernel; query-major dQ
-     * kernel).  NULL disables it. */
+     * Q, K and V in one launch; work list; forward kernel); flamia_bwd has 4
+     * with a dS store (doclen_cap > 0: quantize dO with D; work lists;
+     * key-major dK/dV kernel; query-major dQ kernels) and 3 without one
+     * (work lists; query-major dQ kernel, which also quantizes dO and
+     * computes D; key-major dK/dV kernel).  NULL disables it. */
     void **phase_events;
     int32_t n_events;
 } flamia_opts_t;
@@ -200,7 +202,9 @@ flamia_status_t flamia_fwd(const flamia_dims_t *dims, const flamia_opts_t *opts,
  * A key-major pass accumulates dK and dV; a query-major pass accumulates dQ,
  * either from the dS-hat blocks the key-major pass stored or, without a store
  * (or when the call's documents do not fit it), by rebuilding the same dS-hat
- * payload bit for bit.  Each output element is owned by one workgroup, so the
+ * payload bit for bit.  Without a store the query-major pass runs first and
+ * quantizes dO itself (same codes, scales and D as the separate quantization
+ * launch that precedes the key-major pass when a store is configured).  Each output element is owned by one workgroup, so the
  * backward is deterministic (no atomics).
  */
 flamia_status_t flamia_bwd(const flamia_dims_t *dims, const flamia_opts_t *opts,

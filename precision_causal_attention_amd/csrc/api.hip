@@ -273,15 +273,6 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     uint8_t* os = base + w.oscales;
     float* dvec = (float*)(base + w.dvec);
 
-    // dO launch: codes + scales and D = dO~ . O (Section 3.5.1)
-    QuantArgs qa{};
-    qa.cu = cu_seqlens; qa.ndocs = dims->ndocs; qa.ttot = dims->ttot; qa.d = d;
-    qa.t[0] = QuantTensor{d_o, oc, os, dims->hq, 0, nullptr};
-    qa.ntensors = 1;
-    qa.o = o; qa.dvec = dvec;
-    PhaseMarks pm{opts, st};
-    hipError_t e;
-    if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(qa, st)) != hipSuccess) return hip_fail(e);
     int32_t* ctrl = (int32_t*)(base + w.ctrl);
     int4* tiles_q = (int4*)(base + w.tiles_q);
     int4* tiles_k = (int4*)(base + w.tiles_k);
@@ -290,7 +281,6 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     uint8_t* ds_scales = base + w.ds_scales;
     PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
                 tiles_q, tiles_k, dboff, w.ds_blocks};
-    if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
     const float scale = scale_of(opts, d);
     BwdArgs ba;
     ba.qc = q_mx.codes; ba.qs = q_mx.scales;
@@ -307,8 +297,6 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     ba.qn = opts.mixed ? q_mx.nv : nullptr;
     ba.kn = opts.mixed ? k_mx.nv : nullptr;
     ba.ds_codes = ds_codes; ba.ds_scales = ds_scales; ba.dboff = dboff; ba.ds_blocks = w.ds_blocks;
-    if ((e = pm.mark()) != hipSuccess || (e = launch_bwd(ba, d, w.max_tiles * dims->hkv, st)) != hipSuccess)
-        return hip_fail(e);
     DqArgs qd;
     qd.qc = q_mx.codes; qd.qs = q_mx.scales;
     qd.kc = k_mx.codes; qd.ks = k_mx.scales;
@@ -322,13 +310,36 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     qd.c1 = ba.c1;
     qd.hadamard = opts.hadamard;
     qd.qn = ba.qn; qd.kn = ba.kn;
+    qd.d_o = nullptr; qd.o = nullptr; qd.oc_w = nullptr; qd.os_w = nullptr; qd.dvec_w = nullptr;
     qd.ds_codes = ds_codes; qd.ds_scales = ds_scales; qd.dboff = dboff; qd.ds_blocks = w.ds_blocks;
-    // dQ: from the stored blocks when the call fits the store (decided on the
-    // device; the other kernel returns at once), else by rebuilding dS-hat
-    if ((e = pm.mark()) != hipSuccess) return hip_fail(e);
-    if (w.ds_blocks > 0 && (e = launch_dq_store(qd, d, w.max_tiles * dims->hq, st)) != hipSuccess)
-        return hip_fail(e);
-    if ((e = launch_dq(qd, d, w.max_tiles * dims->hq, st)) != hipSuccess) return hip_fail(e);
+    PhaseMarks pm{opts, st};
+    hipError_t e;
+    const long gq = w.max_tiles * dims->hq, gk = w.max_tiles * dims->hkv;
+    if (w.ds_blocks == 0) {
+        // No dS store: the query-major dQ pass runs first and quantizes dO
+        // itself (codes, scales and D for the key-major pass), so no separate
+        // dO launch (Section 3.5.1 fused quantization).
+        qd.d_o = d_o; qd.o = o; qd.oc_w = oc; qd.os_w = os; qd.dvec_w = dvec;
+        if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
+        if ((e = pm.mark()) != hipSuccess || (e = launch_dq(qd, d, gq, st)) != hipSuccess) return hip_fail(e);
+        if ((e = pm.mark()) != hipSuccess || (e = launch_bwd(ba, d, gk, st)) != hipSuccess) return hip_fail(e);
+    } else {
+        // dS store: dO launch (codes, scales and D = dO~ . O, Section 3.5.1),
+        // work lists, the key-major pass (which stores the dS-hat blocks),
+        // then dQ from the store when the call fits it (decided on the
+        // device; the other dQ kernel returns at once), else by rebuilding
+        QuantArgs qa{};
+        qa.cu = cu_seqlens; qa.ndocs = dims->ndocs; qa.ttot = dims->ttot; qa.d = d;
+        qa.t[0] = QuantTensor{d_o, oc, os, dims->hq, 0, nullptr};
+        qa.ntensors = 1;
+        qa.o = o; qa.dvec = dvec;
+        if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(qa, st)) != hipSuccess) return hip_fail(e);
+        if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
+        if ((e = pm.mark()) != hipSuccess || (e = launch_bwd(ba, d, gk, st)) != hipSuccess) return hip_fail(e);
+        if ((e = pm.mark()) != hipSuccess) return hip_fail(e);
+        if ((e = launch_dq_store(qd, d, gq, st)) != hipSuccess) return hip_fail(e);
+        if ((e = launch_dq(qd, d, gq, st)) != hipSuccess) return hip_fail(e);
+    }
     e = pm.mark();
     return e == hipSuccess ? FLAMIA_OK : hip_fail(e);
 }

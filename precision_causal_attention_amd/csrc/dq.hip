@@ -21,6 +21,12 @@
 // Mixed NVFP4/FP8 path (Section 3.4): S^T comes from the NVFP4 values of K
 // and Q (bf16 MFMAs, as in the forward), while dQ still contracts over the
 // E4M3 token-block K^, so a key tile stages both forms of its rows.
+// Without a dS store the pass runs before the key-major one and quantizes dO
+// itself (Section 3.5.1 fused quantization): the wave's 32 queries are one
+// document-local 32-token block, so the wave computes the block exponent,
+// the codes (its own dP operand) and D = dO~ . O, and writes them for the
+// key-major pass, in the order of the standalone quantizer, so D is the same
+// bit for bit.
 #include <type_traits>
 
 #include "device.h"
@@ -39,7 +45,7 @@ struct DqSmem {
     alignas(16) uint8_t kn[MIX ? kTile * kNStride : 16];
 };
 
-template <int D, int MIX>
+template <int D, int MIX, bool FUSED>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a) {
     constexpr int KC = D / 64;
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
@@ -82,9 +88,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
                 hi = *reinterpret_cast<const uint4*>(qp + 64 * kc + 32 + 16 * lg);
                 qb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             }
-            lo = *reinterpret_cast<const uint4*>(op + 64 * kc + 16 * lg);
-            hi = *reinterpret_cast<const uint4*>(op + 64 * kc + 32 + 16 * lg);
-            ob[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            if constexpr (!FUSED) {
+                lo = *reinterpret_cast<const uint4*>(op + 64 * kc + 16 * lg);
+                hi = *reinterpret_cast<const uint4*>(op + 64 * kc + 32 + 16 * lg);
+                ob[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
         }
         if constexpr (MIX) {
             const uint16_t* np = a.qn + ((long)q_row * a.hq + h) * D;
@@ -93,13 +101,98 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
         }
     }
     const int eq = MIX ? 127 : a.qs[(long)h * a.ttot + q_row];
-    const int eo = a.os[(long)h * a.ttot + q_row];
+    int eo;
+    float nD;
+    if constexpr (FUSED) {
+        // the lane's dO channels: run 0 = 64 kc + 16 lg .. + 16, run 1 = 64 kc
+        // + 32 + 16 lg .. + 16 (the operand's byte order); zero outside the document
+        const long rowoff = ((long)q_row * a.hq + h) * D;
+        float x[KC][2][16];
+        float amax = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int run = 0; run < 2; ++run) {
+                const uint16_t* src = a.d_o + rowoff + 64 * kc + 32 * run + 16 * lg;
+                uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
+                if (q_valid) {
+                    u0 = *reinterpret_cast<const uint4*>(src);
+                    u1 = *reinterpret_cast<const uint4*>(src + 8);
+                }
+                const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    x[kc][run][2 * k] = bf16_to_f32(w[k] & 0xFFFFu);
+                    x[kc][run][2 * k + 1] = bf16_to_f32(w[k] >> 16);
+                }
+#pragma unroll
+                for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[kc][run][k]));
+            }
+        amax = wave_max_nonneg(amax);
+        const int e = block_exponent_uniform(amax, -127);   // the block of the wave's 32 queries
+        eo = e + 127;
+        // codes = E4M3(x 2^-e); D = sum over 8-channel chunks c of the chain
+        // fma(code value, O, .) in channel order, chunks summed as the
+        // standalone quantizer's lane tree sums them: ((c0 + c1) + (c2 + c3)) +
+        // ((c4 + c5) + (c6 + c7)) per 64 channels, then the two halves at d = 128
+        float tot = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            float pr[2];
+#pragma unroll
+            for (int run = 0; run < 2; ++run) {
+                const uint16_t* osrc = a.o + rowoff + 64 * kc + 32 * run + 16 * lg;
+                const uint4 o0 = *reinterpret_cast<const uint4*>(osrc);
+                const uint4 o1 = *reinterpret_cast<const uint4*>(osrc + 8);
+                const uint32_t ow[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+                int cw[4];
+                float chunk[2];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float* v = &x[kc][run][4 * q];
+                    cw[q] = pack_fp8x4(ldexpf(v[0], -e), ldexpf(v[1], -e), ldexpf(v[2], -e), ldexpf(v[3], -e));
+                }
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {     // chunk c of the run: channels 8 c .. 8 c + 7
+                    float dot = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[2 * c + q], false);
+                        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[2 * c + q], true);
+                        const uint32_t o01 = ow[4 * c + 2 * q], o23 = ow[4 * c + 2 * q + 1];
+                        dot = fmaf(lo[0], bf16_to_f32(o01 & 0xFFFFu), dot);
+                        dot = fmaf(lo[1], bf16_to_f32(o01 >> 16), dot);
+                        dot = fmaf(hi[0], bf16_to_f32(o23 & 0xFFFFu), dot);
+                        dot = fmaf(hi[1], bf16_to_f32(o23 >> 16), dot);
+                    }
+                    chunk[c] = dot;
+                }
+                pr[run] = chunk[0] + chunk[1];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ob[kc][4 * run + q] = cw[q];
+                if (q_valid)
+                    *reinterpret_cast<uint4*>(a.oc_w + rowoff + 64 * kc + 32 * run + 16 * lg) =
+                        make_uint4((uint32_t)cw[0], (uint32_t)cw[1], (uint32_t)cw[2], (uint32_t)cw[3]);
+            }
+            // the partner lane (l ^ 32) holds the other chunk pair of each run
+            const float half = add_xor32(pr[0]) + add_xor32(pr[1]);
+            tot = kc == 0 ? half : tot + half;
+        }
+        const float dval = ldexpf(tot, e);
+        if (q_valid && lg == 0) {
+            a.os_w[(long)h * a.ttot + q_row] = (uint8_t)eo;
+            a.dvec_w[(long)h * a.ttot + q_row] = dval;
+        }
+        nD = -dval;
+    } else {
+        eo = a.os[(long)h * a.ttot + q_row];
+        nD = -a.dvec[(long)h * a.ttot + q_row];
+    }
     const float lse_raw = a.lse2[(long)h * a.ttot + q_row];
     const float lse = q_valid ? lse_raw : INFINITY;      // P = 0 on rows outside the document
     // -D as the accumulator input of the dP^T product (every register of a
     // lane belongs to the lane's query): the MFMA returns dP - D directly,
     // with the same error as a separate fp32 subtraction
-    const float nD = -a.dvec[(long)h * a.ttot + q_row];
     v16f negD;
 #pragma unroll
     for (int i = 0; i < 16; ++i) negD[i] = nD;
@@ -127,6 +220,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
         }
     };
     fetch(ds);
+
 
     // One 128-key tile; DIAG marks the last (diagonal) tile, the only one that
     // needs the causal mask and the only one with nothing left to prefetch.
@@ -282,12 +376,23 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a
 hipError_t launch_dq(const DqArgs& a, int d, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), b(256);
+    const bool fused = a.d_o != nullptr;
     if (d == 64) {
-        if (a.qn) hipLaunchKernelGGL((dq_kernel<64, 1>), g, b, 0, st, a);
-        else hipLaunchKernelGGL((dq_kernel<64, 0>), g, b, 0, st, a);
+        if (a.qn) {
+            if (fused) hipLaunchKernelGGL((dq_kernel<64, 1, true>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((dq_kernel<64, 1, false>), g, b, 0, st, a);
+        } else {
+            if (fused) hipLaunchKernelGGL((dq_kernel<64, 0, true>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((dq_kernel<64, 0, false>), g, b, 0, st, a);
+        }
     } else {
-        if (a.qn) hipLaunchKernelGGL((dq_kernel<128, 1>), g, b, 0, st, a);
-        else hipLaunchKernelGGL((dq_kernel<128, 0>), g, b, 0, st, a);
+        if (a.qn) {
+            if (fused) hipLaunchKernelGGL((dq_kernel<128, 1, true>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((dq_kernel<128, 1, false>), g, b, 0, st, a);
+        } else {
+            if (fused) hipLaunchKernelGGL((dq_kernel<128, 0, true>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((dq_kernel<128, 0, false>), g, b, 0, st, a);
+        }
     }
     return hipGetLastError();
 }

@@ -98,6 +98,12 @@ struct DqArgs {
     float c1, scale;
     int hadamard;             // 1: rotate dQ back (Q and K were rotated)
     const uint16_t *qn, *kn;  // mixed path: NVFP4 values of Q and K for the scores; else nullptr
+    // Without a dS store this pass runs first and quantizes dO itself: bf16
+    // dO and O in; the dO codes, scales and D out (read by the key-major
+    // pass that follows).  nullptr: the codes, scales and D are inputs.
+    const uint16_t *d_o, *o;
+    uint8_t *oc_w, *os_w;
+    float* dvec_w;
     const uint8_t* ds_codes;  // dS store (see PlanArgs)
     const uint8_t* ds_scales;
     const int32_t* dboff;
