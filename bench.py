@@ -135,9 +135,9 @@ def recorded_traffic(workload, kernel, doclen_cap):
 def cpu_baseline(inst, hkv, hadamard=0, mixed=0, target_s=10.0):
     """The oracle as it stands on a sample of the workload: key/value head 0
     and its query heads (all documents) is timed first; while a call takes
-    less than target_s, the sample grows to the first n key/value heads (one
-    call, n scaled from the last time; at most two more calls) and the last
-    call is reported.  Scaled to TFLOP/s."""
+    less than target_s, the sample doubles to the first n key/value heads (one
+    call each, at most three more) and the last call is reported.  Scaled to
+    TFLOP/s."""
     import numpy as np
 
     import oracle
@@ -152,10 +152,10 @@ def cpu_baseline(inst, hkv, hadamard=0, mixed=0, target_s=10.0):
         return time.perf_counter() - t0
 
     n, dt = 1, run(1)
-    for _ in range(2):   # more heads also parallelize better: at most two more calls
+    for _ in range(3):   # more heads also parallelize better: double, at most three more calls
         if dt >= target_s or n >= hkv:
             break
-        n = min(hkv, max(n + 1, math.ceil(n * target_s / max(dt, 1e-3))))
+        n = min(hkv, 2 * n)
         dt = run(n)
     hq, d = inst["q"].shape[1], inst["q"].shape[2]
     G = hq // hkv
@@ -221,10 +221,10 @@ def main():
     ap.add_argument("--workload", default="gqa-4x8k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--doclen-cap", type=int, default=-1,
-                    help="dS store capacity as the longest document; 0: no store, dQ rebuilds "
-                         "dS-hat.  Default: the row length at d = 128, where reading the stored "
-                         "blocks is faster on MI355X, and no store at d = 64, where rebuilding is")
+    ap.add_argument("--doclen-cap", type=int, default=0,
+                    help="dS store capacity as the longest document; 0 (default): no store, the "
+                         "dQ pass rebuilds dS-hat (and quantizes dO), which is the faster path on "
+                         "MI355X at both head dimensions")
     ap.add_argument("--hadamard", type=int, default=0, choices=(0, 1),
                     help="1: Hadamard rotation of Q and K before quantization (the pages' default at d = 128)")
     ap.add_argument("--inference", type=int, default=-1, choices=(-1, 0, 5, 8),
@@ -261,8 +261,7 @@ def main():
     dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v, do = (dev(inst[n]) for n in ("q", "k", "v", "do"))
     cu = torch.from_numpy(inst["cu_seqlens"]).cuda()
-    # dS store sized for the longest possible document (a whole row), at d = 128
-    doclen_cap = (wl.row_len if d == 128 else 0) if args.doclen_cap < 0 else args.doclen_cap
+    doclen_cap = args.doclen_cap
     opts = F.flamia_default_opts()
     opts.hadamard = args.hadamard
     opts.mixed = args.mixed

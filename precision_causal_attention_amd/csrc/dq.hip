@@ -45,8 +45,10 @@ struct DqSmem {
     alignas(16) uint8_t kn[MIX ? kTile * kNStride : 16];
 };
 
+// At least two workgroups per CU at both head dimensions (at d = 128 one wave
+// per SIMD left latencies exposed: 36% longer).
 template <int D, int MIX, bool FUSED>
-__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) dq_kernel(const DqArgs a) {
+__global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
     constexpr int KC = D / 64;
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;

@@ -57,8 +57,12 @@ __device__ __forceinline__ constexpr int pair_class(int i) {
     return ((i >> 1) & 1) | (((i >> 2) & 1) << 1) | (((i >> 3) & 1) << 2);
 }
 
+// At least two workgroups per CU (two waves per SIMD) at both head
+// dimensions: at d = 128 one wave per SIMD leaves the matrix-core and memory
+// latencies exposed (the kernel ran 35% longer), and the few registers the
+// mixed and inference variants spill cost less than that.
 template <int D, int ROWSUM, int FAST, int MIX>
-__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fwd_kernel(const FwdArgs a) {
+__global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
     constexpr int KC = D / 64;                    // 64-channel contraction steps of S
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;                    // 32-row channel tiles of O^T
