@@ -431,16 +431,14 @@ static void launch_bwd_mix(const BwdArgs& a, dim3 g, hipStream_t st) {
 
 hipError_t launch_bwd(const BwdArgs& a, int d, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
+    // d = 128: eight-wave workgroups that split each step between wave pairs
+    // (bwd_split.hip)
+    if (d != 64) return launch_bwd_split(a, grid, st);
     // the store variant only where the workspace has a dS store
     const bool store = a.ds_blocks > 0;
     const dim3 g((unsigned)grid);
-    if (d == 64) {
-        if (store) launch_bwd_mix<64, true>(a, g, st);
-        else launch_bwd_mix<64, false>(a, g, st);
-    } else {
-        if (store) launch_bwd_mix<128, true>(a, g, st);
-        else launch_bwd_mix<128, false>(a, g, st);
-    }
+    if (store) launch_bwd_mix<64, true>(a, g, st);
+    else launch_bwd_mix<64, false>(a, g, st);
     return hipGetLastError();
 }
 

@@ -1,0 +1,416 @@
+// Key-major dK/dV pass of the causal backward at head dimension 128 (FLAMIA
+// paper: Section 2 equations dV = P^T dO, dP = dO V^T, dS = P o (dP - D),
+// dK = dS^T Q; Section 3.3 consistency with the forward; Appendix B.1 dV
+// operand E4M3(2^8 P)).  The arithmetic is that of the d = 64 kernel in
+// bwd.hip, value for value; only the division of the work differs.
+//
+// At d = 128 a wave that owns 32 keys holds their dK and dV accumulators over
+// all 128 channels (128 registers) next to its S and dP tiles, which leaves
+// one wave per SIMD and the latencies exposed.  Here a workgroup has eight
+// waves and waves w and w + 4 share keys 32w .. 32w + 31 of the 128-key tile:
+// for each 64-query step, wave half hf = wave / 4
+//   - computes S, dP, P, P-hat_b, dS and the dS-hat block of queries
+//     32 hf .. 32 hf + 31 (one 32x32 block: its exponent needs no exchange),
+//   - writes its P-hat_b and dS-hat codes and the block exponent to LDS, and
+//     after a barrier reads its partner's,
+//   - accumulates dV and dK for channels 64 hf .. 64 hf + 63 over all 64
+//     queries (the MFMA contracts over the two blocks at once).
+// With half the accumulators a wave fits two per SIMD.  The Hadamard
+// back-rotation of dK runs channel bits 0-5 inside the wave and bit 6 across
+// the pair through LDS, in the same order as the unsplit kernel.
+#include <type_traits>
+
+#include "device.h"
+#include "kernels.h"
+
+namespace flamia {
+
+namespace {
+
+constexpr int kSD = 128;                  // head dimension of this kernel
+constexpr int kSStep = 64;                // queries per step
+
+template <int MIX>
+struct SplitStep {
+    static constexpr int kStride = kSD + 16;       // row pitch of code tiles
+    static constexpr int kNStride = 2 * kSD + 16;  // row pitch of the bf16 NVFP4 rows (mixed path)
+    uint8_t q[kSStep * kStride];
+    uint8_t o[kSStep * kStride];                    // quantized dO
+    alignas(16) float lse[kSStep];
+    alignas(16) float dv[kSStep];                   // -D
+    uint8_t eq[kSStep];
+    uint8_t eo[kSStep];
+    alignas(16) uint8_t qn[MIX ? kSStep * kNStride : 16];
+};
+
+// Codes a wave hands to its partner each step: per lane 4 words of P-hat_b
+// and 4 of dS-hat (the lane's accumulator registers), plus the block exponent.
+struct SplitXchg {
+    u32x4 pb[8][64];
+    u32x4 db[8][64];
+    int es[8];
+};
+
+template <int MIX>
+struct SplitSmem {
+    union {
+        struct {
+            SplitStep<MIX> buf[2];   // ring: step i fills buffer i % 2
+            SplitXchg x;
+        } loop;
+        float rot[4][2][16][64];     // epilogue: dK tiles of the waves 4 .. 7 or 0 .. 3
+    };
+};
+
+}  // namespace
+
+template <bool STORE, int MIX>
+__global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
+    constexpr int D = kSD;
+    constexpr int KC = D / 64;
+    constexpr int NC = D / 16;
+    constexpr int DTH = 2;                        // 32-channel tiles of dK / dV per wave
+    constexpr int STR = SplitStep<MIX>::kStride;
+    constexpr int NSTR = SplitStep<MIX>::kNStride;
+    constexpr int NQ = kSStep * D / 16 / 512;     // 16-byte chunks per thread of a 64-row code tile
+    constexpr int NQN = MIX ? 2 * NQ : 1;
+    __shared__ SplitSmem<MIX> sm;
+
+    const int ti = (int)blockIdx.x / a.hkv;
+    if (ti >= *a.ntiles) return;
+    const int4 it = a.tiles[ti];
+    const int k0 = it.x, ds = it.y, de = it.z, doc = it.w;
+    const int g = (int)blockIdx.x - ti * a.hkv;
+    const bool use_store = STORE && a.ntiles[1] != 0;
+    const long doc_blk = use_store ? (long)a.dboff[doc] : 0;
+    const int G = a.hq / a.hkv;
+    const int L = de - ds;
+    const int kt0 = k0 - ds;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int kw = wave_u & 3;                    // key group of the pair
+    const int hf = wave_u >> 2;                   // query block of S / channel half of dK, dV
+    const int lg = lane >> 5, lr = lane & 31;
+    const int key_loc = kt0 + 32 * kw + lr;
+    const bool key_valid = key_loc < L;
+    const int key_row = ds + min(key_loc, L - 1);
+
+    // ---- staging of one 64-query step (prefetched into registers one step ahead)
+    u32x4 pq[NQ], po[NQ], pqn[NQN];
+    uint32_t p_eq = 0, p_eo = 0;
+    float p_lse = 0.f, p_dv = 0.f;
+    bool p_in = true;
+    auto load_step = [&](int h, int q0) {
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            const int c = tid + 512 * r;
+            const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+            const long qr = ds + min(q0 + row, L - 1);
+            pq[r] = *reinterpret_cast<const u32x4*>(a.qc + (qr * a.hq + h) * D + col);
+            po[r] = *reinterpret_cast<const u32x4*>(a.oc + (qr * a.hq + h) * D + col);
+        }
+        if constexpr (MIX) {
+#pragma unroll
+            for (int r = 0; r < NQN; ++r) {
+                const int c = tid + 512 * r;
+                const int row = c / (D / 8), col = (c % (D / 8)) * 8;   // col in bf16 elements
+                const long qr = ds + min(q0 + row, L - 1);
+                pqn[r] = *reinterpret_cast<const u32x4*>(a.qn + (qr * a.hq + h) * D + col);
+            }
+        }
+        const int ql = q0 + (tid & (kSStep - 1));
+        const long qr = ds + min(ql, L - 1);
+        p_eq = a.qs[(long)h * a.ttot + qr];
+        p_eo = a.os[(long)h * a.ttot + qr];
+        p_lse = a.lse2[(long)h * a.ttot + qr];
+        p_in = ql < L;
+        p_dv = a.dvec[(long)h * a.ttot + qr];
+    };
+    auto store_step = [&](SplitStep<MIX>& b) {
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            const int c = tid + 512 * r;
+            const int row = c / (D / 16), col = (c % (D / 16)) * 16;
+            *reinterpret_cast<u32x4*>(&b.q[row * STR + col]) = pq[r];
+            *reinterpret_cast<u32x4*>(&b.o[row * STR + col]) = po[r];
+        }
+        if constexpr (MIX) {
+#pragma unroll
+            for (int r = 0; r < NQN; ++r) {
+                const int c = tid + 512 * r;
+                const int row = c / (D / 8), col = (c % (D / 8)) * 16;   // col in bytes
+                *reinterpret_cast<u32x4*>(&b.qn[row * NSTR + col]) = pqn[r];
+            }
+        }
+        if (tid < kSStep) {
+            b.eq[tid] = (uint8_t)p_eq;
+            b.eo[tid] = (uint8_t)p_eo;
+            b.lse[tid] = p_in ? p_lse : INFINITY;   // +inf: row outside the document
+            b.dv[tid] = -p_dv;                       // -D: accumulator input of dP
+        }
+    };
+    load_step(g * G, kt0);
+
+    // The pair's key rows as B operands of S and dP (column = key, k = channel)
+    v8i kb[MIX ? 1 : KC], vb[KC];
+    u32x4 kn[MIX ? NC : 1];
+    {
+        const uint8_t* kp = a.kc + ((long)key_row * a.hkv + g) * D;
+        const uint8_t* vp = a.vc + ((long)key_row * a.hkv + g) * D;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            uint4 lo, hi;
+            if constexpr (!MIX) {
+                lo = *reinterpret_cast<const uint4*>(kp + 64 * kc + 16 * lg);
+                hi = *reinterpret_cast<const uint4*>(kp + 64 * kc + 32 + 16 * lg);
+                kb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+            lo = *reinterpret_cast<const uint4*>(vp + 64 * kc + 16 * lg);
+            hi = *reinterpret_cast<const uint4*>(vp + 64 * kc + 32 + 16 * lg);
+            vb[kc] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        if constexpr (MIX) {
+            const uint16_t* np = a.kn + ((long)key_row * a.hkv + g) * D;
+#pragma unroll
+            for (int kc = 0; kc < NC; ++kc) kn[kc] = *reinterpret_cast<const u32x4*>(np + 16 * kc + 8 * lg);
+        }
+    }
+    const int ek = MIX ? 127 : a.ks[(long)g * a.ttot + key_row];
+    const int ev = a.vs[(long)g * a.ttot + key_row];
+
+    v16f dvt[DTH], dkt[DTH];                      // channel tiles 2 hf, 2 hf + 1
+#pragma unroll
+    for (int t = 0; t < DTH; ++t) { dvt[t] = v16f{0}; dkt[t] = v16f{0}; }
+
+    const int s16 = lane & 15, grp = (lane >> 4) & 1;
+    const int tr_key = 8 * ((s16 >> 1) >> 2) + 4 * lg + ((s16 >> 1) & 3);
+    const int tr_col = 16 * grp + 8 * (s16 & 1);
+    const float inv256 = 1.f / 256.f;
+
+    int cur = 0;
+    int hh = 0, q0 = kt0;
+    // this wave's dS block of the previous step, stored at the start of the next one
+    u32x4 pend_w = u32x4{0, 0, 0, 0};
+    long pend_blk = 0;
+    int pend_e = 127;
+    bool pend_ok = false;
+    auto flush_store = [&]() {
+        if (!use_store || !pend_ok) return;
+        *reinterpret_cast<u32x4*>(a.ds_codes + pend_blk * kDsBlockBytes + 16 * lane) = pend_w;
+        if (lane == 0) a.ds_scales[pend_blk] = (uint8_t)pend_e;
+        pend_ok = false;
+    };
+    // One 64-query step; MASK marks the steps that meet the causal boundary
+    // (the first two of every head, starting at the diagonal).
+    auto step = [&](auto mask_tag) -> bool {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        SplitStep<MIX>& B = sm.loop.buf[cur];
+        store_step(B);
+        __syncthreads();
+        const int h = g * G + hh;
+        const int qs0 = q0;
+        q0 += kSStep;
+        if (q0 >= L) { q0 = kt0; ++hh; }
+        const bool more = hh < G;
+        flush_store();
+        load_step(g * G + min(hh, G - 1), q0);
+
+        // the step's 32-query blocks are blocks qb0 and qb0 + 1 of the key
+        // tile's diagonal: a block before the pair's keys is skipped (P = 0),
+        // the block on it is masked
+        const int qb0 = (qs0 - kt0) >> 5;
+        const bool skip = MASK && qb0 + hf < kw;
+        const bool part = MASK && qb0 + hf == kw;
+        const bool skip1 = MASK && qb0 + 1 < kw;  // the step's second block skipped: both are
+        int pbc[4] = {0, 0, 0, 0}, dsc[4] = {0, 0, 0, 0}, es = 127;
+        if (!skip) {
+            // ---- S and dP for the pair's 32 keys x the wave's 32 queries
+            const int row = 32 * hf + lr;
+            v16f sacc = v16f{0}, pacc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 d4 = *reinterpret_cast<const float4*>(&B.dv[32 * hf + 8 * j + 4 * lg]);
+                pacc[4 * j] = d4.x;
+                pacc[4 * j + 1] = d4.y;
+                pacc[4 * j + 2] = d4.z;
+                pacc[4 * j + 3] = d4.w;
+            }
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                if constexpr (MIX) {
+#pragma unroll
+                    for (int n = 4 * kc; n < 4 * kc + 4; ++n) {
+                        const u32x4 qa = *reinterpret_cast<const u32x4*>(&B.qn[row * NSTR + 32 * n + 16 * lg]);
+                        sacc = mfma_bf16(qa, kn[n], sacc);
+                    }
+                } else {
+                    const uint4 lo = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 16 * lg]);
+                    const uint4 hi = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 32 + 16 * lg]);
+                    const v8i qa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    sacc = mfma_mx(qa, kb[kc], sacc, B.eq[row], ek);
+                }
+                const uint4 lo = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 16 * lg]);
+                const uint4 hi = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 32 + 16 * lg]);
+                const v8i oa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                pacc = mfma_mx(oa, vb[kc], pacc, B.eo[row], ev);
+            }
+            // ---- P, P-hat_b, dS, dS-hat; register i = 4j + r holds query
+            // qs0 + 32 hf + 8j + 4lg + r, masked while the key lies after it
+            const int lim = key_loc - qs0 - 32 * hf - 4 * lg;
+            float amax = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 l4 = *reinterpret_cast<const float4*>(&B.lse[32 * hf + 8 * j + 4 * lg]);
+                const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * j + r;
+                    float p = exp2_fast(fmaf(sacc[i], a.c1, -lq[r]));
+                    if (part)
+                        if (8 * j + r < lim) p = 0.f;
+                    sacc[i] = p;
+                    pacc[i] = p * pacc[i];
+                    amax = fmaxf(amax, fabsf(pacc[i]));
+                }
+            }
+            amax = wave_max_nonneg(amax);
+            const int e = block_exponent_uniform(amax, -126);
+            es = e + 127;
+            const float sc = __uint_as_float((uint32_t)(e + 127) << 23);   // 2^e
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pbc[j] = pack_fp8x4_div(sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3], inv256);
+                dsc[j] = pack_fp8x4_div(pacc[4 * j], pacc[4 * j + 1], pacc[4 * j + 2], pacc[4 * j + 3], sc);
+            }
+        }
+        // ---- dS store: this wave's block (qb, kb) as [query half][32 keys][16 queries]
+        if (use_store) {
+            const int qb = (qs0 >> 5) + hf, kb = (kt0 >> 5) + kw;
+            pend_ok = !skip && qs0 + 32 * hf < L;
+            pend_blk = (long)h * a.ds_blocks + doc_blk + (long)qb * (qb + 1) / 2 + kb;
+            const auto x02 = __builtin_amdgcn_permlane32_swap(dsc[0], dsc[2], false, false);
+            const auto x13 = __builtin_amdgcn_permlane32_swap(dsc[1], dsc[3], false, false);
+            pend_w = u32x4{(uint32_t)x02[0], (uint32_t)x02[1], (uint32_t)x13[0], (uint32_t)x13[1]};
+            pend_e = es;
+        }
+        // ---- exchange with the partner wave, then dV^T += dO^T P-hat_b and
+        // dK^T += Q^T dS-hat for the wave's channel half over the 64 queries
+        sm.loop.x.pb[wave_u][lane] = u32x4{(uint32_t)pbc[0], (uint32_t)pbc[1], (uint32_t)pbc[2], (uint32_t)pbc[3]};
+        sm.loop.x.db[wave_u][lane] = u32x4{(uint32_t)dsc[0], (uint32_t)dsc[1], (uint32_t)dsc[2], (uint32_t)dsc[3]};
+        if (lane == 0) sm.loop.x.es[wave_u] = es;
+        __syncthreads();
+        if (!skip1) {
+            const int pw = wave_u ^ 4;
+            const u32x4 ppb = sm.loop.x.pb[pw][lane], pdb = sm.loop.x.db[pw][lane];
+            const int pes = sm.loop.x.es[pw];
+            // block 0 of the contraction is wave half 0's, block 1 wave half 1's
+            const u32x4 b0 = hf ? ppb : u32x4{(uint32_t)pbc[0], (uint32_t)pbc[1], (uint32_t)pbc[2], (uint32_t)pbc[3]};
+            const u32x4 b1 = hf ? u32x4{(uint32_t)pbc[0], (uint32_t)pbc[1], (uint32_t)pbc[2], (uint32_t)pbc[3]} : ppb;
+            const u32x4 d0 = hf ? pdb : u32x4{(uint32_t)dsc[0], (uint32_t)dsc[1], (uint32_t)dsc[2], (uint32_t)dsc[3]};
+            const u32x4 d1 = hf ? u32x4{(uint32_t)dsc[0], (uint32_t)dsc[1], (uint32_t)dsc[2], (uint32_t)dsc[3]} : pdb;
+            const v8i pb = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            const v8i db = v8i{(int)d0.x, (int)d0.y, (int)d0.z, (int)d0.w, (int)d1.x, (int)d1.y, (int)d1.z, (int)d1.w};
+            const int e0 = hf ? pes : es, e1 = hf ? es : pes;
+            const int so = B.eo[32 * lg], sq = B.eq[32 * lg];
+            const int sd = lg ? e1 : e0;
+#pragma unroll
+            for (int t = 0; t < DTH; ++t) {
+                const int dt = 2 * hf + t;
+                v2i r[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    r[rr] = lds_read_tr8(&B.o[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                const v8i oa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+                dvt[t] = mfma_mx(oa, pb, dvt[t], so, 127 - 8);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    r[rr] = lds_read_tr8(&B.q[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                const v8i qa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+                dkt[t] = mfma_mx(qa, db, dkt[t], sq, sd);
+            }
+        }
+        cur ^= 1;
+        return more;
+    };
+    bool more = true;
+    while (more) {
+        while (more && q0 < kt0 + kTile) more = step(std::true_type{});
+        while (more && q0 >= kt0 + kTile) more = step(std::false_type{});
+    }
+    flush_store();
+    // ---- epilogue: dK = softmax_scale * sum (rotated back with the Hadamard
+    // option: channel bits 0-5 in the wave, bit 6 with the partner), dV
+    float sck = a.scale;
+    if (a.hadamard) {
+        hadamard_rows<DTH>(dkt, lg);
+        sck *= inv_sqrt_d<D>();
+        // channel bit 6: (x_lo, x_hi) -> (x_lo + x_hi, x_lo - x_hi); wave half
+        // 0 holds x_lo, half 1 x_hi.  The loop's buffers are no longer read
+        // once every wave is past this barrier.
+        __syncthreads();
+        float (&rt)[4][2][16][64] = sm.rot;
+        if (hf == 1)
+#pragma unroll
+            for (int t = 0; t < DTH; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) rt[kw][t][i][lane] = dkt[t][i];
+        __syncthreads();
+        v16f hi_in[DTH];
+        if (hf == 0) {
+#pragma unroll
+            for (int t = 0; t < DTH; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) hi_in[t][i] = rt[kw][t][i][lane];
+        }
+        __syncthreads();
+        if (hf == 0)
+#pragma unroll
+            for (int t = 0; t < DTH; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) rt[kw][t][i][lane] = dkt[t][i];
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < DTH; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (hf == 0) {
+                    dkt[t][i] = dkt[t][i] + hi_in[t][i];
+                } else {
+                    const float lo = rt[kw][t][i][lane];
+                    dkt[t][i] = lo - dkt[t][i];
+                }
+            }
+    }
+    if (key_valid) {
+        uint16_t* kp = a.dk + ((long)(ds + key_loc) * a.hkv + g) * D;
+        uint16_t* vp = a.dv + ((long)(ds + key_loc) * a.hkv + g) * D;
+#pragma unroll
+        for (int t = 0; t < DTH; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int dd = 32 * (2 * hf + t) + 8 * j + 4 * lg;
+                *reinterpret_cast<uint2*>(kp + dd) = make_uint2(
+                    pack_bf16x2(dkt[t][4 * j] * sck, dkt[t][4 * j + 1] * sck),
+                    pack_bf16x2(dkt[t][4 * j + 2] * sck, dkt[t][4 * j + 3] * sck));
+                *reinterpret_cast<uint2*>(vp + dd) = make_uint2(
+                    pack_bf16x2(dvt[t][4 * j], dvt[t][4 * j + 1]),
+                    pack_bf16x2(dvt[t][4 * j + 2], dvt[t][4 * j + 3]));
+            }
+    }
+}
+
+hipError_t launch_bwd_split(const BwdArgs& a, long grid, hipStream_t st) {
+    if (grid <= 0) return hipSuccess;
+    const bool store = a.ds_blocks > 0;
+    const dim3 g((unsigned)grid), b(512);
+    if (a.qn) {
+        if (store) hipLaunchKernelGGL((bwd_split_kernel<true, 1>), g, b, 0, st, a);
+        else hipLaunchKernelGGL((bwd_split_kernel<false, 1>), g, b, 0, st, a);
+    } else {
+        if (store) hipLaunchKernelGGL((bwd_split_kernel<true, 0>), g, b, 0, st, a);
+        else hipLaunchKernelGGL((bwd_split_kernel<false, 0>), g, b, 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace flamia
