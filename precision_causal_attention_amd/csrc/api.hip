@@ -73,7 +73,7 @@ Layout layout(const flamia_dims_t* d) {
     w.max_cost = (int)((tc + kTile - 1) / kTile) + 1;
     w.max_tiles = tc / kTile + d->ndocs_cap + 1;
     size_t off = 0;
-    w.ctrl = off;    off += up256(sizeof(int32_t) * (16 + 2 * (size_t)(w.max_cost + 1)));
+    w.ctrl = off;    off += up256(sizeof(int32_t) * 16);
     w.prefix = off;  off += up256(sizeof(int32_t) * ((size_t)d->ndocs_cap + 1));
     w.tiles_q = off; off += up256(sizeof(int4) * (size_t)w.max_tiles);
     w.tiles_k = off; off += up256(sizeof(int4) * (size_t)w.max_tiles);

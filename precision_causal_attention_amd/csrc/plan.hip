@@ -16,33 +16,54 @@
 // workgroup index, heads innermost.
 //
 // ctrl layout (int32): [0] number of tiles, [1] 1 if the backward's dS store
-// holds this call's blocks (capacity given and not exceeded), else 0,
-// [16, 16+C1) query-major cursors, [16+C1, 16+2 C1) key-major cursors
-// (C1 = max_cost + 1).  The dS block offsets of the documents go to dboff.
+// holds this call's blocks (capacity given and not exceeded), else 0.  The
+// placement cursors of the cost classes live in LDS.  The dS block offsets of
+// the documents go to dboff.
 #include "device.h"
 #include "kernels.h"
 
 namespace flamia {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kPrefixLds = 4096;          // documents whose tile prefix is kept in LDS
 
-// In-place inclusive scan of buf[0..n) in LDS by a 1024-thread block;
-// reverse = true scans from the end (suffix sums).
-__device__ void block_scan(int* buf, int n, bool reverse, int* partial) {
+// Inclusive scan of one value per thread over the block: a shuffle scan in
+// each wave, then the wave totals (integer sums: the result does not depend
+// on the order).  Returns this thread's inclusive prefix; `total` gets the
+// block's sum.  Two barriers; wsum is free again on return.
+template <typename V>
+__device__ V block_incl_scan(V v, V* wsum, V& total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const V t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+    }
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    V before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanWaves; ++i) {
+        const V x = wsum[i];
+        if (i < w) before += x;
+        tot += x;
+    }
+    __syncthreads();
+    total = tot;
+    return v + before;
+}
+
+// In-place inclusive scan of buf[0..n) in LDS; reverse = true scans from the
+// end (suffix sums).  Each thread owns one contiguous chunk.
+__device__ void block_scan(int* buf, int n, bool reverse, int* wsum) {
     const int tid = threadIdx.x;
     const int chunk = (n + kPlanThreads - 1) / kPlanThreads;
     const int lo = tid * chunk, hi = min(lo + chunk, n);
     int sum = 0;
     for (int i = lo; i < hi; ++i) sum += buf[reverse ? n - 1 - i : i];
-    partial[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        const int v = tid >= off ? partial[tid - off] : 0;
-        __syncthreads();
-        partial[tid] += v;
-        __syncthreads();
-    }
-    int run = tid > 0 ? partial[tid - 1] : 0;
+    int total;
+    int run = block_incl_scan(sum, wsum, total) - sum;
     for (int i = lo; i < hi; ++i) {
         const int j = reverse ? n - 1 - i : i;
         run += buf[j];
@@ -56,11 +77,15 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __
             int32_t* __restrict__ ctrl, long max_tiles, int4* __restrict__ tiles_q, int4* __restrict__ tiles_k,
             int32_t* __restrict__ dboff, long ds_blocks) {
     extern __shared__ int smem[];
-    int* partial = smem;                       // kPlanThreads
-    int* hist = smem + kPlanThreads;           // max_cost + 1
-    const int tid = threadIdx.x;
     const int C1 = max_cost + 1;
-    for (int c = tid; c < C1; c += kPlanThreads) hist[c] = 0;
+    int* hist = smem;                          // C1: tile counts by cost class
+    int* curq = smem + C1;                     // C1: query-major placement cursors
+    int* curk = smem + 2 * C1;                 // C1: key-major placement cursors
+    __shared__ int wsum[kPlanWaves];
+    __shared__ long lwsum[kPlanWaves];
+    __shared__ int lpref[kPrefixLds];          // tile prefix of the documents (ndocs < kPrefixLds)
+    const int tid = threadIdx.x;
+    for (int c = tid; c < C1; c += kPlanThreads) hist[c] = curq[c] = curk[c] = 0;
     __syncthreads();
     for (int d = tid; d < ndocs; d += kPlanThreads) {
         const int L = cu[d + 1] - cu[d];
@@ -69,41 +94,34 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __
     }
     __syncthreads();
     // hist[c] = #docs with n >= c = number of tiles of cost c (c >= 1)
-    block_scan(hist, C1, true, partial);
+    block_scan(hist, C1, true, wsum);
     // hist[c] = number of tiles of cost >= c; the class of cost c starts at
     // hist[c + 1] (classes by decreasing cost) and hist[1] is the total
-    block_scan(hist, C1, true, partial);
+    block_scan(hist, C1, true, wsum);
     const int total = C1 > 1 ? (int)min((long)hist[1], max_tiles) : 0;
-    for (int c = tid; c < C1; c += kPlanThreads) {
-        ctrl[16 + c] = 0;                      // query-major cursors
-        ctrl[16 + C1 + c] = 0;                 // key-major cursors
-    }
     if (tid == 0) ctrl[0] = total;
     // exclusive prefix of tile counts over documents
+    const bool lds_pref = ndocs < kPrefixLds;
     {
         const int chunk = (ndocs + kPlanThreads - 1) / kPlanThreads;
         const int lo = tid * chunk, hi = min(lo + chunk, ndocs);
         int sum = 0;
         for (int d = lo; d < hi; ++d) sum += (cu[d + 1] - cu[d] + kTile - 1) / kTile;
-        partial[tid] = sum;
-        __syncthreads();
-        for (int o = 1; o < kPlanThreads; o <<= 1) {
-            const int v = tid >= o ? partial[tid - o] : 0;
-            __syncthreads();
-            partial[tid] += v;
-            __syncthreads();
-        }
-        int run = tid > 0 ? partial[tid - 1] : 0;
+        int all;
+        int run = block_incl_scan(sum, wsum, all) - sum;
         for (int d = lo; d < hi; ++d) {
             tiles_prefix[d] = run;
+            if (lds_pref) lpref[d] = run;
             run += (cu[d + 1] - cu[d] + kTile - 1) / kTile;
         }
-        if (tid == kPlanThreads - 1) tiles_prefix[ndocs] = partial[kPlanThreads - 1];
+        if (tid == 0) {
+            tiles_prefix[ndocs] = all;
+            if (lds_pref) lpref[ndocs] = all;
+        }
     }
     // dS store: first causal 32x32 block of each document (nb (nb + 1) / 2
     // blocks for nb = ceil(L / 32)), and whether the call fits the capacity
     if (dboff) {
-        __syncthreads();
         const int chunk = (ndocs + kPlanThreads - 1) / kPlanThreads;
         const int lo = tid * chunk, hi = min(lo + chunk, ndocs);
         long sum = 0;
@@ -111,18 +129,9 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __
             const long nb = (cu[d + 1] - cu[d] + kBlock - 1) / kBlock;
             sum += nb * (nb + 1) / 2;
         }
-        __shared__ long lpartial[kPlanThreads];
-        lpartial[tid] = sum;
-        __syncthreads();
-        for (int o = 1; o < kPlanThreads; o <<= 1) {
-            const long v = tid >= o ? lpartial[tid - o] : 0;
-            __syncthreads();
-            lpartial[tid] += v;
-            __syncthreads();
-        }
-        const long total_blocks = lpartial[kPlanThreads - 1];
+        long total_blocks;
+        long run = block_incl_scan(sum, lwsum, total_blocks) - sum;
         const bool fits = ds_blocks > 0 && total_blocks <= ds_blocks;
-        long run = tid > 0 ? lpartial[tid - 1] : 0;
         for (int d = lo; d < hi; ++d) {
             dboff[d] = fits ? (int32_t)run : 0;
             const long nb = (cu[d + 1] - cu[d] + kBlock - 1) / kBlock;
@@ -132,31 +141,47 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __
     } else if (tid == 0) {
         ctrl[1] = 0;
     }
-    // the cursor zeros and the prefix table must have reached L2 before any
-    // thread of the workgroup uses them
-    __threadfence();
+    // the prefix table (LDS, or global beyond kPrefixLds documents, which then
+    // must have reached L2) is complete for every thread
+    if (!lds_pref) __threadfence();
     __syncthreads();
-    for (int p = tid; p < total; p += kPlanThreads) {
-        const int doc = find_doc(tiles_prefix, ndocs, p);
-        const int t = p - tiles_prefix[doc];
-        const int n = tiles_prefix[doc + 1] - tiles_prefix[doc];
+    // tile p, the t-th of the n tiles of document doc, whose first tile is pre
+    auto place = [&](int p, int doc, int pre, int next) {
+        const int t = p - pre;
+        const int n = next - pre;
         const int ds = cu[doc], de = cu[doc + 1];
         const int4 tile = make_int4(ds + kTile * t, ds, de, doc);
         {
             const int cost = t + 1;
-            const int slot = (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&ctrl[16 + cost], 1);
+            const int slot = (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&curq[cost], 1);
             if (slot < max_tiles) tiles_q[slot] = tile;
         }
         if (tiles_k) {
             const int cost = n - t;
-            const int slot = (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&ctrl[16 + C1 + cost], 1);
+            const int slot = (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&curk[cost], 1);
             if (slot < max_tiles) tiles_k[slot] = tile;
+        }
+    };
+    if (lds_pref) {
+        for (int p = tid; p < total; p += kPlanThreads) {
+            // the document of tile p: binary search of the LDS prefix
+            int lo = 0, hi = ndocs - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (lpref[mid] <= p) lo = mid; else hi = mid - 1;
+            }
+            place(p, lo, lpref[lo], lpref[lo + 1]);
+        }
+    } else {
+        for (int p = tid; p < total; p += kPlanThreads) {
+            const int doc = find_doc(tiles_prefix, ndocs, p);
+            place(p, doc, tiles_prefix[doc], tiles_prefix[doc + 1]);
         }
     }
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
-    const size_t smem = sizeof(int) * (kPlanThreads + a.max_cost + 1);
+    const size_t smem = sizeof(int) * 3 * ((size_t)a.max_cost + 1);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), smem, st, a.cu, a.ndocs, a.max_cost,
                        a.tiles_prefix, a.ctrl, a.max_tiles, a.tiles_q, a.tiles_k, a.dboff, a.ds_blocks);
     return hipGetLastError();
