@@ -7,6 +7,9 @@
 - the largest call the library accepts: 2^20 tokens (the token capacity),
   thousands of documents from 1 token up, compared on a sample of documents
   that includes the first, the last and the longest;
+- more documents than the work-list kernel keeps in LDS (5000 documents of
+  1 to 40 tokens: the document search then reads the prefix table in global
+  memory), every document compared;
 - the long-document d = 128 workload (1 x 32768, 16 heads) in the benchmark's
   launch configuration (no dS store: the dQ pass rebuilds dS-hat and
   quantizes dO), compared on one head over every document but the longest.
@@ -92,6 +95,18 @@ def test_maximum_size_call(orc):
     r = _oracle(orc, inst, doc_mask=mask)
     rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in pick])
     _check_rows(g, r, rows)
+
+
+def test_many_short_documents(orc):
+    rng = np.random.default_rng(93)
+    lens = [int(x) for x in rng.integers(1, 41, size=5000)]
+    inst = W.generate(W.custom("many", lens, 2, 1, 64), 9, lens=lens)
+    say(f"[many documents] docs={len(lens)} T={sum(lens)}")
+    r = _oracle(orc, inst)
+    for cap in (0, None):                                  # without and with the dS store
+        say(f"  doclen_cap={cap}")
+        g = run_hip(inst, doclen_cap=cap)
+        _check_rows(g, r, slice(None))
 
 
 def test_long_32k_d128_sampled_head(orc):
