@@ -26,7 +26,8 @@ class Workload:
     hq: int
     hkv: int
     d: int
-    docs: str                 # "single" | "uniform:<n>:<min>" | "lognormal:<median>:<sigma>:<lo>"
+    docs: str                 # "single" | "uniform:<n>:<min>" | "lognormal:<median>:<sigma>:<lo>" |
+                              # "equal:<n>" | "skewed:<big>:<n>:<small>" | "loguniform:<n>:<lo>:<hi>"
     do_std: float = 1.0
     outlier_frac: float = 0.0  # fraction of (head, channel) pairs of Q and K scaled
     outlier_gain: float = 1.0
@@ -53,7 +54,22 @@ WORKLOADS = {
     # the mixed NVFP4/FP8 path's workload: one row of 8192, 16 heads, d = 128,
     # lognormal documents (median 1024, sigma 1) clipped to [32, 8192]
     "mixed-8k": Workload("mixed-8k", 1, 8192, 16, 16, 128, "lognormal:1024:1.0:32"),
+    # the paper's nine packed causal workloads (Section 4.1): one row, 16
+    # query heads, d = 128, MHA unless marked GQA 16/4
+    "eq-4x4096": Workload("eq-4x4096", 1, 4 * 4096, 16, 16, 128, "equal:4"),
+    "eq-16x4096": Workload("eq-16x4096", 1, 16 * 4096, 16, 16, 128, "equal:16"),
+    "eq-16x1024": Workload("eq-16x1024", 1, 16 * 1024, 16, 16, 128, "equal:16"),
+    "eq-64x1024": Workload("eq-64x1024", 1, 64 * 1024, 16, 16, 128, "equal:64"),
+    "skew-8k+32x256": Workload("skew-8k+32x256", 1, 8192 + 32 * 256, 16, 16, 128, "skewed:8192:32:256"),
+    "skew-8k+224x256": Workload("skew-8k+224x256", 1, 8192 + 224 * 256, 16, 16, 128, "skewed:8192:224:256"),
+    "logu-11x16k": Workload("logu-11x16k", 1, 16384, 16, 16, 128, "loguniform:11:128:8192"),
+    "logu-11x16k-gqa": Workload("logu-11x16k-gqa", 1, 16384, 16, 4, 128, "loguniform:11:128:8192"),
+    "logu-29x64k": Workload("logu-29x64k", 1, 65536, 16, 16, 128, "loguniform:29:128:8192"),
 }
+
+# the paper's nine packed causal workloads, in the order of its Table 1
+PAPER_WORKLOADS = ["eq-4x4096", "eq-16x4096", "eq-16x1024", "eq-64x1024", "skew-8k+32x256",
+                   "skew-8k+224x256", "logu-11x16k", "logu-11x16k-gqa", "logu-29x64k"]
 
 
 def _row_lengths(rng: np.random.Generator, row_len: int, spec: str) -> list[int]:
@@ -81,7 +97,49 @@ def _row_lengths(rng: np.random.Generator, row_len: int, spec: str) -> list[int]
                 out.append(L)
             room -= L
         return out
+    if kind == "equal":
+        n = int(args[0])
+        return [row_len // n] * n
+    if kind == "skewed":
+        # one long document first, then the short ones
+        big, n, small = int(args[0]), int(args[1]), int(args[2])
+        return [big] + [small] * n
+    if kind == "loguniform":
+        # n lengths drawn log-uniformly in [lo, hi], scaled to fill the row,
+        # rounded and kept in [lo, hi]; the rounding remainder goes to the
+        # documents with room for it, longest first
+        n, lo, hi = int(args[0]), int(args[1]), int(args[2])
+        x = np.exp(rng.uniform(math.log(lo), math.log(hi), size=n))
+        L = np.clip(np.rint(x * row_len / x.sum()), lo, hi).astype(np.int64)
+        order = np.argsort(-L, kind="stable")
+        k = 0
+        while L.sum() != row_len:
+            i = order[k % n]
+            if L.sum() < row_len and L[i] < hi:
+                L[i] += min(hi - L[i], row_len - L.sum())
+            elif L.sum() > row_len and L[i] > lo:
+                L[i] -= min(L[i] - lo, L.sum() - row_len)
+            k += 1
+        return [int(v) for v in L]
     raise ValueError(f"unknown document law {spec!r}")
+
+
+def min_doc_len(wl: Workload) -> int:
+    """The shortest document the workload's law allows."""
+    kind, *args = wl.docs.split(":")
+    if kind == "single":
+        return wl.row_len
+    if kind == "uniform":
+        return int(args[1])
+    if kind == "lognormal":
+        return int(args[2])
+    if kind == "equal":
+        return wl.row_len // int(args[0])
+    if kind == "skewed":
+        return min(int(args[0]), int(args[2]))
+    if kind == "loguniform":
+        return int(args[1])
+    return 1
 
 
 def doc_lengths(wl: Workload, seed: int) -> list[int]:

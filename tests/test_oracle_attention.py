@@ -312,8 +312,7 @@ def test_workload_configs_are_valid():
         for seed in range(3):
             L = W.doc_lengths(wl, seed)
             assert sum(L) == wl.ttot
-            lo = 1 if wl.docs == "single" else int(wl.docs.split(":")[-1])
-            assert min(L) >= lo
+            assert min(L) >= W.min_doc_len(wl)
             # no document crosses a row
             edges = np.cumsum(L)
             for r in range(1, wl.rows):
