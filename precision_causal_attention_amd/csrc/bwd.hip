@@ -5,7 +5,8 @@
 // statistic, dS quantized on 32x32 document-local blocks from the block
 // maximum; Appendix B.1: the dV operand is E4M3(2^8 P) with no stored scale).
 //
-// Key-major dK/dV pass.  One workgroup = one work item (document,
+// Key-major dK/dV pass at d = 64 (d = 128: bwd_split.hip, same arithmetic in
+// wave pairs).  One workgroup = one work item (document,
 // key/value head, 128-key tile anchored at the document start); wave w owns
 // keys 32w..32w+31 of the tile.  For every query head of the group and every
 // 64-query step from the diagonal to the end of the document:
@@ -60,12 +61,13 @@ struct BwdSmem {
 };
 
 template <int D, bool STORE, int MIX>
-__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
     constexpr int KC = D / 64;
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;
     // The mixed path's bf16 operands take the registers the pipeline needs.
-    constexpr bool PIPE = D == 64 && !STORE && !MIX;
+    static_assert(D == 64, "d = 128 runs in bwd_split.hip");
+    constexpr bool PIPE = !STORE && !MIX;
     constexpr int NBUF = PIPE ? 3 : 2;
     constexpr int STR = BwdStep<D, MIX>::kStride;
     constexpr int NSTR = BwdStep<D, MIX>::kNStride;
@@ -210,11 +212,11 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) bwd_kernel(const BwdArgs
             dkt[dt] = mfma_mx(qa, db, dkt[dt], sq, sd);
         }
     };
-    // Software pipeline (d = 64, no dS store): the dV/dK products of a step are issued in
-    // the next step, right after its S and dP products, so that they run on
-    // the matrix cores while the wave computes the next softmax.  At d = 128
-    // the extra live codes cost an occupancy step, and with the store they
-    // spill, so the products follow their own step there.
+    // Software pipeline (MXFP8, no dS store): the dV/dK products of a step are
+    // issued in the next step, right after its S and dP products, so that they
+    // run on the matrix cores while the wave computes the next softmax.  With
+    // the store, or the mixed path's bf16 operands, the extra live codes spill,
+    // so the products follow their own step there.
     int cur = 0;                           // step buffer of the current step
     int prv = 0;                           // step buffer of the previous step
     bool dvdk_due = false;                 // the previous step's dV/dK products are pending
