@@ -68,7 +68,8 @@ BWD_PHASES_STORE = ["quantize_do", "worklist_bwd", "dkv_kernel", "dq_kernel"]
 BWD_PHASES_FUSED = ["worklist_bwd", "dq_kernel", "dkv_kernel"]
 CSRC = os.path.join(ROOT, "precision_causal_attention_amd", "csrc")
 # sources whose text decides each attention kernel's memory traffic
-KERNEL_SOURCES = {"fwd_kernel": ["fwd.hip"], "dkv_kernel": ["bwd.hip"], "dq_kernel": ["dq.hip", "dq_store.hip"]}
+KERNEL_SOURCES = {"fwd_kernel": ["fwd.hip"], "dkv_kernel": ["bwd.hip", "bwd_split.hip"],
+                  "dq_kernel": ["dq.hip", "dq_store.hip"]}
 COMMON_SOURCES = ["device.h", "kernels.h"]
 
 
@@ -136,8 +137,8 @@ def cpu_baseline(inst, hkv, hadamard=0, mixed=0, target_s=10.0):
     """The oracle as it stands on a sample of the workload: key/value head 0
     and its query heads (all documents) is timed first; while a call takes
     less than target_s, the sample doubles to the first n key/value heads (one
-    call each, at most three more) and the last call is reported.  Scaled to
-    TFLOP/s."""
+    call each, the whole workload at most) and the last call is reported.
+    Scaled to TFLOP/s."""
     import numpy as np
 
     import oracle
@@ -152,9 +153,7 @@ def cpu_baseline(inst, hkv, hadamard=0, mixed=0, target_s=10.0):
         return time.perf_counter() - t0
 
     n, dt = 1, run(1)
-    for _ in range(3):   # more heads also parallelize better: double, at most three more calls
-        if dt >= target_s or n >= hkv:
-            break
+    while dt < target_s and n < hkv:   # more heads also parallelize better: double
         n = min(hkv, 2 * n)
         dt = run(n)
     hq, d = inst["q"].shape[1], inst["q"].shape[2]
