@@ -10,8 +10,8 @@ Method: "FLAMIA: FLAsh MIcroscaling Attention for Fast and Causally Safe
 Training on Blackwell" -- Section 2 (attention forward/backward equations),
 Section 3.1 (token-block scaling), Section 3.2 (causally safe exponent),
 Section 3.3 (forward/backward consistency, 32x32 dS blocks), Section 3.6.1
-(document-local statistics) and Appendix B.1 (fixed 2^c P-hat factor,
-conditional running maximum, 2^8 backward P-hat).
+(document-local statistics), Appendix A.3 (the exact options) and Appendix B.1
+(fixed 2^c P-hat factor, conditional running maximum, 2^8 backward P-hat).
 """
 from __future__ import annotations
 
@@ -50,6 +50,7 @@ class _Params(ctypes.Structure):
         ("rowsum", ctypes.c_int32), ("softmax_scale", ctypes.c_double),
         ("unsafe_bound", ctypes.c_int32), ("score_rel_err", ctypes.c_double),
         ("hadamard", ctypes.c_int32), ("fast_exp", ctypes.c_int32), ("mixed", ctypes.c_int32),
+        ("exact", ctypes.c_int32),
     ]
 
 
@@ -109,12 +110,14 @@ class Opts:
     hadamard: int = 0            # 1: Hadamard rotation of Q and K (Section 3.4, Appendix A.2)
     fast_exp: int = 0            # k of 8 key-pair classes use Schraudolph's exponential (forward only)
     mixed: int = 0               # 1: scores from NVFP4 Q and K (Section 3.4 mixed path)
+    exact: int = 0               # 1: the exact options (Appendix A.3): per-token operand
+                                 # exponents, a per-query-row dS exponent for dQ
 
 
 def _params(ttot, ndocs, hq, hkv, d, opts: Opts) -> _Params:
     return _Params(ttot, ndocs, hq, hkv, d, opts.c_log2, opts.tau, opts.key_tile, opts.quant,
                    opts.rowsum, float(opts.softmax_scale), opts.unsafe_bound, float(opts.score_rel_err),
-                   opts.hadamard, opts.fast_exp, opts.mixed)
+                   opts.hadamard, opts.fast_exp, opts.mixed, opts.exact)
 
 
 def max_threads() -> int:

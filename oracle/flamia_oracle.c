@@ -38,7 +38,14 @@
  *   - the mixed path's NVFP4 Q and K: one E4M3 scale per 16 channels of each
  *     token, rounded up (the smallest with 6 s >= the group maximum), tensor
  *     scale 1 (a constant: no statistic over the sequence), E2M1 codes to
- *     nearest even; they serve the scores only.
+ *     nearest even; they serve the scores only;
+ *   - the exact options: per-token exponents (rounded up) for Q, K, V and dO;
+ *     a product that contracts over tokens takes the other operand's token
+ *     exponent into its 8-bit entry, relative to a shared exponent: the
+ *     largest V exponent of the visible keys of the 32-key block (P-hat), the
+ *     largest dO exponent of the 32-query block (P-hat_b), the 32x32 block
+ *     exponent of dS 2^eQ (dK), and one exponent per query row and 32-key
+ *     block of dS 2^eK (dQ).
  *
  * Parity: every exported function is pinned by CPU tests against definitions
  * that do not go through this file (a library FP8 codec, brute-force nearest
@@ -91,6 +98,16 @@ typedef struct {
      * channels of each token, tensor scale 1); dQ = dS K and dK = dS^T Q use
      * the E4M3 token-block Q and K as in the MXFP8 path. */
     int32_t mixed;
+    /* Exact options (Appendix A.3; Section 4.5): 1 = every operand of the
+     * products (Q, K, V and dO) carries one exponent per token instead of
+     * per 32-token block, and the dS operand of dQ carries one exponent per
+     * (query row, 32-key block) taken over the row's visible keys.  The
+     * products that contract over tokens (P-hat V, dV, dK, dQ) take the
+     * other operand's per-token exponent into the 8-bit P-hat, P-hat_b or dS
+     * entry, relative to a shared exponent of the 32-token block (see
+     * fwd_row and unit_run).  Every output of query row i then depends on
+     * tokens <= i only.  Not combined with rowsum = 1, fast_exp or mixed. */
+    int32_t exact;
 } orc_params;
 
 /* ---------------------------------------------------------------------------
@@ -281,14 +298,17 @@ static void hadamard_f64(double *y, int d)
  * blocks and statistics kept inside document boundaries).
  * One document slice of L tokens, d channels, rows `rstride` elements apart;
  * rot = 1 quantizes the Hadamard-rotated rows instead of the bf16 rows.
- * Blocks are [32b, min(32b+32, L)) from the document start; one exponent per
- * block over all d channels; every token of the block stores it.
+ * Blocks are [blk b, min(blk b + blk, L)) from the document start, blk = 32
+ * (token blocks) or 1 (the exact options' per-token exponents); one exponent
+ * per block over all d channels; every token of the block stores it, in
+ * scales (UE8M0 byte) and ex (the exponent itself).
  * deq (L x d, dense) receives value(code) * 2^e, or the (rotated) values
- * themselves when quant is QUANT_NONE.  codes/scales may be NULL.
+ * themselves when quant is QUANT_NONE.  codes/scales/nv/ex may be NULL.
  * Returns 0, or ORC_ERR_NOMEM.
  * ------------------------------------------------------------------------- */
 static int tbq_slice(const uint16_t *x, long rstride, int L, int d, int quant, int rot,
-                     double *deq, uint8_t *codes, long cstride, uint8_t *scales, double *nv)
+                     double *deq, uint8_t *codes, long cstride, uint8_t *scales, double *nv,
+                     int blk, int *ex)
 {
     double *xv = malloc(sizeof(double) * (size_t)L * d);
     float *row = malloc(sizeof(float) * (size_t)d);
@@ -304,8 +324,8 @@ static int tbq_slice(const uint16_t *x, long rstride, int L, int d, int quant, i
     /* the NVFP4 values of the same (rotated) rows, for the mixed path */
     if (nv)
         for (int t = 0; t < L; ++t) nvfp4_row(xv + (long)t * d, d, nv + (long)t * d);
-    for (int b0 = 0; b0 < L; b0 += 32) {
-        int b1 = b0 + 32 < L ? b0 + 32 : L;
+    for (int b0 = 0; b0 < L; b0 += blk) {
+        int b1 = b0 + blk < L ? b0 + blk : L;
         double amax = 0.0;
         int e = 0;
         for (int t = b0; t < b1; ++t)
@@ -316,6 +336,7 @@ static int tbq_slice(const uint16_t *x, long rstride, int L, int d, int quant, i
         if (quant != QUANT_NONE) e = orc_scale_exp(amax, quant == QUANT_FLOOR ? 1 : 0);
         for (int t = b0; t < b1; ++t) {
             if (scales) scales[t] = (uint8_t)(e + 127);
+            if (ex) ex[t] = e;
             for (int k = 0; k < d; ++k) {
                 double v = xv[(long)t * d + k];
                 if (quant == QUANT_NONE) {
@@ -360,7 +381,7 @@ int orc_quantize(const orc_params *p, int heads, const uint16_t *x, const int32_
         if (!deq) { err = ORC_ERR_NOMEM; continue; }
         if (tbq_slice(x + ((long)base * heads + h) * d, (long)heads * d, L, d, p->quant, p->hadamard != 0,
                       deq, codes + ((long)base * heads + h) * d, (long)heads * d,
-                      scales + (long)h * p->ttot + base, 0) != ORC_OK)
+                      scales + (long)h * p->ttot + base, 0, p->exact ? 1 : 32, 0) != ORC_OK)
             err = ORC_ERR_NOMEM;
         free(deq);
     }
@@ -408,6 +429,20 @@ static double code_swing(double y, double r, int loose)
 static double deq_at(double v, int e)
 {
     return ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(v, -e))), e);
+}
+
+/* Largest change of deq_at(v, e) when v moves by at most b and e is any of
+ * es[0..2], measured from ref (the value actually taken). */
+static double deq_swing(double v, double b, const int *es, double ref)
+{
+    double sw = 0.0;
+    for (int a = 0; a < 3; ++a) {
+        double t1 = fabs(deq_at(v + b, es[a]) - ref);
+        double t2 = fabs(deq_at(v - b, es[a]) - ref);
+        if (t1 > sw) sw = t1;
+        if (t2 > sw) sw = t2;
+    }
+    return sw;
 }
 
 /* score error bound (log2 units) of one pair: the implementation's dot
@@ -470,11 +505,12 @@ static int key_pair_class(int j)
 }
 
 static void fwd_row(const orc_params *p, int i, const double *qi, const double *Kt,
-                    const double *Vt, double c1, double *acc, double *x,
+                    const double *Vt, const int *ev, double c1, double *acc, double *x,
                     double *o_out, double *lse_out, int64_t *sat, row_tol *rt)
 {
     int d = p->d, B = p->key_tile, quant = p->quant;
     double m = -INFINITY, l = 0.0;
+    int eblk = -1, E = 0;      /* exact options: key block of E, and E */
     double two_c = ldexp(1.0, p->c_log2);
     /* tolerance bookkeeping (not part of the method) */
     const int track = rt != NULL && quant != QUANT_NONE;
@@ -518,18 +554,38 @@ static void fwd_row(const orc_params *p, int i, const double *qi, const double *
                 w = pj;
                 l += pj;
             } else {
-                double y = pj * two_c;
+                double y = pj * two_c, f = 1.0;
                 uint8_t code;
+                if (ev) {
+                    /* Exact options (Appendix A.3): V~_j carries its own
+                     * exponent e_j.  The entry is taken relative to E, the
+                     * largest exponent of the keys j' <= i in j's 32-key
+                     * block, so that the product applies one factor 2^E per
+                     * (query, key block): y = 2^c p 2^(e_j - E), and
+                     * value(code) 2^(E - e_j) multiplies V~_j.  E never looks
+                     * past key i. */
+                    if ((j >> 5) != eblk) {
+                        int jb1 = (j | 31) < i ? (j | 31) : i;
+                        eblk = j >> 5;
+                        E = ev[j & ~31];
+                        for (int jj = (j & ~31) + 1; jj <= jb1; ++jj)
+                            if (ev[jj] > E) E = ev[jj];
+                    }
+                    f = ldexp(1.0, ev[j] - E);
+                    y *= f;
+                }
                 if (y > 448.0) (*sat)++;
                 code = orc_e4m3_encode(y);
-                w = orc_e4m3_value(code);
+                w = orc_e4m3_value(code) / f;
                 l += (p->rowsum == 1) ? w / two_c : pj;
                 if (track) {
                     /* the approximation's log2 slope is at most 1/ln 2, and the
                      * kernel may land one 1/128 step away */
                     double band = rt->delta[j - j0] + dm;
                     if (approx) band = band / log(2.0) + log2(1.0 + 1.0 / 128.0);
-                    double sw = code_swing(y, band, loose);
+                    /* exact options: the fp32 argument also carries e_j - E */
+                    if (ev) band += 0x1p-20 * (double)(E - ev[j]);
+                    double sw = code_swing(y, band, loose) / f;
                     if (sw > 0.0) {
                         for (int k = 0; k < d; ++k) rt->tacc[k] += sw * fabs(vj[k]);
                         if (p->rowsum == 1) tl += sw / two_c;
@@ -569,6 +625,10 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
     const int mixed = p->mixed != 0 && quant != QUANT_NONE;
     double *Kn = 0, *Qn = 0;
     const double *Ks, *Qs;
+    /* exact options: per-token exponents of K, V, Q, dO (doc-local index) */
+    const int exact = p->exact != 0 && quant != QUANT_NONE;
+    const int blk = exact ? 1 : 32;
+    int *eK = 0, *eV = 0, *eQ = 0, *eO = 0, *erow = 0;
     double *acc = 0, *xbuf = 0, *dS = 0, *dQa = 0, *dKa = 0, *dVa = 0;
     float *lsef = 0;
     int64_t sat = 0, nds = 0, nds0 = 0;
@@ -586,6 +646,14 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         Kn = malloc(sizeof(double) * Ld);
         Qn = malloc(sizeof(double) * Ld);
         if (!Kn || !Qn) { *err = ORC_ERR_NOMEM; goto done; }
+    }
+    if (exact) {
+        eK = malloc(sizeof(int) * (size_t)L);
+        eV = malloc(sizeof(int) * (size_t)L);
+        eQ = malloc(sizeof(int) * (size_t)L);
+        eO = malloc(sizeof(int) * (size_t)L);
+        erow = malloc(sizeof(int) * 32 * 3);
+        if (!eK || !eV || !eQ || !eO || !erow) { *err = ORC_ERR_NOMEM; goto done; }
     }
     Vt = malloc(sizeof(double) * Ld);
     Qt = malloc(sizeof(double) * Ld);
@@ -629,8 +697,9 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
     /* K~ and V~: token blocks of this document and this key/value head. */
     /* K~ is quantized from the rotated rows when the Hadamard rotation is on
      * (Section 3.4); V~ never is. */
-    if (tbq_slice(k + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, p->hadamard != 0, Kt, 0, 0, 0, Kn) ||
-        tbq_slice(v + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, 0, Vt, 0, 0, 0, 0)) {
+    if (tbq_slice(k + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, p->hadamard != 0, Kt, 0, 0, 0, Kn,
+                  blk, eK) ||
+        tbq_slice(v + ((long)base * hkv + g) * d, (long)hkv * d, L, d, quant, 0, Vt, 0, 0, 0, 0, blk, eV)) {
         *err = ORC_ERR_NOMEM;
         goto done;
     }
@@ -639,13 +708,14 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
     Qs = mixed ? Qn : Qt;
     for (int hh = 0; hh < G; ++hh) {
         const int h = g * G + hh;
-        if (tbq_slice(q + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, p->hadamard != 0, Qt, 0, 0, 0, Qn)) {
+        if (tbq_slice(q + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, p->hadamard != 0, Qt, 0, 0, 0, Qn,
+                      blk, eQ)) {
             *err = ORC_ERR_NOMEM;
             goto done;
         }
         /* ---- forward, row by row ---- */
         for (int i = 0; i < L; ++i) {
-            fwd_row(p, i, Qs + (long)i * d, Ks, Vt, c1, acc, xbuf, O + (long)i * d, &lse[i], &sat, rt);
+            fwd_row(p, i, Qs + (long)i * d, Ks, Vt, eV, c1, acc, xbuf, O + (long)i * d, &lse[i], &sat, rt);
             lsef[i] = (float)lse[i];
             if (track) {
                 tlse[i] = rt->tol_lse;
@@ -655,8 +725,8 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                 if (tOall) memcpy(tOall + (long)i * d, tolo, sizeof(double) * d);
             }
             /* MX modes return a bf16 O and the backward reads it back
-             * (Section 3.4: returned outputs are BF16); the exact mode keeps
-             * binary64 throughout. */
+             * (Section 3.4: returned outputs are BF16); the unquantized mode
+             * keeps binary64 throughout. */
             for (int c = 0; c < d; ++c) {
                 long gi = ((long)(base + i) * hq + h) * d + c;
                 uint16_t b = orc_double_to_bf16(O[(long)i * d + c]);
@@ -669,7 +739,7 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         if (!need_bwd) continue;
 
         /* ---- backward (Section 2 equations; Section 3.3 consistency) ---- */
-        if (tbq_slice(dout + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, 0, dOt, 0, 0, 0, 0)) {
+        if (tbq_slice(dout + ((long)base * hq + h) * d, (long)hq * d, L, d, quant, 0, dOt, 0, 0, 0, 0, blk, eO)) {
             *err = ORC_ERR_NOMEM;
             goto done;
         }
@@ -681,6 +751,14 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         if (tdq) memset(tdq, 0, sizeof(double) * Ld);
         for (int i0 = 0; i0 < L; i0 += 32) {
             int i1 = i0 + 32 < L ? i0 + 32 : L;
+            /* exact options: the dV product applies one factor 2^Eo per
+             * 32-query block, Eo = the block's largest dO~ exponent */
+            int Eo = 0;
+            if (exact) {
+                Eo = eO[i0];
+                for (int i = i0 + 1; i < i1; ++i)
+                    if (eO[i] > Eo) Eo = eO[i];
+            }
             /* dS for the 32 query rows of this block, every visible key. */
             for (int i = i0; i < i1; ++i) {
                 double li = (quant == QUANT_NONE) ? lse[i] : (double)lsef[i];
@@ -694,11 +772,14 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                     if (quant == QUANT_NONE) {
                         wb = P;
                     } else {
-                        /* Appendix B.1: the dV operand is E4M3(2^8 P), no scale. */
-                        wb = ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(P, 8))), -8);
+                        /* Appendix B.1: the dV operand is E4M3(2^8 P), no scale.
+                         * Exact options: it also takes dO~_i's own exponent,
+                         * relative to the block's Eo: E4M3(2^8 P 2^(e_i - Eo)). */
+                        const double fo = exact ? ldexp(1.0, eO[i] - Eo) : 1.0;
+                        wb = ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(P, 8) * fo)), -8) / fo;
                         if (track && tdv) {   /* tolerance bookkeeping */
                             double r = score_delta(p, qi, Ks + (long)j * d, d, c1, xij, li) + tlse[i];
-                            double sw = ldexp(code_swing(ldexp(P, 8), r, 0), -8);
+                            double sw = ldexp(code_swing(ldexp(P, 8) * fo, r, 0), -8) / fo;
                             if (sw > 0.0)
                                 for (int c = 0; c < d; ++c) tdv[(long)j * d + c] += sw * fabs(doi[c]);
                         }
@@ -720,6 +801,66 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
             for (int j0 = 0; j0 <= i1 - 1; j0 += 32) {
                 int j1 = j0 + 32 < L ? j0 + 32 : L;
                 int e = 0, elo = 0, ehi = 0;
+                if (exact) {
+                    /* Exact options (Appendix A.3): the two gradient products
+                     * contract over different tokens, so dS~ differs between
+                     * them.  dK's operand takes Q~_i's exponent, y = dS 2^eQ_i,
+                     * with one exponent per 32x32 block of y; dQ's operand
+                     * takes K~_j's exponent, z = dS 2^eK_j, with one exponent
+                     * per query row of the block (the per-query-row dS
+                     * exponent), over that row's visible keys only.  The
+                     * products apply 2^(block or row exponent) and the folded
+                     * exponent returns with the other operand's codes. */
+                    const int rule = quant == QUANT_FLOOR ? 1 : 0;
+                    int *ez = erow, *ezlo = erow + 32, *ezhi = erow + 64;
+                    double ay = 0.0, aylo = 0.0, ayhi = 0.0;
+                    for (int i = i0; i < i1; ++i) {
+                        double az = 0.0, azlo = 0.0, azhi = 0.0;
+                        for (int j = j0; j < j1 && j <= i; ++j) {
+                            double a = fabs(dS[(size_t)(i - i0) * L + j]);
+                            double b = dSd ? dSd[(size_t)(i - i0) * L + j] : 0.0;
+                            double yk = ldexp(a, eQ[i]), yb = ldexp(b, eQ[i]);
+                            double zq = ldexp(a, eK[j]), zb = ldexp(b, eK[j]);
+                            if (yk > ay) ay = yk;
+                            if (yk - yb > aylo) aylo = yk - yb;
+                            if (yk + yb > ayhi) ayhi = yk + yb;
+                            if (zq > az) az = zq;
+                            if (zq - zb > azlo) azlo = zq - zb;
+                            if (zq + zb > azhi) azhi = zq + zb;
+                        }
+                        ez[i - i0] = orc_scale_exp(az, rule);
+                        ezlo[i - i0] = dSd ? orc_scale_exp(azlo, rule) : ez[i - i0];
+                        ezhi[i - i0] = dSd ? orc_scale_exp(azhi, rule) : ez[i - i0];
+                    }
+                    e = orc_scale_exp(ay, rule);
+                    elo = dSd ? orc_scale_exp(aylo, rule) : e;
+                    ehi = dSd ? orc_scale_exp(ayhi, rule) : e;
+                    for (int i = i0; i < i1; ++i)
+                        for (int j = j0; j < j1 && j <= i; ++j) {
+                            double ds = dS[(size_t)(i - i0) * L + j];
+                            double yk = ldexp(ds, eQ[i]), zq = ldexp(ds, eK[j]);
+                            double dkv = ldexp(deq_at(yk, e), -eQ[i]);
+                            double dqv = ldexp(deq_at(zq, ez[i - i0]), -eK[j]);
+                            nds++;
+                            if (ds != 0.0 && dqv == 0.0) nds0++;
+                            if (dSd) {   /* tolerance bookkeeping: how far each dS~ can move */
+                                double band = dSd[(size_t)(i - i0) * L + j];
+                                const int esk[3] = {elo, e, ehi};
+                                const int esq[3] = {ezlo[i - i0], ez[i - i0], ezhi[i - i0]};
+                                double swk = ldexp(deq_swing(yk, ldexp(band, eQ[i]), esk, ldexp(dkv, eQ[i])), -eQ[i]);
+                                double swq = ldexp(deq_swing(zq, ldexp(band, eK[j]), esq, ldexp(dqv, eK[j])), -eK[j]);
+                                for (int c = 0; c < d; ++c) {
+                                    tdq[(long)i * d + c] += swq * fabs(Kt[(long)j * d + c]);
+                                    tdk[(long)j * d + c] += swk * fabs(Qt[(long)i * d + c]);
+                                }
+                            }
+                            for (int c = 0; c < d; ++c) {
+                                dQa[(long)i * d + c] += dqv * Kt[(long)j * d + c];
+                                dKa[(long)j * d + c] += dkv * Qt[(long)i * d + c];
+                            }
+                        }
+                    continue;
+                }
                 if (quant != QUANT_NONE) {
                     double amax = 0.0, alo = 0.0, ahi = 0.0;
                     for (int i = i0; i < i1; ++i)
@@ -746,14 +887,8 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                             nds++;
                             if (ds != 0.0 && dq == 0.0) nds0++;
                             if (dSd) {   /* tolerance bookkeeping: how far dS~ can move */
-                                double band = dSd[(size_t)(i - i0) * L + j], sw = 0.0;
                                 const int es[3] = {elo, e, ehi};
-                                for (int a = 0; a < 3; ++a) {
-                                    double t1 = fabs(deq_at(ds + band, es[a]) - dq);
-                                    double t2 = fabs(deq_at(ds - band, es[a]) - dq);
-                                    if (t1 > sw) sw = t1;
-                                    if (t2 > sw) sw = t2;
-                                }
+                                double sw = deq_swing(ds, dSd[(size_t)(i - i0) * L + j], es, dq);
                                 if (sw > 0.0)
                                     for (int c = 0; c < d; ++c) {
                                         tdq[(long)i * d + c] += sw * fabs(Kt[(long)j * d + c]);
@@ -824,7 +959,7 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
     }
 done:
     free(Kt); free(Vt); free(Qt); free(O); free(lse); free(lsef); free(acc); free(xbuf);
-    free(Kn); free(Qn);
+    free(Kn); free(Qn); free(eK); free(eV); free(eQ); free(eO); free(erow);
     free(dOt); free(Dv); free(dS); free(dQa); free(dKa); free(dVa);
     free(tacc); free(tdel); free(tolo); free(tlse); free(tdv);
     free(tOall); free(dSd); free(tdq); free(tdk);
@@ -865,6 +1000,9 @@ int orc_attention(const orc_params *p, const uint16_t *q, const uint16_t *k, con
     /* the approximate exponential is for the forward only (Section 3.7) */
     if (p->fast_exp < 0 || p->fast_exp > 8 || (p->fast_exp > 0 && dout)) return ORC_ERR_ARG;
     if (p->key_tile <= 0 || p->quant < 0 || p->quant > 2 || !check_cu(p, cu)) return ORC_ERR_ARG;
+    /* the exact options take the unquantized row sum and the exact exponential,
+     * on the MXFP8 path */
+    if (p->exact && (p->rowsum || p->fast_exp || p->mixed)) return ORC_ERR_ARG;
     /* Section 3.4 / Appendix B.1: c + tau <= log2(448) keeps 2^c p below the
      * largest E4M3 value; anything else is rejected. */
     if (p->c_log2 < 0 || p->tau < 0) return ORC_ERR_ARG;
