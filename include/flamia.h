@@ -24,8 +24,9 @@
  *    dense per-token UE8M0 scale table [heads][T] (uint8, value 2^(byte-127)).
  *    Every token of a 32-token block, counted from its document's start,
  *    stores the block's exponent (Section 3.1 token-block scaling, Section
- *    3.6.1 dense per-token metadata).  The exponent is the smallest e with
- *    max|x| <= 448 * 2^e (Section 3.2), so no code saturates.
+ *    3.6.1 dense per-token metadata); with opts.exact = 1 every token stores
+ *    its own.  The exponent is the smallest e with max|x| <= 448 * 2^e over
+ *    the block (or the token), so no code saturates (Section 3.2).
  *    On the mixed NVFP4/FP8 path (opts.mixed = 1, Section 3.4) Q and K also
  *    carry their NVFP4 form (Section 2, "Microscaling floating-point
  *    formats"): per token, one E4M3 scale s per 16 consecutive channels, the
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FLAMIA_ABI_VERSION 5
+#define FLAMIA_ABI_VERSION 6
 
 typedef enum {
     FLAMIA_OK = 0,
@@ -115,6 +116,20 @@ typedef struct {
                               reads from there (both must be non-NULL); every other product
                               is unchanged.  flamia_bwd must be given the value flamia_fwd had.
                               0 (default): the MXFP8 path */
+    int32_t exact;         /* 1: the exact options (Appendix A.3, Section 4.5): every output of
+                              query row i depends on tokens <= i only, bit for bit.  Q, K, V
+                              and dO get one exponent per token (the scale table then differs
+                              between the tokens of a block).  A product that contracts over
+                              tokens carries the other operand's token exponent in its 8-bit
+                              entry, relative to a shared exponent: P-hat takes V's, relative
+                              to the largest V exponent of the visible keys of the 32-key
+                              block; the dV operand takes dO's, relative to the largest of
+                              the 32-query block; dK's dS takes Q's, with one exponent per
+                              32x32 block; dQ's dS takes K's, with one exponent per query row
+                              and 32-key block (the per-query-row dS exponent).  The backward
+                              does not use the dS store (doclen_cap is ignored).  Not with
+                              rowsum, fast_exp or mixed (FLAMIA_ERR_OPTS).  flamia_bwd must be
+                              given the value flamia_fwd had.  0 (default): token blocks */
     /* Optional phase timing: when phase_events is non-NULL it points to
      * n_events hipEvent_t handles (created by the caller); the call records
      * event i on `stream` before its i-th internal launch and the next one

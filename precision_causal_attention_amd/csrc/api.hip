@@ -53,6 +53,10 @@ flamia_status_t check_opts(const flamia_opts_t* o) {
     if (o->fast_exp != 0 && o->fast_exp != 5 && o->fast_exp != 8) return FLAMIA_ERR_OPTS;
     if (o->mixed != 0 && o->mixed != 1) return FLAMIA_ERR_OPTS;
     if (o->mixed && o->fast_exp) return FLAMIA_ERR_OPTS;   // the inference exponential is MXFP8-only
+    if (o->exact != 0 && o->exact != 1) return FLAMIA_ERR_OPTS;
+    // the exact options run on the MXFP8 path with the unquantized row sum
+    // and the exact exponential
+    if (o->exact && (o->rowsum || o->fast_exp || o->mixed)) return FLAMIA_ERR_OPTS;
     if (!(o->softmax_scale <= 0.f || isfinite(o->softmax_scale))) return FLAMIA_ERR_OPTS;
     if (o->n_events < 0 || (o->n_events > 0 && !o->phase_events)) return FLAMIA_ERR_OPTS;
     return FLAMIA_OK;
@@ -138,6 +142,7 @@ flamia_opts_t flamia_default_opts(void) {
     o.hadamard = 0;
     o.fast_exp = 0;
     o.mixed = 0;
+    o.exact = 0;
     o.phase_events = nullptr;
     o.n_events = 0;
     return o;
@@ -217,6 +222,7 @@ flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     qa.t[1] = QuantTensor{k, k_mx.codes, k_mx.scales, dims->hkv, opts.hadamard, kn};
     qa.t[2] = QuantTensor{v, v_mx.codes, v_mx.scales, dims->hkv, 0, nullptr};
     qa.ntensors = 3;
+    qa.per_token = opts.exact;
     PhaseMarks pm{opts, st};
     hipError_t e;
     if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(qa, st)) != hipSuccess) return hip_fail(e);
@@ -238,6 +244,7 @@ flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     fa.rowsum = opts.rowsum;
     fa.fast_exp = opts.fast_exp;
     fa.qn = qn; fa.kn = kn;
+    fa.exact = opts.exact;
     if ((e = pm.mark()) != hipSuccess || (e = launch_fwd(fa, d, w.max_tiles * dims->hq, st)) != hipSuccess)
         return hip_fail(e);
     e = pm.mark();
@@ -273,6 +280,9 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     uint8_t* os = base + w.oscales;
     float* dvec = (float*)(base + w.dvec);
 
+    // the exact options rebuild dS in the dQ pass (its dS operand differs
+    // from the dK one), so the store is not used
+    const long ds_blocks = opts.exact ? 0 : w.ds_blocks;
     int32_t* ctrl = (int32_t*)(base + w.ctrl);
     int4* tiles_q = (int4*)(base + w.tiles_q);
     int4* tiles_k = (int4*)(base + w.tiles_k);
@@ -280,7 +290,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     uint8_t* ds_codes = base + w.ds_codes;
     uint8_t* ds_scales = base + w.ds_scales;
     PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
-                tiles_q, tiles_k, dboff, w.ds_blocks};
+                tiles_q, tiles_k, dboff, ds_blocks};
     const float scale = scale_of(opts, d);
     BwdArgs ba;
     ba.qc = q_mx.codes; ba.qs = q_mx.scales;
@@ -296,7 +306,8 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     ba.hadamard = opts.hadamard;
     ba.qn = opts.mixed ? q_mx.nv : nullptr;
     ba.kn = opts.mixed ? k_mx.nv : nullptr;
-    ba.ds_codes = ds_codes; ba.ds_scales = ds_scales; ba.dboff = dboff; ba.ds_blocks = w.ds_blocks;
+    ba.ds_codes = ds_codes; ba.ds_scales = ds_scales; ba.dboff = dboff; ba.ds_blocks = ds_blocks;
+    ba.exact = opts.exact;
     DqArgs qd;
     qd.qc = q_mx.codes; qd.qs = q_mx.scales;
     qd.kc = k_mx.codes; qd.ks = k_mx.scales;
@@ -311,11 +322,12 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     qd.hadamard = opts.hadamard;
     qd.qn = ba.qn; qd.kn = ba.kn;
     qd.d_o = nullptr; qd.o = nullptr; qd.oc_w = nullptr; qd.os_w = nullptr; qd.dvec_w = nullptr;
-    qd.ds_codes = ds_codes; qd.ds_scales = ds_scales; qd.dboff = dboff; qd.ds_blocks = w.ds_blocks;
+    qd.ds_codes = ds_codes; qd.ds_scales = ds_scales; qd.dboff = dboff; qd.ds_blocks = ds_blocks;
+    qd.exact = opts.exact;
     PhaseMarks pm{opts, st};
     hipError_t e;
     const long gq = w.max_tiles * dims->hq, gk = w.max_tiles * dims->hkv;
-    if (w.ds_blocks == 0) {
+    if (ds_blocks == 0) {
         // No dS store: the query-major dQ pass runs first and quantizes dO
         // itself (codes, scales and D for the key-major pass), so no separate
         // dO launch (Section 3.5.1 fused quantization).

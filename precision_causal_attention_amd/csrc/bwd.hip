@@ -27,6 +27,11 @@
 // and K (bf16, D/16 bf16 MFMAs per 32x32 tile, the forward's instruction with
 // the roles swapped, which gives the same bits); dK still contracts over the
 // E4M3 token-block Q^, so a step stages both forms of its query rows.
+// Exact options (Appendix A.3): Q and dO carry one exponent per query.  S and
+// dP apply them per lane as before; dV and dK contract over queries, so dO's
+// exponent moves into P-hat_b relative to the largest of its 32-query block
+// (E4M3(2^8 P 2^(e_o - E_o)), A scale 2^E_o) and Q's into dS (dS 2^e_q, one
+// exponent per 32x32 block as before, A scale 1).
 #include <type_traits>
 
 #include "device.h"
@@ -36,7 +41,7 @@ namespace flamia {
 
 constexpr int kQStep = 64;
 
-template <int D, int MIX>
+template <int D, int MIX, int EXACT = 0>
 struct BwdStep {
     static constexpr int kStride = D + 16;       // row pitch of code tiles
     static constexpr int kNStride = 2 * D + 16;  // row pitch of the bf16 NVFP4 rows (mixed path)
@@ -47,33 +52,40 @@ struct BwdStep {
     uint8_t eq[kQStep];
     uint8_t eo[kQStep];
     alignas(16) uint8_t qn[MIX ? kQStep * kNStride : 16];   // NVFP4 values of Q (mixed path)
+    // exact options: per query 2^(e_o - E_o) and 2^e_q; E_o per 32-query block
+    alignas(16) float fo[EXACT ? kQStep : 4];
+    alignas(16) float fq[EXACT ? kQStep : 4];
+    uint8_t eob[4];
 };
+
 
 // A ring of step buffers, so that a step fills its buffer without waiting:
 // step i writes buffer i % N, last read by the products of step i - N and,
 // with the software pipeline (d = 64, MXFP8, N = 3), by the dV/dK products
 // of that step issued in step i - N + 1; every wave is past both before it
 // reaches the barrier of step i - 1.
-template <int D, int MIX, int N>
+template <int D, int MIX, int N, int EXACT = 0>
 struct BwdSmem {
-    static constexpr int kStride = BwdStep<D, MIX>::kStride;
-    BwdStep<D, MIX> buf[N];
+    static constexpr int kStride = BwdStep<D, MIX, EXACT>::kStride;
+    BwdStep<D, MIX, EXACT> buf[N];
 };
 
-template <int D, bool STORE, int MIX>
+template <int D, bool STORE, int MIX, int EXACT>
 __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
     constexpr int KC = D / 64;
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;
     // The mixed path's bf16 operands take the registers the pipeline needs.
     static_assert(D == 64, "d = 128 runs in bwd_split.hip");
+    static_assert(!EXACT || (!STORE && !MIX), "the exact options run without the store, on MXFP8");
     constexpr bool PIPE = !STORE && !MIX;
     constexpr int NBUF = PIPE ? 3 : 2;
-    constexpr int STR = BwdStep<D, MIX>::kStride;
-    constexpr int NSTR = BwdStep<D, MIX>::kNStride;
+    using Step = BwdStep<D, MIX, EXACT>;
+    constexpr int STR = Step::kStride;
+    constexpr int NSTR = Step::kNStride;
     constexpr int NQ = kQStep * D / 16 / 256;     // 16-byte chunks per thread of a 64-row code tile
     constexpr int NQN = MIX ? 2 * NQ : 1;         // same for the bf16 NVFP4 rows
-    __shared__ BwdSmem<D, MIX, NBUF> sm;
+    __shared__ BwdSmem<D, MIX, NBUF, EXACT> sm;
 
     const int ti = (int)blockIdx.x / a.hkv;
     if (ti >= *a.ntiles) return;
@@ -128,7 +140,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
             p_dv = a.dvec[(long)h * a.ttot + qr];
         }
     };
-    auto store_step = [&](BwdStep<D, MIX>& b) {
+    auto store_step = [&](Step& b) {
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
             const int c = tid + 256 * r;
@@ -149,6 +161,15 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
             b.eo[tid] = (uint8_t)p_eo;
             b.lse[tid] = p_in ? p_lse : INFINITY;   // +inf: row outside the document
             b.dv[tid] = -p_dv;                       // -D: accumulator input of dP
+        }
+        if constexpr (EXACT) {
+            // thread tid holds query tid % 64: each half-wave one 32-query block
+            const uint32_t eb = halfwave_max(p_eo);
+            if (tid < kQStep) {
+                b.fo[tid] = ldexpf(1.f, (int)p_eo - (int)eb);
+                b.fq[tid] = ldexpf(1.f, (int)p_eq - 127);
+                if ((tid & 31) == 0) b.eob[tid >> 5] = (uint8_t)eb;
+            }
         }
     };
     load_step(g * G, kt0);
@@ -192,10 +213,13 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
 
     // dV^T += dO^T P-hat_b and dK^T += Q^T dS-hat of one step (contraction
     // over its 64 queries), from its codes and its step buffer
-    auto dvdk = [&](const BwdStep<D, MIX>& b, const int (&pbc)[2][4], const int (&dsc)[2][4], const int (&es)[2]) {
+    auto dvdk = [&](const Step& b, const int (&pbc)[2][4], const int (&dsc)[2][4], const int (&es)[2]) {
         const v8i pb = v8i{pbc[0][0], pbc[0][1], pbc[0][2], pbc[0][3], pbc[1][0], pbc[1][1], pbc[1][2], pbc[1][3]};
         const v8i db = v8i{dsc[0][0], dsc[0][1], dsc[0][2], dsc[0][3], dsc[1][0], dsc[1][1], dsc[1][2], dsc[1][3]};
-        const int so = b.eo[32 * lg], sq = b.eq[32 * lg];
+        // A scales: dO's and Q's token blocks, or (exact options) dO's block
+        // maximum and 1 (Q's exponents are inside dS-hat)
+        const int so = EXACT ? (int)b.eob[lg] : (int)b.eo[32 * lg];
+        const int sq = EXACT ? 127 : (int)b.eq[32 * lg];
         const int sd = lg ? es[1] : es[0];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -244,7 +268,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
     auto step = [&](auto mask_tag) -> bool {
         constexpr bool MASK = decltype(mask_tag)::value;
         // ---- publish the prefetched step in LDS, start fetching the next one
-        BwdStep<D, MIX>& B = sm.buf[cur];
+        Step& B = sm.buf[cur];
         store_step(B);
         __syncthreads();
         const int h = g * G + hh;
@@ -324,14 +348,23 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
                 const int q4 = 32 * st + 8 * j + 4 * lg;            // 4 consecutive query rows
                 const float4 l4 = *reinterpret_cast<const float4*>(&B.lse[q4]);
                 const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
+                float fo[4] = {1.f, 1.f, 1.f, 1.f}, fq[4] = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (EXACT) {
+                    const float4 o4 = *reinterpret_cast<const float4*>(&B.fo[q4]);
+                    const float4 g4 = *reinterpret_cast<const float4*>(&B.fq[q4]);
+                    fo[0] = o4.x; fo[1] = o4.y; fo[2] = o4.z; fo[3] = o4.w;
+                    fq[0] = g4.x; fq[1] = g4.y; fq[2] = g4.z; fq[3] = g4.w;
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 4 * j + r;
                     float p = exp2_fast(fmaf(sacc[st][i], a.c1, -lq[r]));
                     if (partial(st))
                         if (32 * st + 8 * j + r < lim) p = 0.f;
-                    sacc[st][i] = p;
-                    const float dsi = p * pacc[st][i];
+                    // exact options: the folds are exact power-of-two scalings
+                    sacc[st][i] = EXACT ? p * fo[r] : p;
+                    float dsi = p * pacc[st][i];
+                    if constexpr (EXACT) dsi *= fq[r];
                     dsv[i] = dsi;
                     amax = fmaxf(amax, fabsf(dsi));
                 }
@@ -427,8 +460,8 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
 
 template <int D, bool STORE>
 static void launch_bwd_mix(const BwdArgs& a, dim3 g, hipStream_t st) {
-    if (a.qn) hipLaunchKernelGGL((bwd_kernel<D, STORE, 1>), g, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((bwd_kernel<D, STORE, 0>), g, dim3(256), 0, st, a);
+    if (a.qn) hipLaunchKernelGGL((bwd_kernel<D, STORE, 1, 0>), g, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((bwd_kernel<D, STORE, 0, 0>), g, dim3(256), 0, st, a);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int d, long grid, hipStream_t st) {
@@ -439,6 +472,11 @@ hipError_t launch_bwd(const BwdArgs& a, int d, long grid, hipStream_t st) {
     // the store variant only where the workspace has a dS store
     const bool store = a.ds_blocks > 0;
     const dim3 g((unsigned)grid);
+    if (a.exact) {
+        if (store || a.qn) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((bwd_kernel<64, false, 0, 1>), g, dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
     if (store) launch_bwd_mix<64, true>(a, g, st);
     else launch_bwd_mix<64, false>(a, g, st);
     return hipGetLastError();

@@ -18,6 +18,9 @@
 // With half the accumulators a wave fits two per SIMD.  The Hadamard
 // back-rotation of dK runs channel bits 0-5 inside the wave and bit 6 across
 // the pair through LDS, in the same order as the unsplit kernel.
+// Exact options (Appendix A.3): the same folds as the d = 64 kernel (dO's
+// token exponent into P-hat_b relative to its 32-query block maximum, Q's
+// into dS).
 #include <type_traits>
 
 #include "device.h"
@@ -30,7 +33,7 @@ namespace {
 constexpr int kSD = 128;                  // head dimension of this kernel
 constexpr int kSStep = 64;                // queries per step
 
-template <int MIX>
+template <int MIX, int EXACT>
 struct SplitStep {
     static constexpr int kStride = kSD + 16;       // row pitch of code tiles
     static constexpr int kNStride = 2 * kSD + 16;  // row pitch of the bf16 NVFP4 rows (mixed path)
@@ -41,6 +44,10 @@ struct SplitStep {
     uint8_t eq[kSStep];
     uint8_t eo[kSStep];
     alignas(16) uint8_t qn[MIX ? kSStep * kNStride : 16];
+    // exact options: per query 2^(e_o - E_o) and 2^e_q; E_o per 32-query block
+    alignas(16) float fo[EXACT ? kSStep : 4];
+    alignas(16) float fq[EXACT ? kSStep : 4];
+    uint8_t eob[4];
 };
 
 // Codes a wave hands to its partner each step: per lane 4 words of P-hat_b
@@ -51,11 +58,11 @@ struct SplitXchg {
     int es[8];
 };
 
-template <int MIX>
+template <int MIX, int EXACT>
 struct SplitSmem {
     union {
         struct {
-            SplitStep<MIX> buf[2];   // ring: step i fills buffer i % 2
+            SplitStep<MIX, EXACT> buf[2];   // ring: step i fills buffer i % 2
             SplitXchg x;
         } loop;
         float rot[4][2][16][64];     // epilogue: dK tiles of the waves 4 .. 7 or 0 .. 3
@@ -64,17 +71,19 @@ struct SplitSmem {
 
 }  // namespace
 
-template <bool STORE, int MIX>
+template <bool STORE, int MIX, int EXACT>
 __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     constexpr int D = kSD;
     constexpr int KC = D / 64;
     constexpr int NC = D / 16;
     constexpr int DTH = 2;                        // 32-channel tiles of dK / dV per wave
-    constexpr int STR = SplitStep<MIX>::kStride;
-    constexpr int NSTR = SplitStep<MIX>::kNStride;
+    using Step = SplitStep<MIX, EXACT>;
+    constexpr int STR = Step::kStride;
+    constexpr int NSTR = Step::kNStride;
+    static_assert(!EXACT || (!STORE && !MIX), "the exact options run without the store, on MXFP8");
     constexpr int NQ = kSStep * D / 16 / 512;     // 16-byte chunks per thread of a 64-row code tile
     constexpr int NQN = MIX ? 2 * NQ : 1;
-    __shared__ SplitSmem<MIX> sm;
+    __shared__ SplitSmem<MIX, EXACT> sm;
 
     const int ti = (int)blockIdx.x / a.hkv;
     if (ti >= *a.ntiles) return;
@@ -126,7 +135,7 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
         p_in = ql < L;
         p_dv = a.dvec[(long)h * a.ttot + qr];
     };
-    auto store_step = [&](SplitStep<MIX>& b) {
+    auto store_step = [&](Step& b) {
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
             const int c = tid + 512 * r;
@@ -147,6 +156,15 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
             b.eo[tid] = (uint8_t)p_eo;
             b.lse[tid] = p_in ? p_lse : INFINITY;   // +inf: row outside the document
             b.dv[tid] = -p_dv;                       // -D: accumulator input of dP
+        }
+        if constexpr (EXACT) {
+            // thread tid holds query tid % 64: each half-wave one 32-query block
+            const uint32_t eb = halfwave_max(p_eo);
+            if (tid < kSStep) {
+                b.fo[tid] = ldexpf(1.f, (int)p_eo - (int)eb);
+                b.fq[tid] = ldexpf(1.f, (int)p_eq - 127);
+                if ((tid & 31) == 0) b.eob[tid >> 5] = (uint8_t)eb;
+            }
         }
     };
     load_step(g * G, kt0);
@@ -204,7 +222,7 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     // (the first two of every head, starting at the diagonal).
     auto step = [&](auto mask_tag) -> bool {
         constexpr bool MASK = decltype(mask_tag)::value;
-        SplitStep<MIX>& B = sm.loop.buf[cur];
+        Step& B = sm.loop.buf[cur];
         store_step(B);
         __syncthreads();
         const int h = g * G + hh;
@@ -260,16 +278,26 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
             float amax = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float4 l4 = *reinterpret_cast<const float4*>(&B.lse[32 * hf + 8 * j + 4 * lg]);
+                const int q4 = 32 * hf + 8 * j + 4 * lg;
+                const float4 l4 = *reinterpret_cast<const float4*>(&B.lse[q4]);
                 const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
+                float fo[4] = {1.f, 1.f, 1.f, 1.f}, fq[4] = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (EXACT) {
+                    const float4 o4 = *reinterpret_cast<const float4*>(&B.fo[q4]);
+                    const float4 g4 = *reinterpret_cast<const float4*>(&B.fq[q4]);
+                    fo[0] = o4.x; fo[1] = o4.y; fo[2] = o4.z; fo[3] = o4.w;
+                    fq[0] = g4.x; fq[1] = g4.y; fq[2] = g4.z; fq[3] = g4.w;
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 4 * j + r;
                     float p = exp2_fast(fmaf(sacc[i], a.c1, -lq[r]));
                     if (part)
                         if (8 * j + r < lim) p = 0.f;
-                    sacc[i] = p;
+                    // exact options: the folds are exact power-of-two scalings
+                    sacc[i] = EXACT ? p * fo[r] : p;
                     pacc[i] = p * pacc[i];
+                    if constexpr (EXACT) pacc[i] *= fq[r];
                     amax = fmaxf(amax, fabsf(pacc[i]));
                 }
             }
@@ -311,7 +339,10 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
             const v8i pb = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
             const v8i db = v8i{(int)d0.x, (int)d0.y, (int)d0.z, (int)d0.w, (int)d1.x, (int)d1.y, (int)d1.z, (int)d1.w};
             const int e0 = hf ? pes : es, e1 = hf ? es : pes;
-            const int so = B.eo[32 * lg], sq = B.eq[32 * lg];
+            // A scales: dO's and Q's token blocks, or (exact options) dO's
+            // block maximum and 1 (Q's exponents are inside dS-hat)
+            const int so = EXACT ? (int)B.eob[lg] : (int)B.eo[32 * lg];
+            const int sq = EXACT ? 127 : (int)B.eq[32 * lg];
             const int sd = lg ? e1 : e0;
 #pragma unroll
             for (int t = 0; t < DTH; ++t) {
@@ -403,12 +434,15 @@ hipError_t launch_bwd_split(const BwdArgs& a, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
     const bool store = a.ds_blocks > 0;
     const dim3 g((unsigned)grid), b(512);
-    if (a.qn) {
-        if (store) hipLaunchKernelGGL((bwd_split_kernel<true, 1>), g, b, 0, st, a);
-        else hipLaunchKernelGGL((bwd_split_kernel<false, 1>), g, b, 0, st, a);
+    if (a.exact) {
+        if (store || a.qn) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((bwd_split_kernel<false, 0, 1>), g, b, 0, st, a);
+    } else if (a.qn) {
+        if (store) hipLaunchKernelGGL((bwd_split_kernel<true, 1, 0>), g, b, 0, st, a);
+        else hipLaunchKernelGGL((bwd_split_kernel<false, 1, 0>), g, b, 0, st, a);
     } else {
-        if (store) hipLaunchKernelGGL((bwd_split_kernel<true, 0>), g, b, 0, st, a);
-        else hipLaunchKernelGGL((bwd_split_kernel<false, 0>), g, b, 0, st, a);
+        if (store) hipLaunchKernelGGL((bwd_split_kernel<true, 0, 0>), g, b, 0, st, a);
+        else hipLaunchKernelGGL((bwd_split_kernel<false, 0, 0>), g, b, 0, st, a);
     }
     return hipGetLastError();
 }

@@ -223,6 +223,17 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
     return __uint_as_float(max((uint32_t)r[0], (uint32_t)r[1]));
 }
 
+// Largest of a non-negative integer over each half-wave (lanes 0-31, 32-63), in every
+// lane of the half: DPP over 16-lane rows, then one row swap.
+__device__ __forceinline__ uint32_t halfwave_max(uint32_t v) {
+    v = umax_dpp<0xB1>(v);
+    v = umax_dpp<0x4E>(v);
+    v = umax_dpp<0x141>(v);
+    v = umax_dpp<0x140>(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+
 // Head of work item `local` (0 <= local < heads) of one tile.  Workgroups
 // are dispatched round-robin over the 8 XCDs (workgroup index % 8), each
 // with its own L2.  When heads % 8 == 0 the tile's items start at a multiple

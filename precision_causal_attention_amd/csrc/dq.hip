@@ -27,6 +27,12 @@
 // the codes (its own dP operand) and D = dO~ . O, and writes them for the
 // key-major pass, in the order of the standalone quantizer, so D is the same
 // bit for bit.
+// Exact options (Appendix A.3): dO gets one exponent per query (the lane's own
+// maximum); dQ contracts over keys, so K's token exponent e_j moves into dS:
+// z = dS 2^e_j, and each query row takes its own exponent per 32-key block
+// (the maximum of |z| over the lane's 16 registers and its partner lane's),
+// which the product applies as its per-column B scale; K^T's A scale is 1.
+// Nothing a query row computes then depends on later tokens.
 #include <type_traits>
 
 #include "device.h"
@@ -34,7 +40,7 @@
 
 namespace flamia {
 
-template <int D, int MIX>
+template <int D, int MIX, int EXACT>
 struct DqSmem {
     static constexpr int kStride = D + 16;
     static constexpr int kNStride = 2 * D + 16;   // bf16 NVFP4 rows of K (mixed path)
@@ -43,20 +49,22 @@ struct DqSmem {
     uint8_t ek[kTile];
     uint8_t ev[kTile];
     alignas(16) uint8_t kn[MIX ? kTile * kNStride : 16];
+    alignas(16) float kf[EXACT ? kTile : 4];      // exact options: 2^(K's token exponent)
 };
 
 // At least two workgroups per CU at both head dimensions (at d = 128 one wave
 // per SIMD left latencies exposed: 36% longer).
-template <int D, int MIX, bool FUSED>
+template <int D, int MIX, bool FUSED, int EXACT>
 __global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
     constexpr int KC = D / 64;
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;
-    constexpr int STR = DqSmem<D, MIX>::kStride;
-    constexpr int NSTR = DqSmem<D, MIX>::kNStride;
+    constexpr int STR = DqSmem<D, MIX, EXACT>::kStride;
+    constexpr int NSTR = DqSmem<D, MIX, EXACT>::kNStride;
     constexpr int CHUNKS = kTile * D / 16;
     constexpr int NCH = MIX ? 2 * CHUNKS / 256 : 1;   // 16-byte chunks per thread of a bf16 K tile
-    __shared__ DqSmem<D, MIX> sm;
+    static_assert(!EXACT || (FUSED && !MIX), "the exact options run the fused MXFP8 pass");
+    __shared__ DqSmem<D, MIX, EXACT> sm;
 
     if (a.ntiles[1] != 0) return;                    // the dS store is in use: dq_store.hip runs
     const int ti = (int)blockIdx.x / a.hq;
@@ -130,8 +138,11 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
 #pragma unroll
                 for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[kc][run][k]));
             }
-        amax = wave_max_nonneg(amax);
-        const int e = block_exponent_uniform(amax, -127);   // the block of the wave's 32 queries
+        // the block of the wave's 32 queries, or (exact options) the lane's
+        // query: its channels lie in this lane and its partner l ^ 32
+        int e;
+        if constexpr (EXACT) e = block_exponent(max_xor32(amax), -127);
+        else e = block_exponent_uniform(wave_max_nonneg(amax), -127);
         eo = e + 127;
         // codes = E4M3(x 2^-e); D = sum over 8-channel chunks c of the chain
         // fma(code value, O, .) in channel order, chunks summed as the
@@ -247,6 +258,7 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
         if (tid < kTile) {
             sm.ek[tid] = (uint8_t)ekr;
             sm.ev[tid] = (uint8_t)evr;
+            if constexpr (EXACT) sm.kf[tid] = ldexpf(1.f, (int)ekr - 127);
         }
         __syncthreads();
         if constexpr (!DIAG) fetch(ds + kTile * (t + 1));
@@ -291,10 +303,14 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
                 float p = exp2_fast(fmaf(sb[i], a.c1, -lse));
                 if (masked && 32 * kk + 8 * (i >> 2) + (i & 3) > lim) p = 0.f;
                 dpb[i] = p * dpb[i];
+                if constexpr (EXACT) {   // z = dS 2^e_j (exact scaling)
+                    dpb[i] *= sm.kf[32 * kk + 8 * (i >> 2) + 4 * lg + (i & 3)];
+                }
                 amax = fmaxf(amax, fabsf(dpb[i]));
             }
-            amax = wave_max_nonneg(amax);
-            const int e = block_exponent_uniform(amax, -126);
+            int e;
+            if constexpr (EXACT) e = block_exponent(max_xor32(amax), -126);   // the lane's query row
+            else e = block_exponent_uniform(wave_max_nonneg(amax), -126);
             ebyte = e + 127;
             const float sc = __uint_as_float((uint32_t)(e + 127) << 23);
 #pragma unroll
@@ -304,7 +320,7 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
         // dQ^T += K^T dS-hat^T over the 64 keys of chunk c
         auto dq_chunk = [&](const int c, const int (&c0)[4], const int (&c1)[4], int e0, int e1) {
             const v8i db = v8i{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-            const int sk = sm.ek[64 * c + 32 * lg];
+            const int sk = EXACT ? 127 : (int)sm.ek[64 * c + 32 * lg];
             const int sd = lg ? e1 : e0;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
@@ -379,21 +395,27 @@ hipError_t launch_dq(const DqArgs& a, int d, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), b(256);
     const bool fused = a.d_o != nullptr;
+    if (a.exact) {
+        if (!fused || a.qn) return hipErrorInvalidValue;
+        if (d == 64) hipLaunchKernelGGL((dq_kernel<64, 0, true, 1>), g, b, 0, st, a);
+        else hipLaunchKernelGGL((dq_kernel<128, 0, true, 1>), g, b, 0, st, a);
+        return hipGetLastError();
+    }
     if (d == 64) {
         if (a.qn) {
-            if (fused) hipLaunchKernelGGL((dq_kernel<64, 1, true>), g, b, 0, st, a);
-            else hipLaunchKernelGGL((dq_kernel<64, 1, false>), g, b, 0, st, a);
+            if (fused) hipLaunchKernelGGL((dq_kernel<64, 1, true, 0>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((dq_kernel<64, 1, false, 0>), g, b, 0, st, a);
         } else {
-            if (fused) hipLaunchKernelGGL((dq_kernel<64, 0, true>), g, b, 0, st, a);
-            else hipLaunchKernelGGL((dq_kernel<64, 0, false>), g, b, 0, st, a);
+            if (fused) hipLaunchKernelGGL((dq_kernel<64, 0, true, 0>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((dq_kernel<64, 0, false, 0>), g, b, 0, st, a);
         }
     } else {
         if (a.qn) {
-            if (fused) hipLaunchKernelGGL((dq_kernel<128, 1, true>), g, b, 0, st, a);
-            else hipLaunchKernelGGL((dq_kernel<128, 1, false>), g, b, 0, st, a);
+            if (fused) hipLaunchKernelGGL((dq_kernel<128, 1, true, 0>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((dq_kernel<128, 1, false, 0>), g, b, 0, st, a);
         } else {
-            if (fused) hipLaunchKernelGGL((dq_kernel<128, 0, true>), g, b, 0, st, a);
-            else hipLaunchKernelGGL((dq_kernel<128, 0, false>), g, b, 0, st, a);
+            if (fused) hipLaunchKernelGGL((dq_kernel<128, 0, true, 0>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((dq_kernel<128, 0, false, 0>), g, b, 0, st, a);
         }
     }
     return hipGetLastError();

@@ -24,6 +24,13 @@
 // block-scaled MFMA cannot apply one E4M3 scale per 16 channels): D/16 bf16
 // MFMAs 32x32x16 per sub-tile, no scale operands; everything after S is the
 // same.
+// Exact options (Appendix A.3): Q, K and V carry one exponent per token.  S
+// applies Q's and K's per lane as before.  P-hat V contracts over keys, so V's
+// token exponent e_j moves into P-hat: P-hat = E4M3(p' 2^(e_j - E)), and the
+// product's B-operand scale (one per query column and 32-key block) is
+// 2^E, with E the largest e_j of the block's keys up to the query: the block
+// maximum below the diagonal, the running maximum on the diagonal block.
+// The row sum keeps the unfolded p'.
 #include <type_traits>
 
 #include "device.h"
@@ -31,7 +38,7 @@
 
 namespace flamia {
 
-template <int D, int MIX>
+template <int D, int MIX, int EXACT>
 struct FwdSmem {
     static constexpr int kStride = D + 16;        // row pitch of a code tile in LDS (bank spread)
     static constexpr int kKStride = MIX ? 2 * D + 16 : kStride;   // K: bf16 NVFP4 values when mixed
@@ -39,6 +46,11 @@ struct FwdSmem {
     uint8_t v[kTile * kStride];
     uint8_t ek[kTile];
     uint8_t ev[kTile];
+    // exact options: 2^(e_j - block maximum) per key, the running maximum of
+    // e_j from the block start (UE8M0 byte) per key, the block maxima
+    alignas(16) float dvp[EXACT ? kTile : 4];
+    uint8_t pmx[EXACT ? kTile : 4];
+    uint8_t bmx[4];
 };
 
 // Schraudolph's exponential (inference only; paper Section 3.7, Appendix
@@ -61,17 +73,17 @@ __device__ __forceinline__ constexpr int pair_class(int i) {
 // dimensions: at d = 128 one wave per SIMD leaves the matrix-core and memory
 // latencies exposed (the kernel ran 35% longer), and the few registers the
 // mixed and inference variants spill cost less than that.
-template <int D, int ROWSUM, int FAST, int MIX>
+template <int D, int ROWSUM, int FAST, int MIX, int EXACT>
 __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
     constexpr int KC = D / 64;                    // 64-channel contraction steps of S
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;                    // 32-row channel tiles of O^T
-    constexpr int STR = FwdSmem<D, MIX>::kStride;
-    constexpr int KSTR = FwdSmem<D, MIX>::kKStride;
+    constexpr int STR = FwdSmem<D, MIX, EXACT>::kStride;
+    constexpr int KSTR = FwdSmem<D, MIX, EXACT>::kKStride;
     constexpr int CHUNKS = kTile * D / 16;        // 16-byte chunks of one code tile
     constexpr int KCHUNKS = MIX ? 2 * CHUNKS : CHUNKS;   // 16-byte chunks of one K tile
     constexpr int KRB = MIX ? 2 * D / 16 : D / 16;       // 16-byte chunks of one K row
-    __shared__ FwdSmem<D, MIX> sm;
+    __shared__ FwdSmem<D, MIX, EXACT> sm;
 
     const int ti = (int)blockIdx.x / a.hq;
     if (ti >= *a.ntiles) return;
@@ -171,6 +183,25 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
             sm.ek[tid] = (uint8_t)ekr;
             sm.ev[tid] = (uint8_t)evr;
         }
+        if constexpr (EXACT) {
+            // V's token exponents (biased bytes): thread tid holds key tid % 128,
+            // and each 32-lane half-wave holds one 32-key block.  Block maximum
+            // by DPP over 16 lanes plus one row swap; running maximum from the
+            // block start by shifted reads.
+            const uint32_t bm = halfwave_max(evr);
+            const int l32 = tid & 31;
+            uint32_t pm = evr;
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) {
+                const uint32_t u = (uint32_t)__shfl_up((int)pm, off, 32);
+                if (l32 >= off) pm = max(pm, u);
+            }
+            if (tid < kTile) {
+                sm.dvp[tid] = ldexpf(1.f, (int)evr - (int)bm);
+                sm.pmx[tid] = (uint8_t)pm;
+                if (l32 == 0) sm.bmx[tid >> 5] = (uint8_t)bm;
+            }
+        }
         __syncthreads();
         if constexpr (!DIAG) fetch(ds + kTile * (t + 1));
 
@@ -256,7 +287,22 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
                 const float p1 = pexp(s[kk][4 * j + 1], 4 * j + 1);
                 const float p2 = pexp(s[kk][4 * j + 2], 4 * j + 2);
                 const float p3 = pexp(s[kk][4 * j + 3], 4 * j + 3);
-                const int w = pack_fp8x4(p0, p1, p2, p3);
+                int w;
+                if constexpr (EXACT) {
+                    // fold 2^(e_j - E) (exact scaling): keys 32kk + 8j + 4lg + 0..3
+                    const int kb = 32 * kk + 8 * j + 4 * lg;
+                    float4 f;
+                    if (DIAG && kk == wave_u) {
+                        const int pe = sm.pmx[32 * kk + lr];   // E of the lane's query
+                        f = make_float4(ldexpf(1.f, (int)sm.ev[kb] - pe), ldexpf(1.f, (int)sm.ev[kb + 1] - pe),
+                                        ldexpf(1.f, (int)sm.ev[kb + 2] - pe), ldexpf(1.f, (int)sm.ev[kb + 3] - pe));
+                    } else {
+                        f = *reinterpret_cast<const float4*>(&sm.dvp[kb]);
+                    }
+                    w = pack_fp8x4(p0 * f.x, p1 * f.y, p2 * f.z, p3 * f.w);
+                } else {
+                    w = pack_fp8x4(p0, p1, p2, p3);
+                }
                 pc[kk][j] = w;
                 if constexpr (ROWSUM == 0) l += (p0 + p1) + (p2 + p3);
                 else l += fp8x4_sum(w);
@@ -267,7 +313,15 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
             if (DIAG && 2 * c > wave_u) continue;      // both sub-tiles skipped: P-hat = 0
             const v8i pb = v8i{pc[2 * c][0], pc[2 * c][1], pc[2 * c][2], pc[2 * c][3],
                                pc[2 * c + 1][0], pc[2 * c + 1][1], pc[2 * c + 1][2], pc[2 * c + 1][3]};
-            const int sv = sm.ev[64 * c + 32 * lg];
+            // scales: V's block (A), or with the exact options E of the lane's
+            // query and key block 2c + lg (B)
+            int sv = 127, sp = 127;
+            if constexpr (EXACT) {
+                const int b = 2 * c + lg;
+                sp = (DIAG && b == wave_u) ? (int)sm.pmx[32 * b + lr] : (int)sm.bmx[b];
+            } else {
+                sv = sm.ev[64 * c + 32 * lg];
+            }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 v2i r[4];
@@ -275,7 +329,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
                 for (int rr = 0; rr < 4; ++rr)
                     r[rr] = lds_read_tr8(&sm.v[(64 * c + 16 * rr + tr_key) * STR + 32 * dt + tr_col]);
                 const v8i va = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
-                acc[dt] = mfma_mx(va, pb, acc[dt], sv, 127);
+                acc[dt] = mfma_mx(va, pb, acc[dt], sv, sp);
             }
         }
     };
@@ -301,20 +355,25 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
 template <int D, int ROWSUM>
 static void launch_fwd_fast(const FwdArgs& a, dim3 g, dim3 b, hipStream_t st) {
     // the inference exponential is offered on the MXFP8 path only
-    if (a.qn) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 0, 1>), g, b, 0, st, a);
-    else if (a.fast_exp == 8) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 8, 0>), g, b, 0, st, a);
-    else if (a.fast_exp == 5) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 5, 0>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 0, 0>), g, b, 0, st, a);
+    if (a.qn) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 0, 1, 0>), g, b, 0, st, a);
+    else if (a.fast_exp == 8) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 8, 0, 0>), g, b, 0, st, a);
+    else if (a.fast_exp == 5) hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 5, 0, 0>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<D, ROWSUM, 0, 0, 0>), g, b, 0, st, a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), b(256);
+    // the exact options take the unquantized row sum, the exact exponential
+    // and the MXFP8 scores (checked by the host layer)
+    if (a.exact && (a.rowsum || a.fast_exp || a.qn)) return hipErrorInvalidValue;
     if (d == 64) {
-        if (a.rowsum) launch_fwd_fast<64, 1>(a, g, b, st);
+        if (a.exact) hipLaunchKernelGGL((fwd_kernel<64, 0, 0, 0, 1>), g, b, 0, st, a);
+        else if (a.rowsum) launch_fwd_fast<64, 1>(a, g, b, st);
         else launch_fwd_fast<64, 0>(a, g, b, st);
     } else {
-        if (a.rowsum) launch_fwd_fast<128, 1>(a, g, b, st);
+        if (a.exact) hipLaunchKernelGGL((fwd_kernel<128, 0, 0, 0, 1>), g, b, 0, st, a);
+        else if (a.rowsum) launch_fwd_fast<128, 1>(a, g, b, st);
         else launch_fwd_fast<128, 0>(a, g, b, st);
     }
     return hipGetLastError();

@@ -26,6 +26,7 @@ struct QuantArgs {
     int ndocs, ttot, d;
     QuantTensor t[3];
     int ntensors;
+    int per_token;            // 1: one exponent per token instead of per 32-token block
     // dO variant only (nullptr otherwise; then t[0] is dO): D = dO~ . O
     const uint16_t* o;
     float* dvec;
@@ -67,6 +68,7 @@ struct FwdArgs {
     int rowsum;
     int fast_exp;          // 0, or 5 / 8 key-pair classes of 8 with the approximate exponential
     const uint16_t *qn, *kn;   // mixed path: NVFP4 values of Q and K (bf16) for the scores; else nullptr
+    int exact;                 // 1: the exact options (per-token scales, V's folded into P-hat)
 };
 
 struct BwdArgs {
@@ -84,6 +86,7 @@ struct BwdArgs {
     uint8_t* ds_scales;
     const int32_t* dboff;
     long ds_blocks;
+    int exact;                // 1: the exact options (dO's and Q's token exponents folded)
 };
 
 struct DqArgs {
@@ -108,6 +111,7 @@ struct DqArgs {
     const uint8_t* ds_scales;
     const int32_t* dboff;
     long ds_blocks;
+    int exact;                // 1: the exact options (K's token exponent folded, per-row dS exponent)
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);

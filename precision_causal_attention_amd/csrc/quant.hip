@@ -119,9 +119,25 @@ __device__ __forceinline__ uint32_t nvfp4_bf16(float x, float s) {
     return s > 0.f ? b : 0u;
 }
 
+// Largest of a non-negative value over the d/8 consecutive lanes that hold
+// one token's chunks, returned in each of them (bit patterns of non-negative
+// floats order like the values).
+template <int CPT>
+__device__ __forceinline__ float token_max(float x) {
+    uint32_t v = __float_as_uint(x);
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));    // lane ^ 1
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));    // lane ^ 2
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));   // other quad of 8
+    if constexpr (CPT == 16)
+        v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true));  // other 8 of 16
+    return __uint_as_float(v);
+}
+
 }  // namespace
 
-template <int D, bool kDO>
+// TOK: the exact options' per-token exponents (Appendix A.3): each token row
+// gets the exponent of its own maximum instead of the block's.
+template <int D, bool kDO, bool TOK>
 __global__ void __launch_bounds__(256) quantize_kernel(const QuantArgs a) {
     constexpr int CPT = D / 8;               // 16-byte bf16 chunks per token row
     constexpr int R = kBlock * CPT / 64;     // chunks per lane
@@ -164,19 +180,34 @@ __global__ void __launch_bounds__(256) quantize_kernel(const QuantArgs a) {
             }
         }
         if (tz.rot) rotate_rows<CPT, R>(v, ch);
-        float amax = 0.f;
+        // exponent of chunk row r (the block's, or with TOK the token's)
+        int er[R];
+        if constexpr (TOK) {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+            for (int r = 0; r < R; ++r) {
+                float m = 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[r][k]));
-        amax = wave_max_nonneg(amax);
-        const int e = block_exponent_uniform(amax, -127);
+                for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[r][k]));
+                er[r] = block_exponent(token_max<CPT>(m), -127);
+            }
+        } else {
+            float amax = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[r][k]));
+            amax = wave_max_nonneg(amax);
+            const int e = block_exponent_uniform(amax, -127);
+#pragma unroll
+            for (int r = 0; r < R; ++r) er[r] = e;
+        }
         // codes = E4M3(x * 2^-e): the power-of-two scaling is exact, the
         // convert rounds to nearest even.
         uint32_t packed[R][2];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int tok = tok0 + r * (64 / CPT);
+            const int e = er[r];
 #pragma unroll
             for (int k = 0; k < 2; ++k)
                 packed[r][k] = (uint32_t)pack_fp8x4(ldexpf(v[r][4 * k], -e), ldexpf(v[r][4 * k + 1], -e),
@@ -185,7 +216,21 @@ __global__ void __launch_bounds__(256) quantize_kernel(const QuantArgs a) {
                 *reinterpret_cast<uint2*>(tz.codes + ((long)(bs + tok) * H + h) * D + 8 * ch) =
                     make_uint2(packed[r][0], packed[r][1]);
         }
-        if (lane < nt) tz.scales[(long)h * a.ttot + bs + lane] = (uint8_t)(e + 127);
+        if constexpr (TOK) {
+            // lane t < 32 stores token t's exponent, held in chunk row t / G by
+            // the lanes (t % G) CPT .. + CPT - 1, G = 64 / CPT tokens per row
+            constexpr int G = 64 / CPT;
+            const int src = (lane % G) * CPT;
+            int et = 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int x = __shfl(er[r], src);
+                if (r == lane / G) et = x;
+            }
+            if (lane < nt) tz.scales[(long)h * a.ttot + bs + lane] = (uint8_t)(et + 127);
+        } else {
+            if (lane < nt) tz.scales[(long)h * a.ttot + bs + lane] = (uint8_t)(er[0] + 127);
+        }
 
         // mixed path (Section 3.4): the NVFP4 values of the same rows, one
         // scale per 16 channels of each token (lanes ch and ch ^ 1 hold the
@@ -230,7 +275,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const QuantArgs a) {
                     dot = fmaf(hi[0], bf16_to_f32(w[2 * k + 1] & 0xFFFFu), dot);
                     dot = fmaf(hi[1], bf16_to_f32(w[2 * k + 1] >> 16), dot);
                 }
-                dot = ldexpf(token_sum<CPT>(dot), e);
+                dot = ldexpf(token_sum<CPT>(dot), er[r]);
                 if (tok < nt && ch == 0) a.dvec[(long)h * a.ttot + bs + tok] = dot;
             }
         }
@@ -243,12 +288,17 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
     for (int i = 0; i < a.ntensors; ++i) chunks += (a.t[i].heads + 3) / 4;
     const dim3 grid((unsigned)chunks, (unsigned)((a.ttot + kBlock - 1) / kBlock)), block(256);
     const bool dO = a.o != nullptr;
+    // per-token exponents serve the operands of the exact options; their dO
+    // is quantized inside the dQ pass, so this launch has no D variant for them
+    if (a.per_token && dO) return hipErrorInvalidValue;
     if (a.d == 64) {
-        if (dO) hipLaunchKernelGGL((quantize_kernel<64, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((quantize_kernel<64, false>), grid, block, 0, st, a);
+        if (a.per_token) hipLaunchKernelGGL((quantize_kernel<64, false, true>), grid, block, 0, st, a);
+        else if (dO) hipLaunchKernelGGL((quantize_kernel<64, true, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((quantize_kernel<64, false, false>), grid, block, 0, st, a);
     } else {
-        if (dO) hipLaunchKernelGGL((quantize_kernel<128, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((quantize_kernel<128, false>), grid, block, 0, st, a);
+        if (a.per_token) hipLaunchKernelGGL((quantize_kernel<128, false, true>), grid, block, 0, st, a);
+        else if (dO) hipLaunchKernelGGL((quantize_kernel<128, true, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((quantize_kernel<128, false, false>), grid, block, 0, st, a);
     }
     return hipGetLastError();
 }

@@ -26,9 +26,10 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_defaults(L):
-    assert F.flamia_abi_version() == 5
+    assert F.flamia_abi_version() == 6
     o = F.flamia_default_opts()
-    assert (o.c_log2, o.tau, o.key_tile, o.rowsum, o.hadamard, o.fast_exp, o.mixed) == (4, 4, 128, 0, 0, 0, 0)
+    assert (o.c_log2, o.tau, o.key_tile, o.rowsum, o.hadamard, o.fast_exp, o.mixed, o.exact) == \
+        (4, 4, 128, 0, 0, 0, 0, 0)
     assert F.flamia_status_str(0) == "ok"
 
 
@@ -132,6 +133,23 @@ def test_mixed_path_validation(call):
     assert call(dims(), opts=o, q_mx=(FAKE, FAKE, FAKE), k_mx=(FAKE, FAKE, FAKE), ws_bytes=100) == 5
     o.mixed = 0                                                         # nv is ignored off the mixed path
     assert call(dims(), opts=o, q_mx=(FAKE, FAKE, FAKE + 2), ws_bytes=100) == 5
+
+
+@pytest.mark.parametrize("call", [call_fwd, call_bwd])
+def test_exact_options_validation(call):
+    """Appendix A.3 exact options: opts.exact is 0 or 1 and runs on the MXFP8
+    path with the unquantized row sum and the exact exponential."""
+    o = F.flamia_default_opts()
+    o.exact = 2
+    assert call(dims(), opts=o) == 4
+    o.exact = 1
+    for field, val in (("rowsum", 1), ("mixed", 1), ("fast_exp", 5)):
+        setattr(o, field, val)
+        assert call(dims(), opts=o, q_mx=(FAKE, FAKE, FAKE), k_mx=(FAKE, FAKE, FAKE)) == 4, field
+        setattr(o, field, 0)
+    assert call(dims(), opts=o, ws_bytes=100) == 5      # accepted: stops at the workspace check
+    # a workspace sized with a dS store is still enough (the options do not use it)
+    assert call(dims(doclen_cap=512), opts=o, ws_bytes=100) == 5
 
 
 def test_quantize_validation():

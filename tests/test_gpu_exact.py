@@ -1,0 +1,137 @@
+"""Parity of the exact options (FLAMIA paper, Appendix A.3 and Section 4.5) of
+the HIP library with the oracle, through the C ABI.
+
+Bit-exact: the per-token E4M3 codes and UE8M0 exponents of Q, K and V that the
+forward saves.  Tolerance as for the MXFP8 path (cosine >= 0.999, |err| <=
+2e-2 at unit scale plus the oracle's decision bounds): O, lse2, dQ, dK, dV on
+ragged small cases (d = 64 with GQA, d = 128), with the Hadamard option, with
+a workspace that has a dS store (which the options do not use), and on the
+4 x 8192 GQA and 1 x 8192 d = 128 workloads on sampled heads.  Bitwise: the
+causal invariant at EVERY earlier position of the perturbed token, and the
+same probe through the default token blocks leaks inside the block.
+"""
+import numpy as np
+import pytest
+
+from precision_causal_attention_amd import flamia as F
+from precision_causal_attention_amd import workloads as W
+
+from gpu_util import SCORE_REL_ERR, assert_close, run_hip, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "packed-2k": lambda: W.generate("packed-2k", 0),
+    "ragged-gqa-d64": lambda: W.generate(W.custom("r64", [1, 31, 33, 127, 128, 129, 255, 300, 0, 17, 64], 4, 2, 64),
+                                         1, lens=[1, 31, 33, 127, 128, 129, 255, 300, 0, 17, 64]),
+    "ragged-d128": lambda: W.generate(W.custom("r128", [5, 200, 130, 0, 77], 2, 1, 128), 2,
+                                      lens=[5, 200, 130, 0, 77]),
+    "gqa-outliers": lambda: W.generate(W.custom("go", [700, 260, 64], 8, 2, 64, outlier_frac=0.01,
+                                                outlier_gain=20.0), 3, lens=[700, 260, 64]),
+}
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.build(force=False)
+    return oracle
+
+
+def exact_opts(on=1, hadamard=0):
+    o = F.flamia_default_opts()
+    o.exact = on
+    o.hadamard = hadamard
+    return o
+
+
+def _oracle(orc, inst, hadamard=0, **kw):
+    opts = orc.Opts(exact=1, hadamard=hadamard)
+    opts.score_rel_err = SCORE_REL_ERR
+    return orc.attention(inst["q"], inst["k"], inst["v"], inst.get("do"), inst["cu_seqlens"], opts,
+                         want_tol=True, **kw)
+
+
+def _check(g, r, heads=slice(None), kvheads=slice(None)):
+    assert_close("O", g["o"][:, heads], r["o64"][:, heads], r["tol_o"][:, heads])
+    lse_err = np.abs(g["lse2"][heads] - r["lse2"][heads])
+    say(f"  lse2: max abs err {lse_err.max():.3e}")
+    assert (lse_err <= r["tol_lse"][heads] + 1e-5).all()
+    assert_close("dQ", g["dq"][:, heads], r["dq64"][:, heads], r["tol_dq"][:, heads])
+    assert_close("dK", g["dk"][:, kvheads], r["dk64"][:, kvheads], r["tol_dk"][:, kvheads])
+    assert_close("dV", g["dv"][:, kvheads], r["dv64"][:, kvheads], r["tol_dv"][:, kvheads])
+
+
+@pytest.mark.parametrize("case,doclen_cap,hadamard", [
+    ("packed-2k", 0, 0), ("ragged-gqa-d64", 0, 0), ("ragged-gqa-d64", None, 0),
+    ("ragged-d128", 0, 0), ("ragged-d128", 0, 1), ("gqa-outliers", 0, 0), ("gqa-outliers", None, 1)])
+def test_exact_forward_backward_match_oracle(orc, case, doclen_cap, hadamard):
+    inst = CASES[case]()
+    say(f"[exact fwd+bwd] {case} doclen_cap={doclen_cap} hadamard={hadamard}")
+    g = run_hip(inst, exact_opts(hadamard=hadamard), doclen_cap=doclen_cap)
+    for name in ("q", "k", "v"):
+        rc, rs = orc.quantize(inst[name], inst["cu_seqlens"],
+                              orc.Opts(exact=1, hadamard=hadamard if name != "v" else 0))
+        assert np.array_equal(g[f"{name}_codes"], rc), name
+        assert np.array_equal(g[f"{name}_scales"], rs), name
+    r = _oracle(orc, inst, hadamard=hadamard)
+    _check(g, r)
+
+
+def test_exact_causal_invariant_at_every_earlier_position():
+    """Raise the row maximum of token p of a 300-token document: O, lse2 and
+    dQ of every earlier token stay bitwise equal with the exact options (not
+    only those before p's 32-token block), and every other document is
+    untouched.  With the default token blocks the same probe moves some
+    earlier position of p's block (the residue the options close)."""
+    inst = CASES["ragged-gqa-d64"]()
+    start = int(inst["cu_seqlens"][7])
+    end = int(inst["cu_seqlens"][8])
+    p = start + 170                       # inside block [160, 192) of the document
+    say("[exact causal] ragged-gqa-d64 p=start+170")
+    leaked = set()
+    for on in (1, 0):
+        base = run_hip(inst, exact_opts(on), doclen_cap=0)
+        for name in ("q", "k", "v", "do"):
+            inst2 = dict(inst)
+            x = inst[name].copy()
+            x[p] = W.bf16_bits(W.bits_to_f32(x[p]) * 40.0 + 3.0)
+            inst2[name] = x
+            r = run_hip(inst2, exact_opts(on), doclen_cap=0)
+            same = np.array_equal(r["o"][:p], base["o"][:p]) and np.array_equal(r["dq"][:p], base["dq"][:p]) \
+                and np.array_equal(r["lse2"][:, :p], base["lse2"][:, :p])
+            if on:
+                assert same, name
+                assert not np.array_equal(r["dq"][p:end], base["dq"][p:end]), name
+            elif not same:
+                leaked.add(name)
+            for key in ("o", "dq", "dk", "dv"):
+                assert np.array_equal(r[key][end:], base[key][end:]), (name, key)
+            for key in ("dk", "dv"):
+                assert np.array_equal(r[key][:start], base[key][:start]), (name, key)
+    say(f"  default token blocks leaked through: {sorted(leaked)}")
+    assert leaked
+
+
+def test_exact_deterministic():
+    inst = CASES["gqa-outliers"]()
+    say("[exact determinism] gqa-outliers")
+    a = run_hip(inst, exact_opts(), doclen_cap=0)
+    b = run_hip(inst, exact_opts(), doclen_cap=0)
+    for key in ("o", "lse2", "dq", "dk", "dv"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("wl,heads,kvheads,nkv", [
+    ("gqa-4x8k", slice(0, 4), slice(0, 1), 8),
+    ("mixed-8k", slice(0, 1), slice(0, 1), 16)])
+def test_exact_full_size_sampled(orc, wl, heads, kvheads, nkv):
+    """Full-size workloads in the benchmark's launch configuration (no dS
+    store); the oracle computes key/value head 0 and its query heads."""
+    inst = W.generate(wl, 0)
+    say(f"[exact full] {wl} docs={len(inst['lengths'])}")
+    g = run_hip(inst, exact_opts(), doclen_cap=0)
+    km = np.zeros(nkv, np.uint8)
+    km[0] = 1
+    r = _oracle(orc, inst, kv_mask=km)
+    _check(g, r, heads=heads, kvheads=kvheads)
