@@ -34,6 +34,10 @@ Prints ONE JSON line:
 score products (forward S and its recomputation in both backward kernels)
 run on the bf16 MFMA, the other products on the FP8 one, so each kernel's
 roofline peak is the FLOP-weighted harmonic mean of the two dense peaks.
+
+--exact 1 times the call with the exact options (Appendix A.3: per-token
+operand scales, a per-query-row dS exponent for dQ); same metric and peak,
+the config records the option.
 """
 import argparse
 import ctypes
@@ -133,7 +137,7 @@ def recorded_traffic(workload, kernel, doclen_cap):
     return None
 
 
-def cpu_baseline(inst, hkv, hadamard=0, mixed=0, target_s=10.0):
+def cpu_baseline(inst, hkv, hadamard=0, mixed=0, exact=0, target_s=10.0):
     """The oracle as it stands on a sample of the workload: key/value head 0
     and its query heads (all documents) is timed first; while a call takes
     less than target_s, the sample doubles to the first n key/value heads (one
@@ -149,7 +153,7 @@ def cpu_baseline(inst, hkv, hadamard=0, mixed=0, target_s=10.0):
         km[:n] = 1
         t0 = time.perf_counter()
         oracle.attention(inst["q"], inst["k"], inst["v"], inst["do"], inst["cu_seqlens"],
-                         oracle.Opts(hadamard=hadamard, mixed=mixed), kv_mask=km, want_f64=False)
+                         oracle.Opts(hadamard=hadamard, mixed=mixed, exact=exact), kv_mask=km, want_f64=False)
         return time.perf_counter() - t0
 
     n, dt = 1, run(1)
@@ -162,7 +166,8 @@ def cpu_baseline(inst, hkv, hadamard=0, mixed=0, target_s=10.0):
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"key/value head{'s 0-' + str(n - 1) if n > 1 else ' 0'} of {hkv} ({n * G} of {hq} query heads), all "
                       f"{len(inst['lengths'])} documents, forward + backward incl. quantization"
-                      f"{' (mixed NVFP4/FP8 path)' if mixed else ''}; {dt:.1f} s wall"}
+                      f"{' (mixed NVFP4/FP8 path)' if mixed else ''}{' (exact options)' if exact else ''}; "
+                      f"{dt:.1f} s wall"}
 
 
 def inference_bench(args, call, q, k, v, cu, stream, hip, wl, inst, doclen_cap):
@@ -233,12 +238,17 @@ def main():
     ap.add_argument("--mixed", type=int, default=0, choices=(0, 1),
                     help="1: the mixed NVFP4/FP8 path (NVFP4 Q and K for the scores; a separate "
                          "metric, measured on the workload mixed-8k)")
+    ap.add_argument("--exact", type=int, default=0, choices=(0, 1),
+                    help="1: the exact options (per-token operand scales, per-query-row dS exponent)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a fill and a widening copy of this many MiB (known-size "
                          "references for hardware byte counters collected over the same run)")
     args = ap.parse_args()
     if args.mixed and args.inference > 0:
         print("the approximate exponential is offered on the MXFP8 path only", file=sys.stderr)
+        sys.exit(2)
+    if args.exact and (args.mixed or args.inference >= 0):
+        print("the exact options run the MXFP8 training call only", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build runs the attention call on a single "
@@ -264,6 +274,7 @@ def main():
     opts = F.flamia_default_opts()
     opts.hadamard = args.hadamard
     opts.mixed = args.mixed
+    opts.exact = args.exact
     call = F.TrainingCall(T, hq, hkv, d, ndocs_cap=ndocs, opts=opts, doclen_cap=doclen_cap)
     hip = Hip()
     BWD_PHASES = BWD_PHASES_FUSED if doclen_cap == 0 else BWD_PHASES_STORE
@@ -396,16 +407,16 @@ def main():
         "config": {"workload": wl.name, "rows": wl.rows, "row_len": wl.row_len, "tokens": T, "hq": hq,
                    "hkv": hkv, "d": d, "docs": ndocs, "sum_L2": sum_l2, "seed": args.seed,
                    "doc_law": wl.docs, "doclen_cap": doclen_cap, "hadamard": args.hadamard,
-                   "mixed": args.mixed, "parallelism": "single-gpu"},
+                   "mixed": args.mixed, "exact": args.exact, "parallelism": "single-gpu"},
         "graph_ms_per_step": round(graph_ms_step, 4),
         "phases_ms": {p: round(t, 4) for p, t in phases.items()},
         "roofline": {"kernel": dom, "kernel_ms": round(dom_ms, 4), "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None if args.mixed else recorded_traffic(wl.name, dom, doclen_cap)},
+                     "traffic": None if (args.mixed or args.exact) else recorded_traffic(wl.name, dom, doclen_cap)},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")
-        result["cpu_baseline"] = cpu_baseline(inst, hkv, args.hadamard, args.mixed)
+        result["cpu_baseline"] = cpu_baseline(inst, hkv, args.hadamard, args.mixed, args.exact)
     print(json.dumps(result), flush=True)
 
 

@@ -72,9 +72,12 @@ __device__ __forceinline__ constexpr int pair_class(int i) {
 // At least two workgroups per CU (two waves per SIMD) at both head
 // dimensions: at d = 128 one wave per SIMD leaves the matrix-core and memory
 // latencies exposed (the kernel ran 35% longer), and the few registers the
-// mixed and inference variants spill cost less than that.
+// mixed and inference variants spill cost less than that.  The exact
+// options' d = 64 variant is held to three waves per SIMD, like the default
+// one reaches by itself: three spilled registers cost less than the lost
+// wave (the forward ran 14% faster).
 template <int D, int ROWSUM, int FAST, int MIX, int EXACT>
-__global__ void __launch_bounds__(256, 2) fwd_kernel(const FwdArgs a) {
+__global__ void __launch_bounds__(256, (D == 64 && EXACT) ? 3 : 2) fwd_kernel(const FwdArgs a) {
     constexpr int KC = D / 64;                    // 64-channel contraction steps of S
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;                    // 32-row channel tiles of O^T
