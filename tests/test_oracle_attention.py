@@ -8,7 +8,7 @@ It is pinned here against things that do not go through it:
   document (Section 2 of the paper: S = QK^T/sqrt(d), P = softmax(S), O = PV),
   and its gradient from torch autograd and from central finite differences;
 - the softmax-gradient identity sum_j dS_ij = 0 (Section 3.3);
-- online (tiled) == two-pass in exact mode;
+- online (tiled) == two-pass in the unquantized mode;
 - the single-tile closed form of the quantized forward;
 - the c + tau <= log2(448) bound and its failing example (Appendix B.1);
 - gradients of the *dequantized* function (the only losses left are the
