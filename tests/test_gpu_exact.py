@@ -5,8 +5,10 @@ Bit-exact: the per-token E4M3 codes and UE8M0 exponents of Q, K and V that the
 forward saves.  Tolerance as for the MXFP8 path (cosine >= 0.999, |err| <=
 2e-2 at unit scale plus the oracle's decision bounds): O, lse2, dQ, dK, dV on
 ragged small cases (d = 64 with GQA, d = 128), with the Hadamard option, with
-a workspace that has a dS store (which the options do not use), and on the
-4 x 8192 GQA and 1 x 8192 d = 128 workloads on sampled heads.  Bitwise: the
+a workspace that has a dS store (which the options do not use), on
+degenerate documents (zero Q = K, V, dO; equal keys) and one whose token rows
+lie up to 2^38 apart, on 5000 short documents, and on the 4 x 8192 GQA,
+1 x 8192 and 1 x 32768 d = 128 workloads on sampled heads.  Bitwise: the
 causal invariant at EVERY earlier position of the perturbed token, and the
 same probe through the default token blocks leaks inside the block.
 """
@@ -135,3 +137,79 @@ def test_exact_full_size_sampled(orc, wl, heads, kvheads, nkv):
     km[0] = 1
     r = _oracle(orc, inst, kv_mask=km)
     _check(g, r, heads=heads, kvheads=kvheads)
+
+
+def _check_rows(g, r, rows, heads=slice(None), kvheads=slice(None)):
+    assert_close("O", g["o"][rows][:, heads], r["o64"][rows][:, heads], r["tol_o"][rows][:, heads])
+    lse_err = np.abs(g["lse2"][heads][:, rows] - r["lse2"][heads][:, rows])
+    say(f"  lse2: max abs err {lse_err.max():.3e}")
+    assert (lse_err <= r["tol_lse"][heads][:, rows] + 1e-5).all()
+    assert_close("dQ", g["dq"][rows][:, heads], r["dq64"][rows][:, heads], r["tol_dq"][rows][:, heads])
+    assert_close("dK", g["dk"][rows][:, kvheads], r["dk64"][rows][:, kvheads], r["tol_dk"][rows][:, kvheads])
+    assert_close("dV", g["dv"][rows][:, kvheads], r["dv64"][rows][:, kvheads], r["tol_dv"][rows][:, kvheads])
+
+
+def test_exact_degenerate_and_wide_range_documents(orc):
+    """Q = K = 0, V = 0, dO = 0, all keys equal, and a document whose token
+    rows are scaled by powers of two (V and dO from 2^-30 to 2^8, Q and K
+    from 2^-30 to 1, which keeps the scores within a few units): token
+    exponents far apart inside every block, so the folds reach deep into the
+    E4M3 subnormals and to zero."""
+    lens = [200, 150, 130, 180, 170, 160]
+    inst = W.generate(W.custom("degenerate-exact", lens, 4, 2, 64), 11, lens=lens)
+    cu = inst["cu_seqlens"]
+    zero = W.bf16_bits(np.zeros(1, np.float32))[0]
+    inst["q"][cu[0]:cu[1]] = zero
+    inst["k"][cu[0]:cu[1]] = zero
+    inst["v"][cu[1]:cu[2]] = zero
+    inst["do"][cu[2]:cu[3]] = zero
+    inst["k"][cu[3]:cu[4]] = inst["k"][cu[3]]
+    rng = np.random.default_rng(12)
+    a, b = int(cu[5]), int(cu[6])
+    for name in ("q", "k", "v", "do"):
+        x = W.bits_to_f32(inst[name][a:b])
+        hi = 1 if name in ("q", "k") else 9
+        x = x * np.exp2(rng.integers(-30, hi, (b - a, x.shape[1], 1))).astype(np.float32)
+        inst[name][a:b] = W.bf16_bits(x)
+    say("[exact degenerate + wide range]")
+    g = run_hip(inst, exact_opts(), doclen_cap=0)
+    for name in ("q", "k", "v"):
+        rc, rs = orc.quantize(inst[name], cu, orc.Opts(exact=1))
+        assert np.array_equal(g[f"{name}_codes"], rc) and np.array_equal(g[f"{name}_scales"], rs), name
+    r = _oracle(orc, inst)
+    _check_rows(g, r, slice(None))
+    for key, rg in (("dq", (cu[2], cu[3])), ("dk", (cu[2], cu[3])), ("dv", (cu[2], cu[3])),
+                    ("o", (cu[1], cu[2])), ("dq", (cu[1], cu[2])), ("dk", (cu[1], cu[2])),
+                    ("dq", (cu[0], cu[1])), ("dk", (cu[0], cu[1]))):
+        assert not np.any(W.bits_to_f32(g[key][rg[0]:rg[1]])), key
+
+
+def test_exact_many_short_documents(orc):
+    """5000 documents of 1 to 40 tokens: nearly every block is a diagonal,
+    partial one."""
+    rng = np.random.default_rng(95)
+    lens = [int(x) for x in rng.integers(1, 41, size=5000)]
+    inst = W.generate(W.custom("many-exact", lens, 2, 1, 128), 13, lens=lens)
+    say(f"[exact many documents] docs={len(lens)} T={sum(lens)}")
+    g = run_hip(inst, exact_opts(), doclen_cap=0)
+    r = _oracle(orc, inst)
+    _check_rows(g, r, slice(None))
+
+
+def test_exact_long_32k_sampled_head(orc):
+    """The 1 x 32768, 16-head, d = 128 workload; head 0 of every document but
+    the longest (one binary64 unit of that length takes the oracle about a
+    minute)."""
+    inst = W.generate("long-32k", 0)
+    lens = inst["lengths"]
+    cu = inst["cu_seqlens"]
+    skip = int(np.argmax(lens))
+    say(f"[exact long-32k] docs={len(lens)} longest={max(lens)} (not compared)")
+    g = run_hip(inst, exact_opts(), doclen_cap=0)
+    km = np.zeros(16, np.uint8)
+    km[0] = 1
+    dm = np.ones(len(lens), np.uint8)
+    dm[skip] = 0
+    r = _oracle(orc, inst, kv_mask=km, doc_mask=dm)
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in range(len(lens)) if i != skip])
+    _check_rows(g, r, rows, heads=slice(0, 1), kvheads=slice(0, 1))
