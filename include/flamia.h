@@ -2,7 +2,8 @@
  * flamia.h -- C ABI of an MI355X (gfx950) library for microscaled (MXFP8, and
  * mixed NVFP4/FP8) causal flash attention over packed variable-length
  * documents: the training call (forward and backward) with the operand
- * quantization fused in.
+ * quantization fused in; options for the Hadamard rotation, the inference
+ * exponential and the exact options (per-token operand scales).
  *
  * Method: "FLAMIA: FLAsh MIcroscaling Attention for Fast and Causally Safe
  * Training on Blackwell".  Section numbers below refer to that paper.
