@@ -419,6 +419,18 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
         } else if (!skipped(1)) {
             dvdk(B, pbc, dsc, es);
         }
+        // Scheduling hint for the unmasked steps: spread the step's eight
+        // MFMAs over its VALU stream (one per 24 VALU instructions), so that
+        // the matrix pipe keeps working through the second block's softmax
+        // (2% faster than the compiler's own order, which issues the last
+        // products early and leaves the tail of the step without any).
+        if constexpr (!MASK) {
+#pragma unroll
+            for (int g8 = 0; g8 < 8; ++g8) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);   // then 24 VALU
+            }
+        }
         prv = cur;
         cur = cur + 1 == NBUF ? 0 : cur + 1;
         return more;
