@@ -1,4 +1,6 @@
-"""A whole training call (flamia_fwd + flamia_bwd) captured as one HIP graph.
+"""A whole training call (flamia_fwd + flamia_bwd) captured as one HIP graph,
+with the default options, the Hadamard rotation, the mixed NVFP4/FP8 path and
+the exact options.
 
 The work lists are rebuilt on the device by every call and the library
 enqueues kernels only (no allocation, no memset, no host synchronization),
@@ -30,18 +32,31 @@ def _snapshot(call):
     return out
 
 
-@pytest.mark.parametrize("doclen_cap", [0, None])
-def test_graph_replays_match_eager(doclen_cap):
+def _opts(variant):
+    o = F.flamia_default_opts()
+    if variant == "hadamard":
+        o.hadamard = 1
+    elif variant == "mixed":
+        o.mixed = 1
+    elif variant == "exact":
+        o.exact = 1
+    return o
+
+
+@pytest.mark.parametrize("variant,doclen_cap,d", [
+    ("default", 0, 64), ("default", None, 64), ("hadamard", None, 128), ("mixed", 0, 128), ("exact", 0, 64),
+    ("exact", 0, 128)])
+def test_graph_replays_match_eager(variant, doclen_cap, d):
     lens = [1, 31, 33, 127, 128, 129, 255, 300, 0, 17, 64]
-    inst = W.generate(W.custom("r64", lens, 4, 2, 64), 1, lens=lens)
-    say(f"[graph replay] ragged-gqa-d64 doclen_cap={doclen_cap}")
+    inst = W.generate(W.custom("ragged", lens, 4, 2, d), 1, lens=lens)
+    say(f"[graph replay] ragged-gqa d={d} {variant} doclen_cap={doclen_cap}")
     T, hq, d = inst["q"].shape
     hkv = inst["k"].shape[1]
     if doclen_cap is None:
         doclen_cap = max(lens)
     q, k, v, do = (dev_bf16(inst[n]) for n in ("q", "k", "v", "do"))
     cu = torch.from_numpy(inst["cu_seqlens"]).cuda()
-    call = F.TrainingCall(T, hq, hkv, d, len(lens), doclen_cap=doclen_cap)
+    call = F.TrainingCall(T, hq, hkv, d, len(lens), opts=_opts(variant), doclen_cap=doclen_cap)
 
     call.forward(q, k, v, cu)
     call.backward(do, cu)
