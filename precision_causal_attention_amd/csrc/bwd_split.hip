@@ -85,11 +85,28 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     constexpr int NQN = MIX ? 2 * NQ : 1;
     __shared__ SplitSmem<MIX, EXACT> sm;
 
-    const int ti = (int)blockIdx.x / a.hkv;
-    if (ti >= *a.ntiles) return;
+    // Persistent workgroups: one per CU (an eight-wave workgroup fills a CU's
+    // registers).  Workgroup b takes item b of the cost-ordered list first,
+    // then the next unclaimed one from a work queue (a counter the work-list
+    // kernel zeroes), as the hardware dispatcher would hand out workgroups,
+    // but without relaunching one per item: that left the CU idle between
+    // items (thousands of cycles each, measured), since no second workgroup
+    // fits to cover the gap.  The next item is claimed at the start of the
+    // current one, so the atomic's latency is hidden.  Every workgroup leaves
+    // the loop once the counter passes the item count.  The mixed path's
+    // variant keeps one workgroup per item: the loop's extra live registers
+    // make it spill (8% slower).
+    constexpr bool PERSIST = !MIX;
+    __shared__ int next_item;
+    const int nitems = *a.ntiles * a.hkv;
+    int item = (int)blockIdx.x;
+    while (item < nitems) {
+    int claim = 0;
+    if (PERSIST && threadIdx.x == 0) claim = (int)gridDim.x + atomicAdd(a.queue, 1);
+    const int ti = item / a.hkv;
     const int4 it = a.tiles[ti];
     const int k0 = it.x, ds = it.y, de = it.z, doc = it.w;
-    const int g = (int)blockIdx.x - ti * a.hkv;
+    const int g = item - ti * a.hkv;
     const bool use_store = STORE && a.ntiles[1] != 0;
     const long doc_blk = use_store ? (long)a.dboff[doc] : 0;
     const int G = a.hq / a.hkv;
@@ -428,12 +445,33 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
                     pack_bf16x2(dvt[t][4 * j + 2], dvt[t][4 * j + 3]));
             }
     }
+    if constexpr (!PERSIST) break;
+    // hand the claimed item to every wave; past this barrier the item's step
+    // buffers and epilogue tiles are read no more
+    if (threadIdx.x == 0) next_item = claim;
+    __syncthreads();
+    item = next_item;
+    }   // work items
 }
 
 hipError_t launch_bwd_split(const BwdArgs& a, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
     const bool store = a.ds_blocks > 0;
-    const dim3 g((unsigned)grid), b(512);
+    // persistent: at most one workgroup per CU (grid = the item capacity
+    // otherwise); the device's CU count, read once per device
+    static int cus[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (cus[dev] == 0) {
+        int n = 0;
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        cus[dev] = n > 0 ? n : 1;
+    }
+    const long pgrid = (a.qn || grid < cus[dev]) ? grid : cus[dev];
+    const dim3 g((unsigned)pgrid), b(512);
     if (a.exact) {
         if (store || a.qn) return hipErrorInvalidValue;
         hipLaunchKernelGGL((bwd_split_kernel<false, 0, 1>), g, b, 0, st, a);

@@ -78,6 +78,7 @@ struct BwdArgs {
     uint16_t *dk, *dv;
     const int4* tiles;
     const int32_t* ntiles;    // ntiles[1] != 0: store dS-hat blocks
+    int32_t* queue;           // work-queue counter of the persistent d = 128 pass (zeroed by the work lists)
     int ttot, hq, hkv;
     float c1, scale;
     int hadamard;             // 1: rotate dK back (Q and K were rotated)

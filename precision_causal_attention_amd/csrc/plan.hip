@@ -16,7 +16,9 @@
 // workgroup index, heads innermost.
 //
 // ctrl layout (int32): [0] number of tiles, [1] 1 if the backward's dS store
-// holds this call's blocks (capacity given and not exceeded), else 0.  The
+// holds this call's blocks (capacity given and not exceeded), else 0, [2] the
+// work-queue counter of the persistent key-major pass at d = 128 (zeroed here,
+// by every call, before that pass runs).  The
 // placement cursors of the cost classes live in LDS.  The dS block offsets of
 // the documents go to dboff.
 #include "device.h"
@@ -99,7 +101,10 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __
     // hist[c + 1] (classes by decreasing cost) and hist[1] is the total
     block_scan(hist, C1, true, wsum);
     const int total = C1 > 1 ? (int)min((long)hist[1], max_tiles) : 0;
-    if (tid == 0) ctrl[0] = total;
+    if (tid == 0) {
+        ctrl[0] = total;
+        ctrl[2] = 0;
+    }
     // exclusive prefix of tile counts over documents
     const bool lds_pref = ndocs < kPrefixLds;
     {
