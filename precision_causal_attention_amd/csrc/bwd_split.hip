@@ -454,23 +454,32 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     }   // work items
 }
 
-hipError_t launch_bwd_split(const BwdArgs& a, long grid, hipStream_t st) {
-    if (grid <= 0) return hipSuccess;
-    const bool store = a.ds_blocks > 0;
-    // persistent: at most one workgroup per CU (grid = the item capacity
-    // otherwise); the device's CU count, read once per device
+hipError_t device_cus(int* n) {
+    // the current device's CU count, read once per device
     static int cus[64] = {0};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     if (cus[dev] == 0) {
-        int n = 0;
-        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        int v = 0;
+        e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        cus[dev] = n > 0 ? n : 1;
+        cus[dev] = v > 0 ? v : 1;
     }
-    const long pgrid = (a.qn || grid < cus[dev]) ? grid : cus[dev];
+    *n = cus[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_bwd_split(const BwdArgs& a, long grid, hipStream_t st) {
+    if (grid <= 0) return hipSuccess;
+    const bool store = a.ds_blocks > 0;
+    // persistent: at most one workgroup per CU (grid = the item capacity
+    // otherwise)
+    int cus = 0;
+    const hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    const long pgrid = (a.qn || grid < cus) ? grid : cus;
     const dim3 g((unsigned)pgrid), b(512);
     if (a.exact) {
         if (store || a.qn) return hipErrorInvalidValue;

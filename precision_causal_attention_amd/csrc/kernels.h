@@ -120,6 +120,7 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, int d, long grid, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, int d, long grid, hipStream_t st);
 hipError_t launch_bwd_split(const BwdArgs& a, long grid, hipStream_t st);   // d = 128
+hipError_t device_cus(int* n);   // CU count of the current device (cached per device)
 hipError_t launch_dq(const DqArgs& a, int d, long grid, hipStream_t st);
 hipError_t launch_dq_store(const DqArgs& a, int d, long grid, hipStream_t st);
 
