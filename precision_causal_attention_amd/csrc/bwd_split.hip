@@ -91,9 +91,11 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     // kernel zeroes), as the hardware dispatcher would hand out workgroups,
     // but without relaunching one per item: that left the CU idle between
     // items (thousands of cycles each, measured), since no second workgroup
-    // fits to cover the gap.  The next item is claimed at the start of the
-    // current one, so the atomic's latency is hidden.  Every workgroup leaves
-    // the loop once the counter passes the item count.  The mixed path's
+    // fits to cover the gap.  The next item is claimed during the current
+    // one's last step, which hides the atomic's latency; claiming at the start
+    // held a claimed item behind a long current one (30% slower where a few
+    // long items set the time).  Every workgroup leaves the loop once the
+    // counter passes the item count.  The mixed path's
     // variant keeps one workgroup per item: the loop's extra live registers
     // make it spill (8% slower).
     constexpr bool PERSIST = !MIX;
@@ -101,8 +103,7 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     const int nitems = *a.ntiles * a.hkv;
     int item = (int)blockIdx.x;
     while (item < nitems) {
-    int claim = 0;
-    if (PERSIST && threadIdx.x == 0) claim = (int)gridDim.x + atomicAdd(a.queue, 1);
+    int claim = 0;   // the next item, claimed during this item's last step
     const int ti = item / a.hkv;
     const int4 it = a.tiles[ti];
     const int k0 = it.x, ds = it.y, de = it.z, doc = it.w;
@@ -247,6 +248,7 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
         q0 += kSStep;
         if (q0 >= L) { q0 = kt0; ++hh; }
         const bool more = hh < G;
+        if (PERSIST && !more && threadIdx.x == 0) claim = (int)gridDim.x + atomicAdd(a.queue, 1);
         flush_store();
         load_step(g * G + min(hh, G - 1), q0);
 
