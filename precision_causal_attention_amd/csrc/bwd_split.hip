@@ -21,6 +21,7 @@
 // Exact options (Appendix A.3): the same folds as the d = 64 kernel (dO's
 // token exponent into P-hat_b relative to its 32-query block maximum, Q's
 // into dS).
+#include <atomic>
 #include <type_traits>
 
 #include "device.h"
@@ -457,19 +458,22 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
 }
 
 hipError_t device_cus(int* n) {
-    // the current device's CU count, read once per device
-    static int cus[64] = {0};
+    // the current device's CU count, read once per device (host threads may
+    // race to fill an entry; they store the same value)
+    static std::atomic<int> cus[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (cus[dev] == 0) {
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         int v = 0;
         e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        cus[dev] = v > 0 ? v : 1;
+        c = v > 0 ? v : 1;
+        cus[dev].store(c, std::memory_order_relaxed);
     }
-    *n = cus[dev];
+    *n = c;
     return hipSuccess;
 }
 
