@@ -224,3 +224,22 @@ def test_causal_invariant():
         for key in ("dk", "dv"):
             assert np.array_equal(r[key][:start], base[key][:start]), (name, key)
             assert np.array_equal(r[key][end:], base[key][end:]), (name, key)
+
+
+def test_many_items_d128_store_equals_rebuild(orc):
+    """The d = 128 key-major pass keeps one workgroup per CU and hands out
+    items from a work queue; a call with more items than CUs (8 documents of
+    512 tokens, 16 heads: 512 items) exercises the claiming in both of its
+    variants: the dS store path and the rebuilding path give the same bits,
+    and head 0 matches the oracle."""
+    lens = [512] * 8
+    inst = W.generate(W.custom("items-d128", lens, 16, 16, 128), 21, lens=lens)
+    say("[many items d128] 8 x 512, 16 heads")
+    a = run_hip(inst, doclen_cap=512)
+    b = run_hip(inst, doclen_cap=0)
+    for key in ("o", "lse2", "dq", "dk", "dv"):
+        assert np.array_equal(a[key], b[key]), key
+    km = np.zeros(16, np.uint8)
+    km[0] = 1
+    r = _oracle(orc, inst, kv_mask=km)
+    _check_all(b, r, heads=slice(0, 1), kvheads=slice(0, 1))
