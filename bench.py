@@ -251,7 +251,7 @@ def main():
         print("the exact options run the MXFP8 training call only", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build runs the attention call on a single "
+        print(f"bench.py measures one GPU only (the library runs each attention call on a single "
               f"MI355X); --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
