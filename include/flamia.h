@@ -175,6 +175,9 @@ size_t flamia_workspace_bytes(const flamia_dims_t *dims, const flamia_opts_t *op
  *            out.nv is non-NULL also the NVFP4 values of the same rows (the
  *            mixed path's form, see the conventions above)
  * No workspace.  heads must be >= 1; only dims->ttot, ndocs and d are read.
+ * The blocks are always 32 tokens and no rotation is applied: the per-token
+ * exponents of the exact options and the rotated Q and K of the Hadamard
+ * option are written by flamia_fwd into the q_mx, k_mx, v_mx it returns.
  */
 flamia_status_t flamia_quantize(const flamia_dims_t *dims, int32_t heads, const uint16_t *x,
                                 const int32_t *cu_seqlens, flamia_mx_t out, void *stream);
