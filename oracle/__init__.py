@@ -48,9 +48,9 @@ class _Params(ctypes.Structure):
         ("hkv", ctypes.c_int32), ("d", ctypes.c_int32), ("c_log2", ctypes.c_int32),
         ("tau", ctypes.c_int32), ("key_tile", ctypes.c_int32), ("quant", ctypes.c_int32),
         ("rowsum", ctypes.c_int32), ("softmax_scale", ctypes.c_double),
-        ("unsafe_bound", ctypes.c_int32), ("score_rel_err", ctypes.c_double),
+        ("unsafe_bound", ctypes.c_int32),
         ("hadamard", ctypes.c_int32), ("fast_exp", ctypes.c_int32), ("mixed", ctypes.c_int32),
-        ("exact", ctypes.c_int32),
+        ("exact", ctypes.c_int32), ("dot_noise", ctypes.c_double), ("noise_seed", ctypes.c_int64),
     ]
 
 
@@ -73,7 +73,7 @@ def _load():
         lib.orc_quantize.restype = ctypes.c_int
         lib.orc_quantize.argtypes = [ctypes.POINTER(_Params), ctypes.c_int, P, P, P, P]
         lib.orc_attention.restype = ctypes.c_int
-        lib.orc_attention.argtypes = [ctypes.POINTER(_Params)] + [P] * 23
+        lib.orc_attention.argtypes = [ctypes.POINTER(_Params)] + [P] * 18
         lib.orc_e4m3_encode_array.argtypes = [P, ctypes.c_long, P]
         lib.orc_e4m3_value_array.argtypes = [P, ctypes.c_long, P]
         lib.orc_scale_exp_array.argtypes = [P, ctypes.c_long, ctypes.c_int, P]
@@ -106,18 +106,24 @@ class Opts:
     rowsum: int = 0
     softmax_scale: float = 0.0
     unsafe_bound: int = 0
-    score_rel_err: float = 0.0   # > 0 with want_tol: decision-sensitivity bounds
     hadamard: int = 0            # 1: Hadamard rotation of Q and K (Section 3.4, Appendix A.2)
     fast_exp: int = 0            # k of 8 key-pair classes use Schraudolph's exponential (forward only)
     mixed: int = 0               # 1: scores from NVFP4 Q and K (Section 3.4 mixed path)
     exact: int = 0               # 1: the exact options (Appendix A.3): per-token operand
                                  # exponents, a per-query-row dS exponent for dQ
+    # Test hook, not part of the method: > 0 adds u * dot_noise * (largest
+    # single product) to every score and dP dot product, u in [-1, 1) hashed
+    # from (noise_seed, head, i, j), the same in the forward and the backward
+    # (a model of a matrix core's reduction error).
+    dot_noise: float = 0.0
+    noise_seed: int = 0
 
 
 def _params(ttot, ndocs, hq, hkv, d, opts: Opts) -> _Params:
     return _Params(ttot, ndocs, hq, hkv, d, opts.c_log2, opts.tau, opts.key_tile, opts.quant,
-                   opts.rowsum, float(opts.softmax_scale), opts.unsafe_bound, float(opts.score_rel_err),
-                   opts.hadamard, opts.fast_exp, opts.mixed, opts.exact)
+                   opts.rowsum, float(opts.softmax_scale), opts.unsafe_bound,
+                   opts.hadamard, opts.fast_exp, opts.mixed, opts.exact, float(opts.dot_noise),
+                   int(opts.noise_seed))
 
 
 def max_threads() -> int:
@@ -215,19 +221,15 @@ def quantize(x_bits: np.ndarray, cu_seqlens: np.ndarray, opts: Opts | None = Non
 
 # ---- attention ---------------------------------------------------------------
 def attention(q_bits, k_bits, v_bits, do_bits, cu_seqlens, opts: Opts | None = None,
-              kv_mask=None, doc_mask=None, want_f64: bool = True, check: bool = True,
-              want_tol: bool = False):
+              kv_mask=None, doc_mask=None, want_f64: bool = True, check: bool = True):
     """Forward (+ backward when do_bits is not None) of the oracle.
 
     q/do: uint16 bf16 patterns [T, Hq, d]; k/v: [T, Hkv, d].  Returns a dict with
     o (bf16 bits), lse2 [Hq,T] fp32, D [Hq,T], dq/dk/dv (bf16 bits) and, with
     want_f64, the binary64 values before output rounding (o64, dq64, dk64, dv64).
     Masks select key/value heads and documents; unselected entries stay zero.
-    With want_tol and opts.score_rel_err > 0 it also returns tol_o [T,Hq,d],
-    tol_lse [Hq,T], tol_dv / tol_dk [T,Hkv,d] and tol_dq [T,Hq,d]: how far each
-    output can move when a
-    quantization decision lies within an implementation's score-error band of
-    its threshold (test bookkeeping, not part of the method).
+    stats = [P-hat entries that saturated, dS entries, nonzero dS entries
+    whose dS-hat code is 0, unused].
     """
     opts = opts or Opts()
     q = np.ascontiguousarray(q_bits, dtype=np.uint16)
@@ -246,12 +248,6 @@ def attention(q_bits, k_bits, v_bits, do_bits, cu_seqlens, opts: Opts | None = N
         "o64": np.zeros((T, Hq, d), np.float64) if want_f64 else None,
         "stats": np.zeros(4, np.int64),
     }
-    if want_tol:
-        r["tol_o"] = np.zeros((T, Hq, d), np.float64)
-        r["tol_lse"] = np.zeros((Hq, T), np.float64)
-        r["tol_dv"] = np.zeros((T, Hkv, d), np.float64) if do is not None else None
-        r["tol_dq"] = np.zeros((T, Hq, d), np.float64) if do is not None else None
-        r["tol_dk"] = np.zeros((T, Hkv, d), np.float64) if do is not None else None
     if do is not None:
         r.update({
             "D": np.zeros((Hq, T), np.float64),
@@ -267,8 +263,7 @@ def attention(q_bits, k_bits, v_bits, do_bits, cu_seqlens, opts: Opts | None = N
         ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(cu), _ptr(km), _ptr(dm),
         _ptr(g("o64")), _ptr(r["o"]), _ptr(r["lse2"]), _ptr(g("D")),
         _ptr(g("dq64")), _ptr(g("dk64")), _ptr(g("dv64")),
-        _ptr(g("dq")), _ptr(g("dk")), _ptr(g("dv")), _ptr(r["stats"]),
-        _ptr(g("tol_o")), _ptr(g("tol_lse")), _ptr(g("tol_dv")), _ptr(g("tol_dq")), _ptr(g("tol_dk")))
+        _ptr(g("dq")), _ptr(g("dk")), _ptr(g("dv")), _ptr(r["stats"]))
     r["rc"] = rc
     if check and rc != ORC_OK:
         raise RuntimeError(f"orc_attention failed: {rc}")

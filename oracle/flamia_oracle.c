@@ -77,14 +77,6 @@ typedef struct {
     int32_t rowsum;       /* 0: unquantized p, 1: represented value(P-hat)/2^c */
     double softmax_scale; /* <= 0 selects 1/sqrt(d) */
     int32_t unsafe_bound; /* 1 skips the c + tau <= 8 check (negative tests only) */
-    /* Tolerance bookkeeping (test infrastructure, not part of the method):
-     * relative error bound of an implementation's score dot products, as a
-     * fraction of the largest single product |q_k k_k|.  When > 0 and the
-     * tol_* outputs are requested, the oracle reports for every output element
-     * how far it can move when a quantization decision (a P-hat or P-hat_b
-     * code, a running-maximum replacement) lies within that error band of its
-     * rounding or comparison threshold. */
-    double score_rel_err;
     /* Hadamard rotation of Q and K before quantization (Section 3.4 and
      * Appendix A.2): 0 off, 1 on. */
     int32_t hadamard;
@@ -108,6 +100,10 @@ typedef struct {
      * fwd_row and unit_run).  Every output of query row i then depends on
      * tokens <= i only.  Not combined with rowsum = 1, fast_exp or mixed. */
     int32_t exact;
+    /* Test hook, not part of the method (zero by default): a model of a
+     * kernel's dot-product error, see score_dot below. */
+    double dot_noise;
+    int64_t noise_seed;
 } orc_params;
 
 /* ---------------------------------------------------------------------------
@@ -388,6 +384,7 @@ int orc_quantize(const orc_params *p, int heads, const uint16_t *x, const int32_
     return err;
 }
 
+
 /* ---------------------------------------------------------------------------
  * Attention.  One unit = one document x one key/value head (all G query heads
  * of the group), so every statistic stays inside the document.
@@ -397,66 +394,7 @@ typedef struct {
     double *dq64, *dk64, *dv64; uint16_t *dq16, *dk16, *dv16;
     int64_t *stats;   /* [0] P-hat entries that saturated, [1] dS entries
                          (causal, in-document), [2] nonzero dS quantized to 0 */
-    double *tol_o, *tol_lse, *tol_dv, *tol_dq, *tol_dk;   /* decision-sensitivity bounds */
 } orc_out;
-
-/* ---------------------------------------------------------------------------
- * Decision-sensitivity helpers (test infrastructure).
- * ------------------------------------------------------------------------- */
-static double e4m3_spacing(double y)
-{
-    /* distance from value(code(y)) to the next larger code value */
-    uint8_t c = orc_e4m3_encode(fabs(y));
-    if (c >= 0x7E) return 32.0;
-    return orc_e4m3_value((uint8_t)(c + 1)) - orc_e4m3_value(c);
-}
-
-/* Largest change of the represented value of E4M3(y) when log2(y) moves by
- * at most r; `loose` widens it to one code step regardless. */
-static double code_swing(double y, double r, int loose)
-{
-    double lo = orc_e4m3_value(orc_e4m3_encode(y * exp2(-r)));
-    double hi = orc_e4m3_value(orc_e4m3_encode(y * exp2(r)));
-    double sw = hi - lo;
-    if (loose) {
-        double sp = e4m3_spacing(y);
-        if (sp > sw) sw = sp;
-    }
-    return sw;
-}
-
-/* E4M3 value of v scaled by 2^-e, scaled back */
-static double deq_at(double v, int e)
-{
-    return ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(v, -e))), e);
-}
-
-/* Largest change of deq_at(v, e) when v moves by at most b and e is any of
- * es[0..2], measured from ref (the value actually taken). */
-static double deq_swing(double v, double b, const int *es, double ref)
-{
-    double sw = 0.0;
-    for (int a = 0; a < 3; ++a) {
-        double t1 = fabs(deq_at(v + b, es[a]) - ref);
-        double t2 = fabs(deq_at(v - b, es[a]) - ref);
-        if (t1 > sw) sw = t1;
-        if (t2 > sw) sw = t2;
-    }
-    return sw;
-}
-
-/* score error bound (log2 units) of one pair: the implementation's dot
- * product error plus fp32 roundings of the score pipeline */
-static double score_delta(const orc_params *p, const double *a, const double *b, int d,
-                          double c1, double x, double m)
-{
-    double mp = 0.0;
-    for (int k = 0; k < d; ++k) {
-        double t = fabs(a[k] * b[k]);
-        if (t > mp) mp = t;
-    }
-    return p->score_rel_err * mp * c1 + 0x1p-20 * (1.0 + fabs(x) + (isfinite(m) ? fabs(m) : 0.0));
-}
 
 static double dotd(const double *a, const double *b, int d)
 {
@@ -465,14 +403,44 @@ static double dotd(const double *a, const double *b, int d)
     return s;
 }
 
-/* Forward for one query row (Section 2 equations for S, P, O; Appendix B.1
- * for the fixed 2^c factor and the conditional running maximum). */
-typedef struct {
-    double *tacc;   /* [d] like acc: sum of code swings x |V| (NULL: no bookkeeping) */
-    double *delta;  /* [key_tile] per-entry score error bounds of the current tile */
-    double tol_lse; /* out: bound on |lse2 change| */
-    double *tol_o;  /* out: [d] */
-} row_tol;
+/* splitmix64 finaliser (Steele, Lea and Flood, "Fast splittable pseudorandom
+ * number generators", 2014) */
+static uint64_t mix64(uint64_t z)
+{
+    z += 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* The dot products that a kernel computes on its matrix cores: the scores
+ * q_i . k_j (forward and backward) and dP_ij = dO_i . v_j.  With dot_noise = 0
+ * (the default, and the method) this is the exact binary64 dot product.
+ * Test hook: with dot_noise > 0 the result gets u * dot_noise * max_k |a_k b_k|
+ * added, u in [-1, 1) from a hash of (noise_seed, query head h, packed token
+ * indices ti and tj, which product), so a forward score and its backward
+ * recomputation carry the same error.  It models a matrix core whose reduction
+ * is exact only to a fraction of its largest single product; the tests use it
+ * to check that the GPU comparison tolerates that much and no more. */
+static double score_dot(const orc_params *p, const double *a, const double *b, int d,
+                        int h, long ti, long tj, int which)
+{
+    double s = dotd(a, b, d);
+    if (p->dot_noise > 0.0) {
+        double mp = 0.0, u;
+        uint64_t z;
+        for (int k = 0; k < d; ++k) {
+            double t = fabs(a[k] * b[k]);
+            if (t > mp) mp = t;
+        }
+        z = mix64((uint64_t)p->noise_seed ^ mix64(((uint64_t)h << 2) | (uint64_t)which));
+        z = mix64(z ^ mix64((uint64_t)ti) ^ (mix64((uint64_t)tj) << 1));
+        u = (double)(z >> 11) * 0x1p-52 - 1.0;
+        s += u * p->dot_noise * mp;
+    }
+    return s;
+}
+
 
 /* ---------------------------------------------------------------------------
  * Schraudolph's exponential (Section 3.7; Appendix C.2).  One fp32 fused
@@ -504,45 +472,34 @@ static int key_pair_class(int j)
     return ((j >> 1) & 1) | (((j >> 3) & 1) << 1) | (((j >> 4) & 1) << 2);
 }
 
-static void fwd_row(const orc_params *p, int i, const double *qi, const double *Kt,
+/* Forward for query row i of a document (Section 2 equations for S, P, O;
+ * Appendix B.1 for the fixed 2^c factor and the conditional running maximum).
+ * Keys j <= i in tiles of B_c keys from the document start, ascending; x_ij =
+ * (q_i . k_j) s log2(e).  h and tok0 (the document's first packed token) only
+ * key the test hook of score_dot. */
+static void fwd_row(const orc_params *p, int h, long tok0, int i, const double *qi, const double *Kt,
                     const double *Vt, const int *ev, double c1, double *acc, double *x,
-                    double *o_out, double *lse_out, int64_t *sat, row_tol *rt)
+                    double *o_out, double *lse_out, int64_t *sat)
 {
     int d = p->d, B = p->key_tile, quant = p->quant;
     double m = -INFINITY, l = 0.0;
     int eblk = -1, E = 0;      /* exact options: key block of E, and E */
     double two_c = ldexp(1.0, p->c_log2);
-    /* tolerance bookkeeping (not part of the method) */
-    const int track = rt != NULL && quant != QUANT_NONE;
-    double dm = 0.0, dmax = 0.0, tl = 0.0;
-    int loose = 0;
     for (int k = 0; k < d; ++k) acc[k] = 0.0;
-    if (track) for (int k = 0; k < d; ++k) rt->tacc[k] = 0.0;
     for (int j0 = 0; j0 <= i; j0 += B) {
         int j1 = j0 + B <= i + 1 ? j0 + B : i + 1;
-        double mu = -INFINITY, dmu = 0.0;
+        double mu = -INFINITY;
         for (int j = j0; j < j1; ++j) {
-            x[j - j0] = dotd(qi, Kt + (long)j * d, d) * c1;
+            x[j - j0] = score_dot(p, qi, Kt + (long)j * d, d, h, tok0 + i, tok0 + j, 0) * c1;
             if (x[j - j0] > mu) mu = x[j - j0];
         }
-        if (track) {
-            for (int j = j0; j < j1; ++j) {
-                rt->delta[j - j0] = score_delta(p, qi, Kt + (long)j * d, d, c1, x[j - j0], m);
-                if (rt->delta[j - j0] > dmu) dmu = rt->delta[j - j0];
-            }
-            if (m != -INFINITY && fabs(mu - m - (double)p->tau) <= dmu + dm) loose = 1;
-            if (dmu > dmax) dmax = dmu;
-        }
+        /* replace the running maximum on the first tile, or when the tile's
+         * maximum exceeds it by more than tau */
         if (m == -INFINITY || mu - m > (double)p->tau) {
             double alpha = (m == -INFINITY) ? 0.0 : exp2(m - mu);
             l *= alpha;
             for (int k = 0; k < d; ++k) acc[k] *= alpha;
             m = mu;
-            if (track) {
-                for (int k = 0; k < d; ++k) rt->tacc[k] *= alpha;
-                tl *= alpha;
-                dm = dmu;
-            }
         }
         for (int j = j0; j < j1; ++j) {
             const int approx = p->fast_exp > 0 && quant != QUANT_NONE && key_pair_class(j) < p->fast_exp;
@@ -578,19 +535,6 @@ static void fwd_row(const orc_params *p, int i, const double *qi, const double *
                 code = orc_e4m3_encode(y);
                 w = orc_e4m3_value(code) / f;
                 l += (p->rowsum == 1) ? w / two_c : pj;
-                if (track) {
-                    /* the approximation's log2 slope is at most 1/ln 2, and the
-                     * kernel may land one 1/128 step away */
-                    double band = rt->delta[j - j0] + dm;
-                    if (approx) band = band / log(2.0) + log2(1.0 + 1.0 / 128.0);
-                    /* exact options: the fp32 argument also carries e_j - E */
-                    if (ev) band += 0x1p-20 * (double)(E - ev[j]);
-                    double sw = code_swing(y, band, loose) / f;
-                    if (sw > 0.0) {
-                        for (int k = 0; k < d; ++k) rt->tacc[k] += sw * fabs(vj[k]);
-                        if (p->rowsum == 1) tl += sw / two_c;
-                    }
-                }
             }
             for (int k = 0; k < d; ++k) acc[k] += w * vj[k];
         }
@@ -599,15 +543,6 @@ static void fwd_row(const orc_params *p, int i, const double *qi, const double *
         double den = (quant == QUANT_NONE) ? l : l * two_c;
         for (int k = 0; k < d; ++k) o_out[k] = acc[k] / den;
         *lse_out = m + log2(l);
-        if (track) {
-            /* codes that may move, plus the smooth movement of the row sum */
-            double band2 = dmax + dm;                 /* log2 band of one p */
-            if (p->fast_exp > 0) band2 = band2 / log(2.0) + log2(1.0 + 1.0 / 128.0);
-            double rel_l = log(2.0) * band2;
-            for (int k = 0; k < d; ++k)
-                rt->tol_o[k] = rt->tacc[k] / den + fabs(o_out[k]) * (tl / l + rel_l);
-            rt->tol_lse = band2 + log2(1.0 + tl / l) + 0x1p-20 * (1.0 + fabs(*lse_out));
-        }
     }
 }
 
@@ -633,12 +568,6 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
     float *lsef = 0;
     int64_t sat = 0, nds = 0, nds0 = 0;
     size_t Ld = (size_t)L * d;
-    /* tolerance bookkeeping (test infrastructure) */
-    const int track = p->score_rel_err > 0 && quant != QUANT_NONE &&
-                      (out->tol_o || out->tol_lse || out->tol_dv || out->tol_dq || out->tol_dk);
-    double *tacc = 0, *tdel = 0, *tolo = 0, *tlse = 0, *tdv = 0;
-    double *tOall = 0, *dSd = 0, *tdq = 0, *tdk = 0;
-    row_tol rt_store, *rt = 0;
 
     if (L == 0) return;
     Kt = malloc(sizeof(double) * Ld);
@@ -652,7 +581,7 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         eV = malloc(sizeof(int) * (size_t)L);
         eQ = malloc(sizeof(int) * (size_t)L);
         eO = malloc(sizeof(int) * (size_t)L);
-        erow = malloc(sizeof(int) * 32 * 3);
+        erow = malloc(sizeof(int) * 32);
         if (!eK || !eV || !eQ || !eO || !erow) { *err = ORC_ERR_NOMEM; goto done; }
     }
     Vt = malloc(sizeof(double) * Ld);
@@ -670,27 +599,8 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         dKa = calloc(Ld, sizeof(double));
         dVa = calloc(Ld, sizeof(double));
     }
-    if (track) {
-        tacc = malloc(sizeof(double) * d);
-        tdel = malloc(sizeof(double) * (p->key_tile > 32 ? p->key_tile : 32));
-        tolo = malloc(sizeof(double) * d);
-        tlse = malloc(sizeof(double) * L);
-        if (need_bwd) {
-            tdv = calloc(Ld, sizeof(double));
-            tOall = malloc(sizeof(double) * Ld);
-            dSd = malloc(sizeof(double) * 32 * (size_t)L);
-            tdq = malloc(sizeof(double) * Ld);
-            tdk = calloc(Ld, sizeof(double));
-        }
-        rt_store.tacc = tacc;
-        rt_store.delta = tdel;
-        rt_store.tol_o = tolo;
-        rt = &rt_store;
-    }
     if (!Kt || !Vt || !Qt || !O || !lse || !lsef || !acc || !xbuf ||
-        (need_bwd && (!dOt || !Dv || !dS || !dQa || !dKa || !dVa)) ||
-        (track && (!tacc || !tdel || !tolo || !tlse ||
-                   (need_bwd && (!tdv || !tOall || !dSd || !tdq || !tdk))))) {
+        (need_bwd && (!dOt || !Dv || !dS || !dQa || !dKa || !dVa))) {
         *err = ORC_ERR_NOMEM;
         goto done;
     }
@@ -715,15 +625,8 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         }
         /* ---- forward, row by row ---- */
         for (int i = 0; i < L; ++i) {
-            fwd_row(p, i, Qs + (long)i * d, Ks, Vt, eV, c1, acc, xbuf, O + (long)i * d, &lse[i], &sat, rt);
+            fwd_row(p, h, base, i, Qs + (long)i * d, Ks, Vt, eV, c1, acc, xbuf, O + (long)i * d, &lse[i], &sat);
             lsef[i] = (float)lse[i];
-            if (track) {
-                tlse[i] = rt->tol_lse;
-                if (out->tol_lse) out->tol_lse[(long)h * p->ttot + base + i] = rt->tol_lse;
-                if (out->tol_o)
-                    for (int c = 0; c < d; ++c) out->tol_o[((long)(base + i) * hq + h) * d + c] = tolo[c];
-                if (tOall) memcpy(tOall + (long)i * d, tolo, sizeof(double) * d);
-            }
             /* MX modes return a bf16 O and the backward reads it back
              * (Section 3.4: returned outputs are BF16); the unquantized mode
              * keeps binary64 throughout. */
@@ -748,7 +651,6 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
             if (out->dvec) out->dvec[(long)h * p->ttot + base + i] = Dv[i];
         }
         memset(dQa, 0, sizeof(double) * Ld);
-        if (tdq) memset(tdq, 0, sizeof(double) * Ld);
         for (int i0 = 0; i0 < L; i0 += 32) {
             int i1 = i0 + 32 < L ? i0 + 32 : L;
             /* exact options: the dV product applies one factor 2^Eo per
@@ -766,9 +668,9 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                 double *row = dS + (size_t)(i - i0) * L;
                 for (int j = 0; j < L; ++j) row[j] = 0.0;
                 for (int j = 0; j <= i; ++j) {
-                    double xij = dotd(qi, Ks + (long)j * d, d) * c1;
+                    double xij = score_dot(p, qi, Ks + (long)j * d, d, h, base + i, base + j, 0) * c1;
                     double P = exp2(xij - li), wb;
-                    double dP = dotd(doi, Vt + (long)j * d, d);
+                    double dP = score_dot(p, doi, Vt + (long)j * d, d, h, base + i, base + j, 1);
                     if (quant == QUANT_NONE) {
                         wb = P;
                     } else {
@@ -777,30 +679,16 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                          * relative to the block's Eo: E4M3(2^8 P 2^(e_i - Eo)). */
                         const double fo = exact ? ldexp(1.0, eO[i] - Eo) : 1.0;
                         wb = ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(P, 8) * fo)), -8) / fo;
-                        if (track && tdv) {   /* tolerance bookkeeping */
-                            double r = score_delta(p, qi, Ks + (long)j * d, d, c1, xij, li) + tlse[i];
-                            double sw = ldexp(code_swing(ldexp(P, 8) * fo, r, 0), -8) / fo;
-                            if (sw > 0.0)
-                                for (int c = 0; c < d; ++c) tdv[(long)j * d + c] += sw * fabs(doi[c]);
-                        }
                     }
                     for (int c = 0; c < d; ++c) dVa[(long)j * d + c] += wb * doi[c];
                     row[j] = P * (dP - Dv[i]);
-                    if (dSd) {   /* tolerance bookkeeping: error band of dS */
-                        double dx = score_delta(p, qi, Ks + (long)j * d, d, c1, xij, li) + tlse[i];
-                        double ddp = score_delta(p, doi, Vt + (long)j * d, d, 1.0, dP, 0.0);
-                        double dD = 0x1p-20 * fabs(Dv[i]);
-                        for (int c = 0; c < d; ++c) dD += fabs(doi[c]) * tOall[(long)i * d + c];
-                        dSd[(size_t)(i - i0) * L + j] =
-                            fabs(row[j]) * (exp2(dx) - 1.0) + P * (ddp + dD);
-                    }
                 }
             }
             /* dS~: one exponent per 32x32 document-local block (Section 3.3),
              * then dQ += dS~ K~ and dK += dS~^T Q~. */
             for (int j0 = 0; j0 <= i1 - 1; j0 += 32) {
                 int j1 = j0 + 32 < L ? j0 + 32 : L;
-                int e = 0, elo = 0, ehi = 0;
+                int e = 0;
                 if (exact) {
                     /* Exact options (Appendix A.3): the two gradient products
                      * contract over different tokens, so dS~ differs between
@@ -812,48 +700,28 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                      * products apply 2^(block or row exponent) and the folded
                      * exponent returns with the other operand's codes. */
                     const int rule = quant == QUANT_FLOOR ? 1 : 0;
-                    int *ez = erow, *ezlo = erow + 32, *ezhi = erow + 64;
-                    double ay = 0.0, aylo = 0.0, ayhi = 0.0;
+                    int *ez = erow;
+                    double ay = 0.0;
                     for (int i = i0; i < i1; ++i) {
-                        double az = 0.0, azlo = 0.0, azhi = 0.0;
+                        double az = 0.0;
                         for (int j = j0; j < j1 && j <= i; ++j) {
                             double a = fabs(dS[(size_t)(i - i0) * L + j]);
-                            double b = dSd ? dSd[(size_t)(i - i0) * L + j] : 0.0;
-                            double yk = ldexp(a, eQ[i]), yb = ldexp(b, eQ[i]);
-                            double zq = ldexp(a, eK[j]), zb = ldexp(b, eK[j]);
+                            double yk = ldexp(a, eQ[i]), zq = ldexp(a, eK[j]);
                             if (yk > ay) ay = yk;
-                            if (yk - yb > aylo) aylo = yk - yb;
-                            if (yk + yb > ayhi) ayhi = yk + yb;
                             if (zq > az) az = zq;
-                            if (zq - zb > azlo) azlo = zq - zb;
-                            if (zq + zb > azhi) azhi = zq + zb;
                         }
                         ez[i - i0] = orc_scale_exp(az, rule);
-                        ezlo[i - i0] = dSd ? orc_scale_exp(azlo, rule) : ez[i - i0];
-                        ezhi[i - i0] = dSd ? orc_scale_exp(azhi, rule) : ez[i - i0];
                     }
                     e = orc_scale_exp(ay, rule);
-                    elo = dSd ? orc_scale_exp(aylo, rule) : e;
-                    ehi = dSd ? orc_scale_exp(ayhi, rule) : e;
                     for (int i = i0; i < i1; ++i)
                         for (int j = j0; j < j1 && j <= i; ++j) {
                             double ds = dS[(size_t)(i - i0) * L + j];
                             double yk = ldexp(ds, eQ[i]), zq = ldexp(ds, eK[j]);
-                            double dkv = ldexp(deq_at(yk, e), -eQ[i]);
-                            double dqv = ldexp(deq_at(zq, ez[i - i0]), -eK[j]);
+                            double dkv = ldexp(ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(yk, -e))), e), -eQ[i]);
+                            double dqv = ldexp(ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(zq, -ez[i - i0]))),
+                                                     ez[i - i0]), -eK[j]);
                             nds++;
                             if (ds != 0.0 && dqv == 0.0) nds0++;
-                            if (dSd) {   /* tolerance bookkeeping: how far each dS~ can move */
-                                double band = dSd[(size_t)(i - i0) * L + j];
-                                const int esk[3] = {elo, e, ehi};
-                                const int esq[3] = {ezlo[i - i0], ez[i - i0], ezhi[i - i0]};
-                                double swk = ldexp(deq_swing(yk, ldexp(band, eQ[i]), esk, ldexp(dkv, eQ[i])), -eQ[i]);
-                                double swq = ldexp(deq_swing(zq, ldexp(band, eK[j]), esq, ldexp(dqv, eK[j])), -eK[j]);
-                                for (int c = 0; c < d; ++c) {
-                                    tdq[(long)i * d + c] += swq * fabs(Kt[(long)j * d + c]);
-                                    tdk[(long)j * d + c] += swk * fabs(Qt[(long)i * d + c]);
-                                }
-                            }
                             for (int c = 0; c < d; ++c) {
                                 dQa[(long)i * d + c] += dqv * Kt[(long)j * d + c];
                                 dKa[(long)j * d + c] += dkv * Qt[(long)i * d + c];
@@ -862,20 +730,13 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                     continue;
                 }
                 if (quant != QUANT_NONE) {
-                    double amax = 0.0, alo = 0.0, ahi = 0.0;
+                    double amax = 0.0;
                     for (int i = i0; i < i1; ++i)
                         for (int j = j0; j < j1 && j <= i; ++j) {
                             double a = fabs(dS[(size_t)(i - i0) * L + j]);
                             if (a > amax) amax = a;
-                            if (dSd) {   /* tolerance bookkeeping: exponent band */
-                                double b = dSd[(size_t)(i - i0) * L + j];
-                                if (a - b > alo) alo = a - b;
-                                if (a + b > ahi) ahi = a + b;
-                            }
                         }
                     e = orc_scale_exp(amax, quant == QUANT_FLOOR ? 1 : 0);
-                    elo = dSd ? orc_scale_exp(alo, quant == QUANT_FLOOR ? 1 : 0) : e;
-                    ehi = dSd ? orc_scale_exp(ahi, quant == QUANT_FLOOR ? 1 : 0) : e;
                 }
                 for (int i = i0; i < i1; ++i)
                     for (int j = j0; j < j1 && j <= i; ++j) {
@@ -886,15 +747,6 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                             dq = ldexp(orc_e4m3_value(orc_e4m3_encode(ldexp(ds, -e))), e);
                             nds++;
                             if (ds != 0.0 && dq == 0.0) nds0++;
-                            if (dSd) {   /* tolerance bookkeeping: how far dS~ can move */
-                                const int es[3] = {elo, e, ehi};
-                                double sw = deq_swing(ds, dSd[(size_t)(i - i0) * L + j], es, dq);
-                                if (sw > 0.0)
-                                    for (int c = 0; c < d; ++c) {
-                                        tdq[(long)i * d + c] += sw * fabs(Kt[(long)j * d + c]);
-                                        tdk[(long)j * d + c] += sw * fabs(Qt[(long)i * d + c]);
-                                    }
-                            }
                         }
                         if (dq == 0.0) continue;
                         for (int c = 0; c < d; ++c) {
@@ -906,37 +758,20 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
         }
         if (p->hadamard) {
             /* dQ' is the gradient for the rotated Q' = Q H / sqrt(d): dQ = dQ' H / sqrt(d)
-             * (H / sqrt(d) is symmetric and its own inverse).  An output element
-             * is a +-1/sqrt(d) combination of the row, so the bound of each
-             * element is the row's bounds summed, over sqrt(d). */
-            for (int i = 0; i < L; ++i) {
-                hadamard_f64(dQa + (long)i * d, d);
-                if (tdq) {
-                    double t = 0.0;
-                    for (int c = 0; c < d; ++c) t += tdq[(long)i * d + c];
-                    for (int c = 0; c < d; ++c) tdq[(long)i * d + c] = t / sqrt((double)d);
-                }
-            }
+             * (H / sqrt(d) is symmetric and its own inverse). */
+            for (int i = 0; i < L; ++i) hadamard_f64(dQa + (long)i * d, d);
         }
         for (int i = 0; i < L; ++i)
             for (int c = 0; c < d; ++c) {
                 long gi = ((long)(base + i) * hq + h) * d + c;
                 double val = s * dQa[(long)i * d + c];
                 if (out->dq64) out->dq64[gi] = val;
-                if (tdq && out->tol_dq) out->tol_dq[gi] = s * tdq[(long)i * d + c];
                 if (out->dq16) out->dq16[gi] = orc_double_to_bf16(val);
             }
     }
     if (need_bwd) {
         if (p->hadamard)   /* dK = dK' H / sqrt(d), as for dQ */
-            for (int j = 0; j < L; ++j) {
-                hadamard_f64(dKa + (long)j * d, d);
-                if (tdk) {
-                    double t = 0.0;
-                    for (int c = 0; c < d; ++c) t += tdk[(long)j * d + c];
-                    for (int c = 0; c < d; ++c) tdk[(long)j * d + c] = t / sqrt((double)d);
-                }
-            }
+            for (int j = 0; j < L; ++j) hadamard_f64(dKa + (long)j * d, d);
         for (int j = 0; j < L; ++j)
             for (int c = 0; c < d; ++c) {
                 long gj = ((long)(base + j) * hkv + g) * d + c;
@@ -945,8 +780,6 @@ static void unit_run(const orc_params *p, int doc, int g, const int32_t *cu,
                 if (out->dv64) out->dv64[gj] = vv;
                 if (out->dk16) out->dk16[gj] = orc_double_to_bf16(kv);
                 if (out->dv16) out->dv16[gj] = orc_double_to_bf16(vv);
-                if (tdv && out->tol_dv) out->tol_dv[gj] = tdv[(long)j * d + c];
-                if (tdk && out->tol_dk) out->tol_dk[gj] = s * tdk[(long)j * d + c];
             }
     }
     if (out->stats) {
@@ -961,9 +794,8 @@ done:
     free(Kt); free(Vt); free(Qt); free(O); free(lse); free(lsef); free(acc); free(xbuf);
     free(Kn); free(Qn); free(eK); free(eV); free(eQ); free(eO); free(erow);
     free(dOt); free(Dv); free(dS); free(dQa); free(dKa); free(dVa);
-    free(tacc); free(tdel); free(tolo); free(tlse); free(tdv);
-    free(tOall); free(dSd); free(tdq); free(tdk);
 }
+
 
 typedef struct { long len; int doc, g; } unit_t;
 
@@ -987,11 +819,9 @@ int orc_attention(const orc_params *p, const uint16_t *q, const uint16_t *k, con
                   const uint8_t *doc_mask,
                   double *o64, uint16_t *o16, float *lse2, double *dvec,
                   double *dq64, double *dk64, double *dv64,
-                  uint16_t *dq16, uint16_t *dk16, uint16_t *dv16, int64_t *stats,
-                  double *tol_o, double *tol_lse, double *tol_dv, double *tol_dq, double *tol_dk)
+                  uint16_t *dq16, uint16_t *dk16, uint16_t *dv16, int64_t *stats)
 {
-    orc_out out = {o64, o16, lse2, dvec, dq64, dk64, dv64, dq16, dk16, dv16, stats,
-                   tol_o, tol_lse, tol_dv, tol_dq, tol_dk};
+    orc_out out = {o64, o16, lse2, dvec, dq64, dk64, dv64, dq16, dk16, dv16, stats};
     unit_t *units;
     long nu = 0;
     int err = ORC_OK;

@@ -228,3 +228,26 @@ def flop_count(hq: int, d: int, sum_L2: int) -> float:
     backward 2.5x the forward (FlashAttention convention with the causal
     discount of the paper's Appendix E)."""
     return 7.0 * hq * d * float(sum_L2)
+
+
+def generate_integer(lens, hq: int, hkv: int, d: int, qk_max: int, vo_max: int, seed: int) -> dict:
+    """Integer-valued inputs: Q and K uniform on {-qk_max, ..., qk_max}, V and
+    dO on {-vo_max, ..., vo_max} (at most 15, so every value has at most four
+    significant bits).  Such values survive the E4M3 token-block quantization
+    unchanged, and their dot products are integers small enough that a matrix
+    core computes them exactly, so a kernel and a reference take the same
+    rounding decisions downstream of the scores.  Same dict as generate()."""
+    if not (0 < qk_max <= 15 and 0 < vo_max <= 15):
+        raise ValueError("integer ranges must lie in 1..15")
+    lens = [int(L) for L in lens]
+    T = int(sum(lens))
+    rng = np.random.default_rng([seed, 0x1D7E])
+
+    def draw(H, a):
+        return bf16_bits(rng.integers(-a, a + 1, size=(T, H, d)).astype(np.float32))
+
+    q, k = draw(hq, qk_max), draw(hkv, qk_max)
+    v, do = draw(hkv, vo_max), draw(hq, vo_max)
+    return {"workload": custom(f"int-{T}", lens, hq, hkv, d), "q": q, "k": k, "v": v, "do": do,
+            "cu_seqlens": cu_from_lengths(lens), "lengths": lens,
+            "sum_L2": int(sum(L * L for L in lens))}

@@ -8,7 +8,7 @@ import pytest
 
 from precision_causal_attention_amd import workloads as W
 
-from gpu_util import SCORE_REL_ERR, assert_close, run_hip, say
+from gpu_util import check_outputs, run_hip, say
 
 pytestmark = pytest.mark.gpu
 
@@ -42,15 +42,6 @@ def test_paper_workload(orc, name):
     km[0] = 1
     dm = np.zeros(len(lens), np.uint8)
     dm[pick] = 1
-    opts = orc.Opts()
-    opts.score_rel_err = SCORE_REL_ERR
-    r = orc.attention(inst["q"], inst["k"], inst["v"], inst["do"], cu, opts, want_tol=True,
-                      kv_mask=km, doc_mask=dm)
+    r = orc.attention(inst["q"], inst["k"], inst["v"], inst["do"], cu, orc.Opts(), kv_mask=km, doc_mask=dm)
     rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in pick])
-    hs, ks = slice(0, G), slice(0, 1)
-    assert_close("O", g["o"][rows][:, hs], r["o64"][rows][:, hs], r["tol_o"][rows][:, hs])
-    lse_err = np.abs(g["lse2"][hs][:, rows] - r["lse2"][hs][:, rows])
-    assert (lse_err <= r["tol_lse"][hs][:, rows] + 1e-5).all()
-    assert_close("dQ", g["dq"][rows][:, hs], r["dq64"][rows][:, hs], r["tol_dq"][rows][:, hs])
-    assert_close("dK", g["dk"][rows][:, ks], r["dk64"][rows][:, ks], r["tol_dk"][rows][:, ks])
-    assert_close("dV", g["dv"][rows][:, ks], r["dv64"][rows][:, ks], r["tol_dv"][rows][:, ks])
+    check_outputs(g, r, rows=rows, heads=slice(0, G), kvheads=slice(0, 1))
