@@ -204,6 +204,28 @@ flamia_status_t flamia_fwd(const flamia_dims_t *dims, const flamia_opts_t *opts,
                            uint16_t *o, float *lse2, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * flamia_fwd_noalloc -- flamia_fwd without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments (minus
+ * ws / ws_bytes), kernels and results as flamia_fwd, bit for bit.  The
+ * forward's control block, tile prefix and work list live in a static device
+ * array of 4 MiB instead, one per GPU the library runs on, held until the
+ * process ends.  Capacities whose work list does not fit it (ndocs_cap + 1
+ * prefix entries of 4 bytes and ttot_cap / 128 + ndocs_cap + 1 tiles of 16
+ * bytes, 256-byte aligned: about 200,000 documents at the largest ttot_cap)
+ * return FLAMIA_ERR_WORKSPACE, with the sizes in flamia_last_error().
+ * Nothing is allocated and nothing synchronizes with the host.  Every call on
+ * a GPU uses that GPU's one array, which keeps the last call's contents
+ * (nothing in it needs to start at zero): calls that overlap on one GPU (on
+ * different streams or host threads) race, so order them on one stream.
+ */
+flamia_status_t flamia_fwd_noalloc(const flamia_dims_t *dims, const flamia_opts_t *opts,
+                                   const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                   const int32_t *cu_seqlens,
+                                   flamia_mx_t q_mx, flamia_mx_t k_mx, flamia_mx_t v_mx,
+                                   uint16_t *o, float *lse2, void *stream);
+
+/*
  * flamia_bwd -- backward of the training call (Section 2 equations for dV,
  * dP, dS, dQ, dK; Section 3.3: scores rebuilt from the forward's quantized
  * Q/K, the same tiling, diagonal handling, exponential and saved row

@@ -2,12 +2,22 @@
 // sequence of the training call.  Nothing here synchronizes with the device
 // or allocates memory; every launch goes to the caller's stream.
 #include <math.h>
+#include <stdio.h>
 #include <string.h>
+
+#include <atomic>
 
 #include "flamia.h"
 #include "kernels.h"
 
 using namespace flamia;
+
+// Static scratch of flamia_fwd_noalloc: the forward's control block, tile
+// prefix and work list, one copy per device (each device's copy lives at its
+// own address, found with hipGetSymbolAddress).  Host code never passes the
+// array's name to a kernel or a copy, only the per-device addresses.
+constexpr size_t kNoallocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -128,6 +138,91 @@ flamia_status_t check_nv(const flamia_opts_t& o, flamia_mx_t q, flamia_mx_t k) {
     return FLAMIA_OK;
 }
 
+// Validation shared by flamia_fwd and flamia_fwd_noalloc (everything but
+// the workspace).
+flamia_status_t check_fwd(const flamia_dims_t* dims, const flamia_opts_t& opts,
+                          const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const int32_t* cu_seqlens, flamia_mx_t q_mx, flamia_mx_t k_mx, flamia_mx_t v_mx,
+                          const uint16_t* o, const float* lse2) {
+    flamia_status_t s;
+    if ((s = check_opts(&opts)) != FLAMIA_OK) return s;
+    if (!q || !k || !v || !cu_seqlens || !o || !lse2 || !q_mx.codes || !q_mx.scales ||
+        !k_mx.codes || !k_mx.scales || !v_mx.codes || !v_mx.scales)
+        return FLAMIA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !mx_ok(q_mx) ||
+        !mx_ok(k_mx) || !mx_ok(v_mx))
+        return FLAMIA_ERR_ALIGN;
+    return check_nv(opts, q_mx, k_mx);
+}
+
+// The forward's launches; `base` holds the forward's part of the layout `w`
+// (control block, tile prefix, query-major work list).
+flamia_status_t fwd_enqueue(const flamia_dims_t* dims, const flamia_opts_t& opts,
+                            const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const int32_t* cu_seqlens, flamia_mx_t q_mx, flamia_mx_t k_mx, flamia_mx_t v_mx,
+                            uint16_t* o, float* lse2, uint8_t* base, const Layout& w, hipStream_t st) {
+    const int d = dims->d;
+    // quantization of the three operands in one launch (Section 3.5.1)
+    QuantArgs qa{};
+    qa.cu = cu_seqlens; qa.ndocs = dims->ndocs; qa.ttot = dims->ttot; qa.d = d;
+    // with the Hadamard option Q and K are quantized from their rotated rows
+    // (Section 3.4: the rotation is fused into the quantizer), V never is;
+    // on the mixed path Q and K also get their NVFP4 values
+    uint16_t* qn = opts.mixed ? q_mx.nv : nullptr;
+    uint16_t* kn = opts.mixed ? k_mx.nv : nullptr;
+    qa.t[0] = QuantTensor{q, q_mx.codes, q_mx.scales, dims->hq, opts.hadamard, qn};
+    qa.t[1] = QuantTensor{k, k_mx.codes, k_mx.scales, dims->hkv, opts.hadamard, kn};
+    qa.t[2] = QuantTensor{v, v_mx.codes, v_mx.scales, dims->hkv, 0, nullptr};
+    qa.ntensors = 3;
+    qa.per_token = opts.exact;
+    PhaseMarks pm{opts, st};
+    hipError_t e;
+    if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(qa, st)) != hipSuccess) return hip_fail(e);
+    int32_t* ctrl = (int32_t*)(base + w.ctrl);
+    int4* tiles = (int4*)(base + w.tiles_q);
+    PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
+                tiles, nullptr, nullptr, 0};
+    if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
+    FwdArgs fa;
+    fa.qc = q_mx.codes; fa.qs = q_mx.scales;
+    fa.kc = k_mx.codes; fa.ks = k_mx.scales;
+    fa.vc = v_mx.codes; fa.vs = v_mx.scales;
+    fa.o = o; fa.lse2 = lse2;
+    fa.tiles = tiles; fa.ntiles = ctrl;
+    fa.ttot = dims->ttot; fa.hq = dims->hq; fa.hkv = dims->hkv;
+    fa.c1 = scale_of(opts, d) * 1.4426950408889634f;
+    fa.c_log2 = (float)opts.c_log2;
+    fa.tau = (float)opts.tau;
+    fa.rowsum = opts.rowsum;
+    fa.fast_exp = opts.fast_exp;
+    fa.qn = qn; fa.kn = kn;
+    fa.exact = opts.exact;
+    if ((e = pm.mark()) != hipSuccess || (e = launch_fwd(fa, d, w.max_tiles * dims->hq, st)) != hipSuccess)
+        return hip_fail(e);
+    e = pm.mark();
+    return e == hipSuccess ? FLAMIA_OK : hip_fail(e);
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of the scratch array (looked up once per device).
+hipError_t scratch_of_current_device(uint8_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    uint8_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* a = nullptr;
+        if ((e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        p = (uint8_t*)a;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -194,61 +289,40 @@ flamia_status_t flamia_fwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     flamia_status_t s = check_dims(dims);
     if (s != FLAMIA_OK) return s;
     const flamia_opts_t opts = resolve(opts_in);
-    if ((s = check_opts(&opts)) != FLAMIA_OK) return s;
-    if (!q || !k || !v || !cu_seqlens || !o || !lse2 || !q_mx.codes || !q_mx.scales ||
-        !k_mx.codes || !k_mx.scales || !v_mx.codes || !v_mx.scales)
-        return FLAMIA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !mx_ok(q_mx) ||
-        !mx_ok(k_mx) || !mx_ok(v_mx))
-        return FLAMIA_ERR_ALIGN;
-    if ((s = check_nv(opts, q_mx, k_mx)) != FLAMIA_OK) return s;
+    if ((s = check_fwd(dims, opts, q, k, v, cu_seqlens, q_mx, k_mx, v_mx, o, lse2)) != FLAMIA_OK) return s;
     const Layout w = layout(dims);
     if (!ws || ws_bytes < w.total) return FLAMIA_ERR_WORKSPACE;
     if (!aligned16(ws)) return FLAMIA_ERR_ALIGN;
     if (dims->ttot == 0) return FLAMIA_OK;
-    hipStream_t st = (hipStream_t)stream;
-    uint8_t* base = (uint8_t*)ws;
-    const int d = dims->d;
+    return fwd_enqueue(dims, opts, q, k, v, cu_seqlens, q_mx, k_mx, v_mx, o, lse2, (uint8_t*)ws, w,
+                       (hipStream_t)stream);
+}
 
-    // quantization of the three operands in one launch (Section 3.5.1)
-    QuantArgs qa{};
-    qa.cu = cu_seqlens; qa.ndocs = dims->ndocs; qa.ttot = dims->ttot; qa.d = d;
-    // with the Hadamard option Q and K are quantized from their rotated rows
-    // (Section 3.4: the rotation is fused into the quantizer), V never is;
-    // on the mixed path Q and K also get their NVFP4 values
-    uint16_t* qn = opts.mixed ? q_mx.nv : nullptr;
-    uint16_t* kn = opts.mixed ? k_mx.nv : nullptr;
-    qa.t[0] = QuantTensor{q, q_mx.codes, q_mx.scales, dims->hq, opts.hadamard, qn};
-    qa.t[1] = QuantTensor{k, k_mx.codes, k_mx.scales, dims->hkv, opts.hadamard, kn};
-    qa.t[2] = QuantTensor{v, v_mx.codes, v_mx.scales, dims->hkv, 0, nullptr};
-    qa.ntensors = 3;
-    qa.per_token = opts.exact;
-    PhaseMarks pm{opts, st};
-    hipError_t e;
-    if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(qa, st)) != hipSuccess) return hip_fail(e);
-    int32_t* ctrl = (int32_t*)(base + w.ctrl);
-    int4* tiles = (int4*)(base + w.tiles_q);
-    PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
-                tiles, nullptr, nullptr, 0};
-    if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
-    FwdArgs fa;
-    fa.qc = q_mx.codes; fa.qs = q_mx.scales;
-    fa.kc = k_mx.codes; fa.ks = k_mx.scales;
-    fa.vc = v_mx.codes; fa.vs = v_mx.scales;
-    fa.o = o; fa.lse2 = lse2;
-    fa.tiles = tiles; fa.ntiles = ctrl;
-    fa.ttot = dims->ttot; fa.hq = dims->hq; fa.hkv = dims->hkv;
-    fa.c1 = scale_of(opts, d) * 1.4426950408889634f;
-    fa.c_log2 = (float)opts.c_log2;
-    fa.tau = (float)opts.tau;
-    fa.rowsum = opts.rowsum;
-    fa.fast_exp = opts.fast_exp;
-    fa.qn = qn; fa.kn = kn;
-    fa.exact = opts.exact;
-    if ((e = pm.mark()) != hipSuccess || (e = launch_fwd(fa, d, w.max_tiles * dims->hq, st)) != hipSuccess)
-        return hip_fail(e);
-    e = pm.mark();
-    return e == hipSuccess ? FLAMIA_OK : hip_fail(e);
+flamia_status_t flamia_fwd_noalloc(const flamia_dims_t* dims, const flamia_opts_t* opts_in,
+                                   const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int32_t* cu_seqlens,
+                                   flamia_mx_t q_mx, flamia_mx_t k_mx, flamia_mx_t v_mx,
+                                   uint16_t* o, float* lse2, void* stream) {
+    flamia_status_t s = check_dims(dims);
+    if (s != FLAMIA_OK) return s;
+    const flamia_opts_t opts = resolve(opts_in);
+    if ((s = check_fwd(dims, opts, q, k, v, cu_seqlens, q_mx, k_mx, v_mx, o, lse2)) != FLAMIA_OK) return s;
+    const Layout w = layout(dims);
+    // the forward uses the layout's leading part only: control block, tile
+    // prefix and the query-major work list
+    const size_t need = w.tiles_q + up256(sizeof(int4) * (size_t)w.max_tiles);
+    if (need > kNoallocScratchBytes) {
+        snprintf(g_last_error, sizeof g_last_error,
+                 "flamia_fwd_noalloc: capacities need %zu bytes of scratch, the static array holds %zu",
+                 need, kNoallocScratchBytes);
+        return FLAMIA_ERR_WORKSPACE;
+    }
+    if (dims->ttot == 0) return FLAMIA_OK;
+    uint8_t* base = nullptr;
+    hipError_t e = scratch_of_current_device(&base);
+    if (e != hipSuccess) return hip_fail(e);
+    return fwd_enqueue(dims, opts, q, k, v, cu_seqlens, q_mx, k_mx, v_mx, o, lse2, base, w,
+                       (hipStream_t)stream);
 }
 
 flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_in,

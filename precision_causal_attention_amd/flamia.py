@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.flamia_bwd.restype = ctypes.c_int
         L.flamia_bwd.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts), P, P, P, P, Mx, Mx, Mx,
                                  P, P, P, P, S, P]
+        L.flamia_fwd_noalloc.restype = ctypes.c_int
+        L.flamia_fwd_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Opts), P, P, P, P, Mx, Mx, Mx,
+                                         P, P, P]
         _lib = L
     return _lib
 
@@ -142,6 +145,16 @@ def flamia_fwd(dims: Dims, opts: Opts | None, q, k, v, cu_seqlens, q_mx, k_mx, v
                           _ptr(o), _ptr(lse2), _ptr(ws), ws_bytes, _stream(stream))
     if check:
         _check("flamia_fwd", rc)
+    return rc
+
+
+def flamia_fwd_noalloc(dims: Dims, opts: Opts | None, q, k, v, cu_seqlens, q_mx, k_mx, v_mx, o, lse2,
+                       stream=None, check=True) -> int:
+    rc = lib().flamia_fwd_noalloc(ctypes.byref(dims), ctypes.byref(opts) if opts else None,
+                                  _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _mx(q_mx), _mx(k_mx),
+                                  _mx(v_mx), _ptr(o), _ptr(lse2), _stream(stream))
+    if check:
+        _check("flamia_fwd_noalloc", rc)
     return rc
 
 

@@ -160,3 +160,21 @@ def test_quantize_validation():
     assert F.flamia_quantize(dm, 2, FAKE + 2, FAKE, mx, stream=0, check=False) == 3
     assert F.flamia_quantize(dims(d=32), 2, FAKE, FAKE, mx, stream=0, check=False) == 2
     assert F.flamia_quantize(dm, 2, FAKE, FAKE, (FAKE, FAKE, FAKE + 2), stream=0, check=False) == 3
+
+
+def test_noalloc_forward_refuses_capacities_beyond_its_scratch():
+    """flamia_fwd_noalloc keeps the forward's work list in a static 4 MiB
+    device array; capacities that need more are refused on the host, before
+    the array's address is looked up or anything is launched."""
+    L = F.lib()
+    P = ctypes.c_void_p
+    mx = F.Mx(FAKE, FAKE, None)
+    big = dims(ttot_cap=1 << 20, ndocs_cap=300000)       # ~6.2 MB of prefix and work list
+    rc = L.flamia_fwd_noalloc(ctypes.byref(big), None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), mx, mx, mx,
+                              P(FAKE), P(FAKE), None)
+    assert rc == 5                                           # FLAMIA_ERR_WORKSPACE
+    assert "static array" in F.flamia_last_error()
+    # the usual argument checks come first
+    rc = L.flamia_fwd_noalloc(ctypes.byref(big), None, None, P(FAKE), P(FAKE), P(FAKE), mx, mx, mx,
+                              P(FAKE), P(FAKE), None)
+    assert rc == 1                                           # FLAMIA_ERR_NULL
