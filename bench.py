@@ -14,11 +14,15 @@ dispatch gap, so the measurement runs in passes:
   2. timed pass: K eager steps with two events per step, around the dominant
      kernel -> value / ms_per_step (bracketed by device synchronizations)
      and the roofline's average kernel duration;
-  3. graph pass: one whole call captured as a HIP graph and replayed K times,
-     bracketed by device synchronizations -> graph_ms_per_step (the pages
-     time a replayed graph; on MI355X with ROCm 7 the replay adds about
-     10-15 us per kernel node over stream launches, so the eager time is the
-     one reported as value).
+  3. step pass: K eager steps with one event at each step boundary ->
+     eager_median_ms (the median step);
+  4. graph pass: one whole call captured as a HIP graph and replayed K times
+     with one event at each replay boundary -> graph_median_ms (the pages
+     time replayed graphs and take medians) and graph_ms_per_step (the
+     mean, bracketed by device synchronizations);
+  5. matrix-core probe: the block-scaled FP8 instruction issued back to back
+     from registers on every SIMD (libflamia_probe.so) -> the achievable
+     peak, reported beside the specification's 5.0 PFLOP/s.
 
 Prints ONE JSON line:
   value     whole-call throughput, FLOP = 7 * Hq * d * sum(L^2) (forward 2
@@ -90,6 +94,12 @@ class Hip:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, e, stream):
+        rc = self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
 
     def events(self, n):
         out = []
@@ -137,6 +147,47 @@ def recorded_traffic(workload, kernel, doclen_cap):
     return None
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def mfma_probe(hip, stream):
+    """Achievable FP8 matrix-core rate: the best of a few launch shapes of the
+    probe kernel (4 waves per workgroup, each issuing 4 x iters products of
+    2 * 32 * 32 * 64 FLOP), timed with HIP events on `stream`.  TFLOP/s."""
+    import torch
+    path = os.path.join(ROOT, "precision_causal_attention_amd", "libflamia_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.flamia_probe_mfma_peak.restype = ctypes.c_int
+    lib.flamia_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 4096
+    best = 0.0
+    for per_cu in (2, 4, 8):
+        wg = cus * per_cu
+        sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+        ev = hip.events(2)
+        for rep in range(3):
+            hip.record(ev[0], stream)
+            rc = lib.flamia_probe_mfma_peak(wg, iters, ctypes.c_void_p(sink.data_ptr()),
+                                            ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"flamia_probe_mfma_peak failed: {rc}")
+            hip.record(ev[1], stream)
+            ms = hip.elapsed_ms(ev[0], ev[1])
+            if rep > 0:    # the first launch warms up
+                best = max(best, wg * 4 * 4 * iters * 131072.0 / (ms * 1e-3) / 1e12)
+    return best
+
+
 def cpu_baseline(inst, hkv, hadamard=0, mixed=0, exact=0, target_s=10.0):
     """The oracle as it stands on a sample of the workload: key/value head 0
     and its query heads (all documents) is timed first; while a call takes
@@ -163,7 +214,8 @@ def cpu_baseline(inst, hkv, hadamard=0, mixed=0, exact=0, target_s=10.0):
     hq, d = inst["q"].shape[1], inst["q"].shape[2]
     G = hq // hkv
     flop = 7.0 * n * G * d * inst["sum_L2"]
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"key/value head{'s 0-' + str(n - 1) if n > 1 else ' 0'} of {hkv} ({n * G} of {hq} query heads), all "
                       f"{len(inst['lengths'])} documents, forward + backward incl. quantization"
                       f"{' (mixed NVFP4/FP8 path)' if mixed else ''}{' (exact options)' if exact else ''}; "
@@ -374,6 +426,20 @@ def main():
         torch.cuda.synchronize()
         return g
 
+    # ---- pass 3: eager steps with one event per step boundary (median step)
+    log(f"[bench] step pass, {args.steps} steps")
+    sev = hip.events(args.steps + 1)
+    torch.cuda.synchronize()
+    hip.record(sev[0], stream)
+    for i in range(args.steps):
+        run_step()
+        hip.record(sev[i + 1], stream)
+    torch.cuda.synchronize()
+    eager_steps = sorted(hip.elapsed_ms(sev[i], sev[i + 1]) for i in range(args.steps))
+    eager_median = eager_steps[args.steps // 2] if args.steps % 2 else \
+        0.5 * (eager_steps[args.steps // 2 - 1] + eager_steps[args.steps // 2])
+
+    # ---- pass 4: the call as a HIP graph, replayed K times
     log(f"[bench] graph pass, {args.steps} replays")
     graph = capture()
     for _ in range(3):
@@ -385,6 +451,19 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     graph_ms_step = t0.elapsed_time(t1) / args.steps
+    gev = hip.events(args.steps + 1)
+    hip.record(gev[0], stream)
+    for i in range(args.steps):
+        graph.replay()
+        hip.record(gev[i + 1], stream)
+    torch.cuda.synchronize()
+    graph_steps = sorted(hip.elapsed_ms(gev[i], gev[i + 1]) for i in range(args.steps))
+    graph_median = graph_steps[args.steps // 2] if args.steps % 2 else \
+        0.5 * (graph_steps[args.steps // 2 - 1] + graph_steps[args.steps // 2])
+
+    # ---- pass 5: achievable matrix-core rate
+    log("[bench] matrix-core probe")
+    probe_tflops = mfma_probe(hip, stream)
 
     tflops = flop / (ms_step * 1e-3) / 1e12
     achieved = kflop[dom] / (dom_ms * 1e-3) / 1e12
@@ -408,7 +487,12 @@ def main():
                    "hkv": hkv, "d": d, "docs": ndocs, "sum_L2": sum_l2, "seed": args.seed,
                    "doc_law": wl.docs, "doclen_cap": doclen_cap, "hadamard": args.hadamard,
                    "mixed": args.mixed, "exact": args.exact, "parallelism": "single-gpu"},
+        "eager_median_ms": round(eager_median, 4),
+        "graph_median_ms": round(graph_median, 4),
         "graph_ms_per_step": round(graph_ms_step, 4),
+        "graph_median_tflops": round(flop / (graph_median * 1e-3) / 1e12, 2),
+        "measured_mfma_peak_tflops": round(probe_tflops, 1),
+        "frac_of_measured_mfma_peak": round(tflops / probe_tflops, 4) if probe_tflops > 0 else None,
         "phases_ms": {p: round(t, 4) for p, t in phases.items()},
         "roofline": {"kernel": dom, "kernel_ms": round(dom_ms, 4), "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
