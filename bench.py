@@ -203,14 +203,14 @@ def cpu_baseline(inst, hkv, hadamard=0, mixed=0, exact=0, target_s=10.0):
         km = np.zeros(hkv, np.uint8)
         km[:n] = 1
         t0 = time.perf_counter()
-        oracle.attention(inst["q"], inst["k"], inst["v"], inst["do"], inst["cu_seqlens"],
-                         oracle.Opts(hadamard=hadamard, mixed=mixed, exact=exact), kv_mask=km, want_f64=False)
-        return time.perf_counter() - t0
+        r = oracle.attention(inst["q"], inst["k"], inst["v"], inst["do"], inst["cu_seqlens"],
+                             oracle.Opts(hadamard=hadamard, mixed=mixed, exact=exact), kv_mask=km, want_f64=False)
+        return time.perf_counter() - t0, r["stats"]
 
-    n, dt = 1, run(1)
+    n, (dt, stats) = 1, run(1)
     while dt < target_s and n < hkv:   # more heads also parallelize better: double
         n = min(hkv, 2 * n)
-        dt = run(n)
+        dt, stats = run(n)
     hq, d = inst["q"].shape[1], inst["q"].shape[2]
     G = hq // hkv
     flop = 7.0 * n * G * d * inst["sum_L2"]
@@ -219,7 +219,9 @@ def cpu_baseline(inst, hkv, hadamard=0, mixed=0, exact=0, target_s=10.0):
             "sample": f"key/value head{'s 0-' + str(n - 1) if n > 1 else ' 0'} of {hkv} ({n * G} of {hq} query heads), all "
                       f"{len(inst['lengths'])} documents, forward + backward incl. quantization"
                       f"{' (mixed NVFP4/FP8 path)' if mixed else ''}{' (exact options)' if exact else ''}; "
-                      f"{dt:.1f} s wall"}
+                      f"{dt:.1f} s wall",
+            # the oracle's fraction of nonzero dS entries quantized to zero on the sample
+            "ds_zero_fraction": round(float(stats[2]) / max(1, int(stats[1])), 6)}
 
 
 def inference_bench(args, call, q, k, v, cu, stream, hip, wl, inst, doclen_cap):
@@ -461,6 +463,19 @@ def main():
     graph_median = graph_steps[args.steps // 2] if args.steps % 2 else \
         0.5 * (graph_steps[args.steps // 2 - 1] + graph_steps[args.steps // 2])
 
+    # ---- diagnostics (outside the timed passes): the fraction of nonzero dS
+    # entries that quantize to a zero dS-hat code (Sections 3.3, 4.5), counted
+    # by the diagnostics instantiation of the key-major pass
+    ds_zero_fraction = None
+    if not (args.mixed or args.exact):
+        cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        call.opts.ds_zero_count = cnt.data_ptr()
+        run_step()
+        torch.cuda.synchronize()
+        call.opts.ds_zero_count = None
+        entries = hq * sum(int(L) * (int(L) + 1) // 2 for L in inst["lengths"])
+        ds_zero_fraction = round(int(cnt.item()) / entries, 6)
+
     # ---- pass 5: achievable matrix-core rate
     log("[bench] matrix-core probe")
     probe_tflops = mfma_probe(hip, stream)
@@ -492,6 +507,7 @@ def main():
         "graph_ms_per_step": round(graph_ms_step, 4),
         "graph_median_tflops": round(flop / (graph_median * 1e-3) / 1e12, 2),
         "measured_mfma_peak_tflops": round(probe_tflops, 1),
+        "ds_zero_fraction": ds_zero_fraction,
         "frac_of_measured_mfma_peak": round(tflops / probe_tflops, 4) if probe_tflops > 0 else None,
         "phases_ms": {p: round(t, 4) for p, t in phases.items()},
         "roofline": {"kernel": dom, "kernel_ms": round(dom_ms, 4), "bound": "mfma", "achieved": round(achieved, 2),

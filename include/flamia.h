@@ -48,8 +48,12 @@
  *  - Errors: arguments are validated on the host before anything is enqueued;
  *    on any error nothing is enqueued and a status code is returned.
  *    FLAMIA_ERR_HIP reports a failed launch (the HIP error text is kept per
- *    thread, see flamia_last_error()).  Contents of cu_seqlens are not
- *    checked (a device array); a malformed array is undefined behaviour.
+ *    thread, see flamia_last_error()).  cu_seqlens is checked on the device
+ *    by the work-list kernel of every flamia_fwd / flamia_bwd call: a
+ *    malformed array (cu[0] != 0, a decreasing pair, a boundary outside
+ *    [0, ttot], cu[ndocs] != ttot) makes the call do no attention work (its
+ *    outputs are then unspecified, and nothing is read or written outside the
+ *    tensors) and is reported through opts->cu_status.
  */
 #ifndef FLAMIA_H
 #define FLAMIA_H
@@ -61,7 +65,7 @@
 extern "C" {
 #endif
 
-#define FLAMIA_ABI_VERSION 6
+#define FLAMIA_ABI_VERSION 7
 
 typedef enum {
     FLAMIA_OK = 0,
@@ -143,6 +147,32 @@ typedef struct {
      * computes D; key-major dK/dV kernel).  NULL disables it. */
     void **phase_events;
     int32_t n_events;
+    /* Optional diagnostics; NULL pointers (the defaults) switch them off.
+     * cu_status: device int32, written by every flamia_fwd / flamia_bwd call:
+     *   0 when cu_seqlens is well formed (Section 3.6.1 packed layout), else
+     *   bit 0 (cu[0] != 0) | bit 1 (a decreasing pair) | bit 2 (a boundary
+     *   outside [0, ttot] or cu[ndocs] != ttot).
+     * ds_zero_count: device uint64, flamia_bwd adds the number of dS entries
+     *   that are nonzero but quantize to a zero dS-hat code (the fraction of
+     *   such entries tracks degradation, Sections 3.3 and 4.5); the caller
+     *   zeroes it.
+     * probe_scores: device fp32 [3][128][probe_keys]: the raw scores
+     *   S = q . k (block scales applied, before softmax_scale) of the 128
+     *   queries that start at packed token probe_q0 (a query tile: probe_q0 -
+     *   probe_doc_start a multiple of 128) of the document that starts at
+     *   packed token probe_doc_start, query head probe_head, document-local
+     *   keys 0 .. probe_keys - 1: table 0 as flamia_fwd computes them, 1 as
+     *   the dQ pass of flamia_bwd rebuilds them (without a dS store), 2 as
+     *   the dK/dV pass does (Section 3.3: the backward reproduces the
+     *   forward's scores).  Entries of keys after the query, or outside the
+     *   document, are not written.
+     * Diagnostics run separate kernel instantiations, on the MXFP8 path with
+     * the exact exponential only (FLAMIA_ERR_OPTS with mixed, exact or
+     * fast_exp). */
+    int32_t *cu_status;
+    uint64_t *ds_zero_count;
+    float *probe_scores;
+    int32_t probe_doc_start, probe_q0, probe_head, probe_keys;
 } flamia_opts_t;
 
 typedef struct {

@@ -69,7 +69,17 @@ flamia_status_t check_opts(const flamia_opts_t* o) {
     if (o->exact && (o->rowsum || o->fast_exp || o->mixed)) return FLAMIA_ERR_OPTS;
     if (!(o->softmax_scale <= 0.f || isfinite(o->softmax_scale))) return FLAMIA_ERR_OPTS;
     if (o->n_events < 0 || (o->n_events > 0 && !o->phase_events)) return FLAMIA_ERR_OPTS;
+    // diagnostics instantiations exist for the MXFP8 path with the exact exponential
+    if ((o->probe_scores || o->ds_zero_count) && (o->mixed || o->exact || o->fast_exp)) return FLAMIA_ERR_OPTS;
+    if (o->probe_scores && (o->probe_keys <= 0 || o->probe_head < 0 || o->probe_doc_start < 0 ||
+                            o->probe_q0 < o->probe_doc_start || (o->probe_q0 - o->probe_doc_start) % kTile))
+        return FLAMIA_ERR_OPTS;
     return FLAMIA_OK;
+}
+
+ProbeArgs probe_of(const flamia_opts_t& o) {
+    return ProbeArgs{o.probe_scores, o.probe_doc_start, o.probe_q0, o.probe_head, o.probe_keys,
+                     (unsigned long long*)o.ds_zero_count};
 }
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -180,8 +190,8 @@ flamia_status_t fwd_enqueue(const flamia_dims_t* dims, const flamia_opts_t& opts
     if ((e = pm.mark()) != hipSuccess || (e = launch_quantize(qa, st)) != hipSuccess) return hip_fail(e);
     int32_t* ctrl = (int32_t*)(base + w.ctrl);
     int4* tiles = (int4*)(base + w.tiles_q);
-    PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
-                tiles, nullptr, nullptr, 0};
+    PlanArgs pa{cu_seqlens, dims->ndocs, dims->ttot, opts.cu_status, w.max_cost, (int32_t*)(base + w.prefix),
+                ctrl, w.max_tiles, tiles, nullptr, nullptr, 0};
     if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
     FwdArgs fa;
     fa.qc = q_mx.codes; fa.qs = q_mx.scales;
@@ -197,6 +207,8 @@ flamia_status_t fwd_enqueue(const flamia_dims_t* dims, const flamia_opts_t& opts
     fa.fast_exp = opts.fast_exp;
     fa.qn = qn; fa.kn = kn;
     fa.exact = opts.exact;
+    fa.probe = probe_of(opts);
+    fa.probe.ds_zero = nullptr;
     if ((e = pm.mark()) != hipSuccess || (e = launch_fwd(fa, d, w.max_tiles * dims->hq, st)) != hipSuccess)
         return hip_fail(e);
     e = pm.mark();
@@ -240,6 +252,11 @@ flamia_opts_t flamia_default_opts(void) {
     o.exact = 0;
     o.phase_events = nullptr;
     o.n_events = 0;
+    o.cu_status = nullptr;
+    o.ds_zero_count = nullptr;
+    o.probe_scores = nullptr;
+    o.probe_doc_start = o.probe_q0 = o.probe_head = 0;
+    o.probe_keys = 0;
     return o;
 }
 
@@ -363,8 +380,8 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     int32_t* dboff = (int32_t*)(base + w.dboff);
     uint8_t* ds_codes = base + w.ds_codes;
     uint8_t* ds_scales = base + w.ds_scales;
-    PlanArgs pa{cu_seqlens, dims->ndocs, w.max_cost, (int32_t*)(base + w.prefix), ctrl, w.max_tiles,
-                tiles_q, tiles_k, dboff, ds_blocks};
+    PlanArgs pa{cu_seqlens, dims->ndocs, dims->ttot, opts.cu_status, w.max_cost, (int32_t*)(base + w.prefix),
+                ctrl, w.max_tiles, tiles_q, tiles_k, dboff, ds_blocks};
     const float scale = scale_of(opts, d);
     BwdArgs ba;
     ba.qc = q_mx.codes; ba.qs = q_mx.scales;
@@ -382,6 +399,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     ba.kn = opts.mixed ? k_mx.nv : nullptr;
     ba.ds_codes = ds_codes; ba.ds_scales = ds_scales; ba.dboff = dboff; ba.ds_blocks = ds_blocks;
     ba.exact = opts.exact;
+    ba.probe = probe_of(opts);
     DqArgs qd;
     qd.qc = q_mx.codes; qd.qs = q_mx.scales;
     qd.kc = k_mx.codes; qd.ks = k_mx.scales;
@@ -398,6 +416,8 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     qd.d_o = nullptr; qd.o = nullptr; qd.oc_w = nullptr; qd.os_w = nullptr; qd.dvec_w = nullptr;
     qd.ds_codes = ds_codes; qd.ds_scales = ds_scales; qd.dboff = dboff; qd.ds_blocks = ds_blocks;
     qd.exact = opts.exact;
+    qd.probe = probe_of(opts);
+    qd.probe.ds_zero = nullptr;
     PhaseMarks pm{opts, st};
     hipError_t e;
     const long gq = w.max_tiles * dims->hq, gk = w.max_tiles * dims->hkv;

@@ -70,7 +70,8 @@ struct BwdSmem {
     BwdStep<D, MIX, EXACT> buf[N];
 };
 
-template <int D, bool STORE, int MIX, int EXACT>
+// PROBE = 1: the diagnostics instantiation (probed raw scores, dS-hat zero count).
+template <int D, bool STORE, int MIX, int EXACT, int PROBE = 0>
 __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
     constexpr int KC = D / 64;
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
@@ -205,6 +206,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
     v16f dvt[DT], dkt[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) { dvt[dt] = v16f{0}; dkt[dt] = v16f{0}; }
+    unsigned nzero = 0;     // diagnostics: nonzero dS entries whose dS-hat code is zero
 
     const int s16 = lane & 15, grp = (lane >> 4) & 1;
     const int tr_key = 8 * ((s16 >> 1) >> 2) + 4 * lg + ((s16 >> 1) & 3);
@@ -341,6 +343,15 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
                 es[st] = 127;
                 continue;
             }
+            if constexpr (PROBE) {
+                // diagnostics: the raw scores of the probed query tile
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float* sp = probe_slot(a.probe, 2, h, ds, ds + qs0 + 32 * st + 8 * (i >> 2) + 4 * lg + (i & 3),
+                                           key_loc);
+                    if (sp) *sp = sacc[st][i];
+                }
+            }
             float dsv[16];
             float amax = 0.f;
 #pragma unroll
@@ -378,6 +389,11 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
                 pbc[st][j] = pack_fp8x4_div(sacc[st][4 * j], sacc[st][4 * j + 1], sacc[st][4 * j + 2],
                                             sacc[st][4 * j + 3], inv256);
                 dsc[st][j] = pack_fp8x4_div(dsv[4 * j], dsv[4 * j + 1], dsv[4 * j + 2], dsv[4 * j + 3], sc);
+            }
+            if constexpr (PROBE) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    nzero += (dsv[i] != 0.f && ((((uint32_t)dsc[st][i >> 2] >> (8 * (i & 3))) & 0x7Fu) == 0u)) ? 1u : 0u;
             }
         }
         // ---- dS store: block (qb, kb) as [query half][32 keys][16 queries]
@@ -444,6 +460,10 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
     }
     if (PIPE && dvdk_due) dvdk(sm.buf[prv], ppbc, pdsc, pes);
     flush_store();
+    if constexpr (PROBE) {
+        const unsigned n = wave_sum_u32(nzero);
+        if (a.probe.ds_zero && lane == 0 && n) atomicAdd(a.probe.ds_zero, (unsigned long long)n);
+    }
     // ---- epilogue: dK = softmax_scale * sum, dV; summed over the group's heads.
     // With the Hadamard option the dK sum is the gradient of the rotated K and
     // is rotated back first.
@@ -487,6 +507,13 @@ hipError_t launch_bwd(const BwdArgs& a, int d, long grid, hipStream_t st) {
     if (a.exact) {
         if (store || a.qn) return hipErrorInvalidValue;
         hipLaunchKernelGGL((bwd_kernel<64, false, 0, 1>), g, dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    if (a.probe.scores || a.probe.ds_zero) {
+        // diagnostics: the MXFP8 path (checked by the host layer)
+        if (a.qn) return hipErrorInvalidValue;
+        if (store) hipLaunchKernelGGL((bwd_kernel<64, true, 0, 0, 1>), g, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((bwd_kernel<64, false, 0, 0, 1>), g, dim3(256), 0, st, a);
         return hipGetLastError();
     }
     if (store) launch_bwd_mix<64, true>(a, g, st);

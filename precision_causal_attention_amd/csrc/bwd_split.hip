@@ -72,7 +72,8 @@ struct SplitSmem {
 
 }  // namespace
 
-template <bool STORE, int MIX, int EXACT>
+// PROBE = 1: the diagnostics instantiation (probed raw scores, dS-hat zero count).
+template <bool STORE, int MIX, int EXACT, int PROBE = 0>
 __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     constexpr int D = kSD;
     constexpr int KC = D / 64;
@@ -103,6 +104,7 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     __shared__ int next_item;
     const int nitems = *a.ntiles * a.hkv;
     int item = (int)blockIdx.x;
+    unsigned nzero = 0;     // diagnostics: nonzero dS entries whose dS-hat code is zero
     while (item < nitems) {
     int claim = 0;   // the next item, claimed during this item's last step
     const int ti = item / a.hkv;
@@ -295,6 +297,15 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
             // ---- P, P-hat_b, dS, dS-hat; register i = 4j + r holds query
             // qs0 + 32 hf + 8j + 4lg + r, masked while the key lies after it
             const int lim = key_loc - qs0 - 32 * hf - 4 * lg;
+            if constexpr (PROBE) {
+                // diagnostics: the raw scores of the probed query tile
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float* sp = probe_slot(a.probe, 2, h, ds, ds + qs0 + 32 * hf + 8 * (i >> 2) + 4 * lg + (i & 3),
+                                           key_loc);
+                    if (sp) *sp = sacc[i];
+                }
+            }
             float amax = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -329,6 +340,11 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
             for (int j = 0; j < 4; ++j) {
                 pbc[j] = pack_fp8x4_div(sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3], inv256);
                 dsc[j] = pack_fp8x4_div(pacc[4 * j], pacc[4 * j + 1], pacc[4 * j + 2], pacc[4 * j + 3], sc);
+            }
+            if constexpr (PROBE) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    nzero += (pacc[i] != 0.f && ((((uint32_t)dsc[i >> 2] >> (8 * (i & 3))) & 0x7Fu) == 0u)) ? 1u : 0u;
             }
         }
         // ---- dS store: this wave's block (qb, kb) as [query half][32 keys][16 queries]
@@ -455,6 +471,10 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     __syncthreads();
     item = next_item;
     }   // work items
+    if constexpr (PROBE) {
+        const unsigned n = wave_sum_u32(nzero);
+        if (a.probe.ds_zero && (threadIdx.x & 63) == 0 && n) atomicAdd(a.probe.ds_zero, (unsigned long long)n);
+    }
 }
 
 hipError_t device_cus(int* n) {
@@ -490,6 +510,11 @@ hipError_t launch_bwd_split(const BwdArgs& a, long grid, hipStream_t st) {
     if (a.exact) {
         if (store || a.qn) return hipErrorInvalidValue;
         hipLaunchKernelGGL((bwd_split_kernel<false, 0, 1>), g, b, 0, st, a);
+    } else if (a.probe.scores || a.probe.ds_zero) {
+        // diagnostics: the MXFP8 path (checked by the host layer)
+        if (a.qn) return hipErrorInvalidValue;
+        if (store) hipLaunchKernelGGL((bwd_split_kernel<true, 0, 0, 1>), g, b, 0, st, a);
+        else hipLaunchKernelGGL((bwd_split_kernel<false, 0, 0, 1>), g, b, 0, st, a);
     } else if (a.qn) {
         if (store) hipLaunchKernelGGL((bwd_split_kernel<true, 1, 0>), g, b, 0, st, a);
         else hipLaunchKernelGGL((bwd_split_kernel<false, 1, 0>), g, b, 0, st, a);

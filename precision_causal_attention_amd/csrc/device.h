@@ -102,6 +102,14 @@ __device__ __forceinline__ float fp8_to_f32(uint32_t code) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ unsigned wave_sum_u32(unsigned v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += (unsigned)__shfl_xor((int)v, off);
+    return v;
+}
+
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
 // Two fp32 -> two bf16 packed in one word (a in the low half), round to

@@ -54,7 +54,8 @@ struct DqSmem {
 
 // At least two workgroups per CU at both head dimensions (at d = 128 one wave
 // per SIMD left latencies exposed: 36% longer).
-template <int D, int MIX, bool FUSED, int EXACT>
+// PROBE = 1: the diagnostics instantiation (writes the probed raw scores).
+template <int D, int MIX, bool FUSED, int EXACT, int PROBE = 0>
 __global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
     constexpr int KC = D / 64;
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
@@ -297,6 +298,15 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
         // P, dS and the dS-hat codes of block kk (in place in dpb); `masked`:
         // the block holds the diagonal of the wave's queries
         auto softmax = [&](const int kk, const v16f& sb, v16f& dpb, int (&codes)[4], int& ebyte, bool masked) {
+            if constexpr (PROBE) {
+                // diagnostics: the raw scores of the probed query tile
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float* sp = probe_slot(a.probe, 1, h, ds, ds + q_loc,
+                                           kTile * t + 32 * kk + 8 * (i >> 2) + 4 * lg + (i & 3));
+                    if (sp) *sp = sb[i];
+                }
+            }
             float amax = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -395,6 +405,18 @@ hipError_t launch_dq(const DqArgs& a, int d, long grid, hipStream_t st) {
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), b(256);
     const bool fused = a.d_o != nullptr;
+    if (a.probe.scores) {
+        // diagnostics: the MXFP8 path (checked by the host layer)
+        if (a.exact || a.qn) return hipErrorInvalidValue;
+        if (d == 64) {
+            if (fused) hipLaunchKernelGGL((dq_kernel<64, 0, true, 0, 1>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((dq_kernel<64, 0, false, 0, 1>), g, b, 0, st, a);
+        } else {
+            if (fused) hipLaunchKernelGGL((dq_kernel<128, 0, true, 0, 1>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((dq_kernel<128, 0, false, 0, 1>), g, b, 0, st, a);
+        }
+        return hipGetLastError();
+    }
     if (a.exact) {
         if (!fused || a.qn) return hipErrorInvalidValue;
         if (d == 64) hipLaunchKernelGGL((dq_kernel<64, 0, true, 1>), g, b, 0, st, a);

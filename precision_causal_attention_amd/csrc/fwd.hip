@@ -76,7 +76,8 @@ __device__ __forceinline__ constexpr int pair_class(int i) {
 // options' d = 64 variant is held to three waves per SIMD, like the default
 // one reaches by itself: three spilled registers cost less than the lost
 // wave (the forward ran 14% faster).
-template <int D, int ROWSUM, int FAST, int MIX, int EXACT>
+// PROBE = 1: the diagnostics instantiation (writes the probed raw scores).
+template <int D, int ROWSUM, int FAST, int MIX, int EXACT, int PROBE = 0>
 __global__ void __launch_bounds__(256, (D == 64 && EXACT) ? 3 : 2) fwd_kernel(const FwdArgs a) {
     constexpr int KC = D / 64;                    // 64-channel contraction steps of S
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
@@ -235,6 +236,19 @@ __global__ void __launch_bounds__(256, (D == 64 && EXACT) ? 3 : 2) fwd_kernel(co
                 }
             }
         }
+        if constexpr (PROBE) {
+            // diagnostics: the raw scores of the probed query tile (before the mask)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (DIAG && kk > wave_u) continue;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float* sp = probe_slot(a.probe, 0, h, ds, ds + q_loc,
+                                           kTile * t + 32 * kk + 8 * (i >> 2) + 4 * lg + (i & 3));
+                    if (sp) *sp = s[kk][i];
+                }
+            }
+        }
         // ---- causal mask (sub-tile kk == wave of the diagonal tile):
         // accumulator register i of sub-tile kk holds key 128t + 32kk +
         // 8(i/4) + 4lg + i%4; it is masked when that key lies after the lane's
@@ -370,6 +384,18 @@ hipError_t launch_fwd(const FwdArgs& a, int d, long grid, hipStream_t st) {
     // the exact options take the unquantized row sum, the exact exponential
     // and the MXFP8 scores (checked by the host layer)
     if (a.exact && (a.rowsum || a.fast_exp || a.qn)) return hipErrorInvalidValue;
+    if (a.probe.scores) {
+        // diagnostics: the MXFP8 path with the exact exponential (checked by the host layer)
+        if (a.exact || a.fast_exp || a.qn) return hipErrorInvalidValue;
+        if (d == 64) {
+            if (a.rowsum) hipLaunchKernelGGL((fwd_kernel<64, 1, 0, 0, 0, 1>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((fwd_kernel<64, 0, 0, 0, 0, 1>), g, b, 0, st, a);
+        } else {
+            if (a.rowsum) hipLaunchKernelGGL((fwd_kernel<128, 1, 0, 0, 0, 1>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((fwd_kernel<128, 0, 0, 0, 0, 1>), g, b, 0, st, a);
+        }
+        return hipGetLastError();
+    }
     if (d == 64) {
         if (a.exact) hipLaunchKernelGGL((fwd_kernel<64, 0, 0, 0, 1>), g, b, 0, st, a);
         else if (a.rowsum) launch_fwd_fast<64, 1>(a, g, b, st);

@@ -42,9 +42,38 @@ struct QuantArgs {
 // ([2][32][16]: query half, key, 16 queries) and one UE8M0 scale byte.
 constexpr int kDsBlockBytes = kBlock * kBlock;
 
+// Optional diagnostics of the attention kernels, run by separate
+// instantiations (PROBE = 1) that the default launches never use.
+//   scores: fp32 [3][128][keys], the raw scores S = q.k (block scales
+//   applied, before the softmax scale) of the 128-query tile that starts at
+//   packed token q0 of the document starting at packed token doc_start, query
+//   head `head`, keys in document-local order: [0] as the forward computes
+//   them, [1] the dQ pass, [2] the dK/dV pass (nullptr: none);
+//   ds_zero: the dK/dV pass adds the number of nonzero dS entries whose
+//   dS-hat code is zero (nullptr: none).
+struct ProbeArgs {
+    float* scores;
+    int doc_start, q0, head, keys;
+    unsigned long long* ds_zero;
+};
+
+// Address of the probed score of query `qrow` (packed token) and
+// key `key` (document-local) in table `which` (0 forward, 1 dQ pass, 2 dK/dV
+// pass), or nullptr when this (head, document, query, key) is not probed.
+__device__ __forceinline__ float* probe_slot(const ProbeArgs& p, int which, int head, int doc_start,
+                                             int qrow, int key) {
+    const int qi = qrow - p.q0;
+    if (!p.scores || head != p.head || doc_start != p.doc_start || qi < 0 || qi >= kTile || key < 0 ||
+        key >= p.keys)
+        return nullptr;
+    return p.scores + ((long)which * kTile + qi) * p.keys + key;
+}
+
 struct PlanArgs {
     const int32_t* cu;
     int ndocs;
+    int ttot;
+    int32_t* cu_status;    // nonzero bits when cu_seqlens is malformed (nullptr: not reported)
     int max_cost;          // >= max tiles of one document
     int32_t* tiles_prefix; // [ndocs + 1]
     int32_t* ctrl;         // control block, see plan.hip
@@ -69,6 +98,7 @@ struct FwdArgs {
     int fast_exp;          // 0, or 5 / 8 key-pair classes of 8 with the approximate exponential
     const uint16_t *qn, *kn;   // mixed path: NVFP4 values of Q and K (bf16) for the scores; else nullptr
     int exact;                 // 1: the exact options (per-token scales, V's folded into P-hat)
+    ProbeArgs probe;           // diagnostics (launches the PROBE instantiation when set)
 };
 
 struct BwdArgs {
@@ -88,6 +118,7 @@ struct BwdArgs {
     const int32_t* dboff;
     long ds_blocks;
     int exact;                // 1: the exact options (dO's and Q's token exponents folded)
+    ProbeArgs probe;
 };
 
 struct DqArgs {
@@ -113,6 +144,7 @@ struct DqArgs {
     const int32_t* dboff;
     long ds_blocks;
     int exact;                // 1: the exact options (K's token exponent folded, per-row dS exponent)
+    ProbeArgs probe;
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);

@@ -15,6 +15,12 @@
 // Work item (tile, head) is decoded by the attention kernels from the
 // workgroup index, heads innermost.
 //
+// A malformed cu_seqlens (cu[0] != 0, a decreasing pair, a boundary outside
+// [0, ttot], or cu[ndocs] != ttot) yields no tile at all, so the attention
+// kernels do no work, and the caller's status word (when given) gets the
+// reason: bit 0 cu[0] != 0, bit 1 a decreasing pair, bit 2 a boundary outside
+// [0, ttot] or cu[ndocs] != ttot; 0 for a well-formed array.
+//
 // ctrl layout (int32): [0] number of tiles, [1] 1 if the backward's dS store
 // holds this call's blocks (capacity given and not exceeded), else 0, [2] the
 // work-queue counter of the persistent key-major pass at d = 128 (zeroed here,
@@ -75,7 +81,8 @@ __device__ void block_scan(int* buf, int n, bool reverse, int* wsum) {
 }
 
 __global__ void __launch_bounds__(kPlanThreads)
-plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __restrict__ tiles_prefix,
+plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __restrict__ cu_status,
+            int max_cost, int32_t* __restrict__ tiles_prefix,
             int32_t* __restrict__ ctrl, long max_tiles, int4* __restrict__ tiles_q, int4* __restrict__ tiles_k,
             int32_t* __restrict__ dboff, long ds_blocks) {
     extern __shared__ int smem[];
@@ -86,7 +93,28 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __
     __shared__ int wsum[kPlanWaves];
     __shared__ long lwsum[kPlanWaves];
     __shared__ int lpref[kPrefixLds];          // tile prefix of the documents (ndocs < kPrefixLds)
+    __shared__ int bad_all;
     const int tid = threadIdx.x;
+    // ---- the packed layout's preconditions (Section 3.6.1)
+    int bad = 0;
+    for (int d = tid; d < ndocs; d += kPlanThreads) {
+        const int a0 = cu[d], a1 = cu[d + 1];
+        if (a1 < a0) bad |= 2;
+        if (a0 < 0 || a1 > ttot) bad |= 4;
+    }
+    if (tid == 0) {
+        if (cu[0] != 0) bad |= 1;
+        if (cu[ndocs] != ttot) bad |= 4;
+        bad_all = 0;
+    }
+    __syncthreads();
+    if (bad) atomicOr(&bad_all, bad);
+    __syncthreads();
+    if (tid == 0 && cu_status) *cu_status = bad_all;
+    if (bad_all) {
+        if (tid == 0) ctrl[0] = ctrl[1] = ctrl[2] = 0;
+        return;
+    }
     for (int c = tid; c < C1; c += kPlanThreads) hist[c] = curq[c] = curk[c] = 0;
     __syncthreads();
     for (int d = tid; d < ndocs; d += kPlanThreads) {
@@ -187,7 +215,8 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int max_cost, int32_t* __
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
     const size_t smem = sizeof(int) * 3 * ((size_t)a.max_cost + 1);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), smem, st, a.cu, a.ndocs, a.max_cost,
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), smem, st, a.cu, a.ndocs, a.ttot, a.cu_status,
+                       a.max_cost,
                        a.tiles_prefix, a.ctrl, a.max_tiles, a.tiles_q, a.tiles_k, a.dboff, a.ds_blocks);
     return hipGetLastError();
 }

@@ -158,7 +158,10 @@ __global__ void __launch_bounds__(256) quantize_kernel(const QuantArgs a) {
     const int tok0 = lane / CPT;             // token of chunk r is tok0 + r * (64 / CPT)
 
     for (int doc = find_doc(a.cu, a.ndocs, w0); doc < a.ndocs; ++doc) {
-        const int ds = a.cu[doc], de = a.cu[doc + 1];
+        // boundaries clamped into [0, ttot], non-decreasing: a malformed
+        // cu_seqlens (reported by the work-list kernel) never reads or
+        // writes outside the tensors
+        const int ds = min(max(a.cu[doc], 0), a.ttot), de = min(max(a.cu[doc + 1], ds), a.ttot);
         if (ds >= w0 + kBlock) break;
         if (de <= w0) continue;
         const int rel = w0 - ds;

@@ -30,7 +30,10 @@ class Opts(ctypes.Structure):
     _fields_ = [("c_log2", ctypes.c_int32), ("tau", ctypes.c_int32), ("key_tile", ctypes.c_int32),
                 ("rowsum", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("hadamard", ctypes.c_int32), ("fast_exp", ctypes.c_int32), ("mixed", ctypes.c_int32),
-                ("exact", ctypes.c_int32), ("phase_events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32)]
+                ("exact", ctypes.c_int32), ("phase_events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32),
+                ("cu_status", ctypes.c_void_p), ("ds_zero_count", ctypes.c_void_p), ("probe_scores", ctypes.c_void_p),
+                ("probe_doc_start", ctypes.c_int32), ("probe_q0", ctypes.c_int32), ("probe_head", ctypes.c_int32),
+                ("probe_keys", ctypes.c_int32)]
 
 
 class Mx(ctypes.Structure):

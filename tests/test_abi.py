@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_defaults(L):
-    assert F.flamia_abi_version() == 6
+    assert F.flamia_abi_version() == 7
     o = F.flamia_default_opts()
     assert (o.c_log2, o.tau, o.key_tile, o.rowsum, o.hadamard, o.fast_exp, o.mixed, o.exact) == \
         (4, 4, 128, 0, 0, 0, 0, 0)
