@@ -52,8 +52,12 @@ __device__ __forceinline__ v2i lds_read_tr8(const uint8_t* lds_addr) {
 // Four fp32 -> four E4M3 bytes (byte i = element i), round to nearest even;
 // bit-identical to the format's definition for |x| <= 448.
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-    // both halves are overwritten, so the incoming register content is irrelevant
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
+    // Both halves are overwritten, so the destination's incoming content is
+    // irrelevant; leaving the seed undefined lets the compiler convert in
+    // place instead of first copying a live value into the destination (one
+    // VALU move per four codes).
+    int seed;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, seed, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 // Same with an exact power-of-two divisor: byte i = E4M3(x_i / scale).
