@@ -191,7 +191,7 @@ flamia_status_t fwd_enqueue(const flamia_dims_t* dims, const flamia_opts_t& opts
     int32_t* ctrl = (int32_t*)(base + w.ctrl);
     int4* tiles = (int4*)(base + w.tiles_q);
     PlanArgs pa{cu_seqlens, dims->ndocs, dims->ttot, opts.cu_status, w.max_cost, (int32_t*)(base + w.prefix),
-                ctrl, w.max_tiles, tiles, nullptr, nullptr, 0};
+                ctrl, w.max_tiles, tiles, nullptr, 0, nullptr, 0};
     if ((e = pm.mark()) != hipSuccess || (e = launch_plan(pa, st)) != hipSuccess) return hip_fail(e);
     FwdArgs fa;
     fa.qc = q_mx.codes; fa.qs = q_mx.scales;
@@ -381,7 +381,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     uint8_t* ds_codes = base + w.ds_codes;
     uint8_t* ds_scales = base + w.ds_scales;
     PlanArgs pa{cu_seqlens, dims->ndocs, dims->ttot, opts.cu_status, w.max_cost, (int32_t*)(base + w.prefix),
-                ctrl, w.max_tiles, tiles_q, tiles_k, dboff, ds_blocks};
+                ctrl, w.max_tiles, tiles_q, tiles_k, d == 128 ? 1 : 0, dboff, ds_blocks};
     const float scale = scale_of(opts, d);
     BwdArgs ba;
     ba.qc = q_mx.codes; ba.qs = q_mx.scales;

@@ -33,7 +33,8 @@ struct QuantArgs {
 };
 
 // Tile lists: int4 {first token of the 128-token tile (global), document
-// start, document end, document index}, ordered by decreasing cost; ctrl[0]
+// start, document end, document index}, expensive items first (plan.hip);
+// ctrl[0]
 // holds the number of tiles.  A work item is (tile, head): the attention
 // kernels decode it from the workgroup index (tile = index / heads).
 // dS store: per query head, the 32x32 causal blocks (qb >= kb, document-local
@@ -81,6 +82,7 @@ struct PlanArgs {
     int4* tiles_q;         // query-major order: cost = tile index + 1 (forward, dQ)
     int4* tiles_k;         // key-major order: cost = tiles from the diagonal to the end
                            // (dK/dV); nullptr: not built
+    int key_docmajor;      // 1: the key-major list in document-major order (else cost-major)
     int32_t* dboff;        // [ndocs] first dS block of each document (nullptr: none)
     long ds_blocks;        // dS store capacity in blocks per head (0: no store)
 };

@@ -6,12 +6,20 @@
 // its first token.
 //   query-major (forward, dQ): query tile t attends t+1 key tiles  -> cost t + 1
 //   key-major (dK/dV)        : key tile t meets n - t query tiles  -> cost n - t
-// Both give every document the costs 1..n, so one histogram serves both.
-// Tiles are ordered by decreasing cost (longest first; the hardware
-// dispatches workgroups in index order, so the expensive items start first
-// and the cheap ones fill in at the end).  Sorting is a counting sort on the
-// small integer cost instead of a comparison sort.  Within one cost class the
-// order is whatever the atomics give; it does not change any result.
+// Both give every document the costs 1..n.  Two orders, both with the
+// expensive items first (the hardware dispatches workgroups in index order,
+// so the expensive items start first and the cheap ones fill in at the end):
+//   document-major: documents by decreasing tile count, and within a
+//   document its tiles by decreasing cost, so the items that run at the same
+//   time on an XCD mostly belong to one document and share its K/V (query
+//   major) or Q/dO rows (key major) in that XCD's L2;
+//   cost-major: all tiles by decreasing cost, documents interleaved.
+// The query-major list is document-major; the key-major one is document-major
+// when the caller asks for it (the d = 128 pass: 2-5% faster; the d = 64 pass
+// ran 2% slower so), else cost-major.  Beyond kPrefixLds documents both lists
+// are cost-major.  Sorting is a counting sort on the small integer tile count
+// or cost instead of a comparison sort.  Within one class the order is
+// whatever the atomics give; it does not change any result.
 // Work item (tile, head) is decoded by the attention kernels from the
 // workgroup index, heads innermost.
 //
@@ -84,15 +92,19 @@ __global__ void __launch_bounds__(kPlanThreads)
 plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __restrict__ cu_status,
             int max_cost, int32_t* __restrict__ tiles_prefix,
             int32_t* __restrict__ ctrl, long max_tiles, int4* __restrict__ tiles_q, int4* __restrict__ tiles_k,
-            int32_t* __restrict__ dboff, long ds_blocks) {
+            int key_docmajor, int32_t* __restrict__ dboff, long ds_blocks) {
     extern __shared__ int smem[];
     const int C1 = max_cost + 1;
     int* hist = smem;                          // C1: tile counts by cost class
-    int* curq = smem + C1;                     // C1: query-major placement cursors
-    int* curk = smem + 2 * C1;                 // C1: key-major placement cursors
+    // C1 each: placement cursors of the cost-major lists; with the LDS prefix
+    // table curq first holds the tiles of the documents with at least c tiles
+    // and curk the document cursors by tile count (document-major order)
+    int* curq = smem + C1;
+    int* curk = smem + 2 * C1;
     __shared__ int wsum[kPlanWaves];
     __shared__ long lwsum[kPlanWaves];
     __shared__ int lpref[kPrefixLds];          // tile prefix of the documents (ndocs < kPrefixLds)
+    __shared__ int ldbase[kPrefixLds];         // first slot of each document, document-major
     __shared__ int bad_all;
     const int tid = threadIdx.x;
     // ---- the packed layout's preconditions (Section 3.6.1)
@@ -123,6 +135,15 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
         if (n > 0) atomicAdd(&hist[n], 1);
     }
     __syncthreads();
+    const bool lds_pref = ndocs < kPrefixLds;
+    int* above = curq;
+    if (lds_pref) {
+        // above[c] = c x (#docs with n == c), summed from the end: the tiles
+        // of the documents with at least c tiles
+        for (int c = tid; c < C1; c += kPlanThreads) above[c] = c * hist[c];
+        __syncthreads();
+        block_scan(above, C1, true, wsum);
+    }
     // hist[c] = #docs with n >= c = number of tiles of cost c (c >= 1)
     block_scan(hist, C1, true, wsum);
     // hist[c] = number of tiles of cost >= c; the class of cost c starts at
@@ -134,7 +155,6 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
         ctrl[2] = 0;
     }
     // exclusive prefix of tile counts over documents
-    const bool lds_pref = ndocs < kPrefixLds;
     {
         const int chunk = (ndocs + kPlanThreads - 1) / kPlanThreads;
         const int lo = tid * chunk, hi = min(lo + chunk, ndocs);
@@ -178,7 +198,21 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
     // must have reached L2) is complete for every thread
     if (!lds_pref) __threadfence();
     __syncthreads();
+    // document-major: each document's first slot, after the documents with
+    // more tiles
+    if (lds_pref) {
+        int* curd = curk;
+        for (int d = tid; d < ndocs; d += kPlanThreads) {
+            const int n = lpref[d + 1] - lpref[d];
+            const int c = min(n, max_cost);
+            if (n > 0) ldbase[d] = (c + 1 < C1 ? above[c + 1] : 0) + atomicAdd(&curd[c], n);
+        }
+        __syncthreads();
+        for (int c = tid; c < C1; c += kPlanThreads) curk[c] = 0;
+        __syncthreads();
+    }
     // tile p, the t-th of the n tiles of document doc, whose first tile is pre
+    const bool kdoc = lds_pref && key_docmajor;
     auto place = [&](int p, int doc, int pre, int next) {
         const int t = p - pre;
         const int n = next - pre;
@@ -186,12 +220,14 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
         const int4 tile = make_int4(ds + kTile * t, ds, de, doc);
         {
             const int cost = t + 1;
-            const int slot = (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&curq[cost], 1);
+            const int slot = lds_pref ? ldbase[doc] + (n - cost)
+                                      : (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&curq[cost], 1);
             if (slot < max_tiles) tiles_q[slot] = tile;
         }
         if (tiles_k) {
             const int cost = n - t;
-            const int slot = (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&curk[cost], 1);
+            const int slot = kdoc ? ldbase[doc] + (n - cost)
+                                  : (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&curk[cost], 1);
             if (slot < max_tiles) tiles_k[slot] = tile;
         }
     };
@@ -216,8 +252,8 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
     const size_t smem = sizeof(int) * 3 * ((size_t)a.max_cost + 1);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), smem, st, a.cu, a.ndocs, a.ttot, a.cu_status,
-                       a.max_cost,
-                       a.tiles_prefix, a.ctrl, a.max_tiles, a.tiles_q, a.tiles_k, a.dboff, a.ds_blocks);
+                       a.max_cost, a.tiles_prefix, a.ctrl, a.max_tiles, a.tiles_q, a.tiles_k, a.key_docmajor,
+                       a.dboff, a.ds_blocks);
     return hipGetLastError();
 }
 
