@@ -70,20 +70,65 @@ __device__ V block_incl_scan(V v, V* wsum, V& total) {
     return v + before;
 }
 
-// In-place inclusive scan of buf[0..n) in LDS; reverse = true scans from the
-// end (suffix sums).  Each thread owns one contiguous chunk.
-__device__ void block_scan(int* buf, int n, bool reverse, int* wsum) {
+// block_incl_scan of two values at once (the same two barriers).
+template <typename A, typename B>
+__device__ void block_incl_scan2(A& va, B& vb, A* wa, B* wb, A& ta, B& tb) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const A x = __shfl_up(va, off);
+        const B y = __shfl_up(vb, off);
+        if (lane >= off) {
+            va += x;
+            vb += y;
+        }
+    }
+    if (lane == 63) {
+        wa[w] = va;
+        wb[w] = vb;
+    }
+    __syncthreads();
+    A ba = 0, sa = 0;
+    B bb = 0, sb = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanWaves; ++i) {
+        const A x = wa[i];
+        const B y = wb[i];
+        if (i < w) {
+            ba += x;
+            bb += y;
+        }
+        sa += x;
+        sb += y;
+    }
+    __syncthreads();
+    ta = sa;
+    tb = sb;
+    va += ba;
+    vb += bb;
+}
+
+// In-place inclusive suffix scans of a[0..n) and b[0..n) in LDS (sums from the
+// end).  Each thread owns one contiguous chunk.
+__device__ void block_suffix_scan2(int* a, int* b, int n, int* wa, int* wb) {
     const int tid = threadIdx.x;
     const int chunk = (n + kPlanThreads - 1) / kPlanThreads;
     const int lo = tid * chunk, hi = min(lo + chunk, n);
-    int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += buf[reverse ? n - 1 - i : i];
-    int total;
-    int run = block_incl_scan(sum, wsum, total) - sum;
+    int sa = 0, sb = 0;
     for (int i = lo; i < hi; ++i) {
-        const int j = reverse ? n - 1 - i : i;
-        run += buf[j];
-        buf[j] = run;
+        sa += a[n - 1 - i];
+        sb += b[n - 1 - i];
+    }
+    int ta, tb;
+    int ra = sa, rb = sb;
+    block_incl_scan2(ra, rb, wa, wb, ta, tb);
+    ra -= sa;
+    rb -= sb;
+    for (int i = lo; i < hi; ++i) {
+        ra += a[n - 1 - i];
+        rb += b[n - 1 - i];
+        a[n - 1 - i] = ra;
+        b[n - 1 - i] = rb;
     }
     __syncthreads();
 }
@@ -102,24 +147,31 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
     int* curq = smem + C1;
     int* curk = smem + 2 * C1;
     __shared__ int wsum[kPlanWaves];
+    __shared__ int wsum2[kPlanWaves];
     __shared__ long lwsum[kPlanWaves];
     __shared__ int lpref[kPrefixLds];          // tile prefix of the documents (ndocs < kPrefixLds)
     __shared__ int ldbase[kPrefixLds];         // first slot of each document, document-major
+    __shared__ int lcu[kPrefixLds + 1];        // cu_seqlens (ndocs < kPrefixLds)
     __shared__ int bad_all;
     const int tid = threadIdx.x;
+    const bool lds_pref = ndocs < kPrefixLds;
+    // cu_seqlens is read from global memory once when it fits in LDS
+    if (lds_pref)
+        for (int d = tid; d <= ndocs; d += kPlanThreads) lcu[d] = cu[d];
+    if (tid == 0) bad_all = 0;
+    __syncthreads();
+    const int32_t* cux = lds_pref ? lcu : cu;
     // ---- the packed layout's preconditions (Section 3.6.1)
     int bad = 0;
     for (int d = tid; d < ndocs; d += kPlanThreads) {
-        const int a0 = cu[d], a1 = cu[d + 1];
+        const int a0 = cux[d], a1 = cux[d + 1];
         if (a1 < a0) bad |= 2;
         if (a0 < 0 || a1 > ttot) bad |= 4;
     }
     if (tid == 0) {
-        if (cu[0] != 0) bad |= 1;
-        if (cu[ndocs] != ttot) bad |= 4;
-        bad_all = 0;
+        if (cux[0] != 0) bad |= 1;
+        if (cux[ndocs] != ttot) bad |= 4;
     }
-    __syncthreads();
     if (bad) atomicOr(&bad_all, bad);
     __syncthreads();
     if (tid == 0 && cu_status) *cu_status = bad_all;
@@ -130,69 +182,73 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
     for (int c = tid; c < C1; c += kPlanThreads) hist[c] = curq[c] = curk[c] = 0;
     __syncthreads();
     for (int d = tid; d < ndocs; d += kPlanThreads) {
-        const int L = cu[d + 1] - cu[d];
+        const int L = cux[d + 1] - cux[d];
         const int n = min((L + kTile - 1) / kTile, max_cost);
         if (n > 0) atomicAdd(&hist[n], 1);
     }
     __syncthreads();
-    const bool lds_pref = ndocs < kPrefixLds;
+    // With cnt[c] = #docs with n == c, one pass of suffix sums gives
+    //   A[c] = #docs with n >= c = number of tiles of cost c (c >= 1), and
+    //   above[c] = sum over n >= c of n cnt[n] = tiles of the documents with
+    //   at least c tiles (document-major slots);
+    // the number of tiles of cost >= c (cost-major slots: the class of cost c
+    // starts at hist[c + 1]) is then sum over n >= c of cnt[n] (n - c + 1) =
+    // above[c] - (c - 1) A[c], and hist[1] is the total.
     int* above = curq;
-    if (lds_pref) {
-        // above[c] = c x (#docs with n == c), summed from the end: the tiles
-        // of the documents with at least c tiles
-        for (int c = tid; c < C1; c += kPlanThreads) above[c] = c * hist[c];
-        __syncthreads();
-        block_scan(above, C1, true, wsum);
-    }
-    // hist[c] = #docs with n >= c = number of tiles of cost c (c >= 1)
-    block_scan(hist, C1, true, wsum);
-    // hist[c] = number of tiles of cost >= c; the class of cost c starts at
-    // hist[c + 1] (classes by decreasing cost) and hist[1] is the total
-    block_scan(hist, C1, true, wsum);
+    for (int c = tid; c < C1; c += kPlanThreads) above[c] = c * hist[c];
+    __syncthreads();
+    block_suffix_scan2(hist, above, C1, wsum, wsum2);
+    for (int c = tid; c < C1; c += kPlanThreads) hist[c] = above[c] - (c - 1) * hist[c];
+    // the cost-major query list places with the cursors curq (document-major
+    // keeps `above`)
+    if (!lds_pref)
+        for (int c = tid; c < C1; c += kPlanThreads) curq[c] = 0;
+    __syncthreads();
     const int total = C1 > 1 ? (int)min((long)hist[1], max_tiles) : 0;
     if (tid == 0) {
         ctrl[0] = total;
         ctrl[2] = 0;
     }
-    // exclusive prefix of tile counts over documents
+    // exclusive prefix of tile counts over documents and, with a dS store,
+    // of their causal 32x32 blocks (nb (nb + 1) / 2 for nb = ceil(L / 32):
+    // each document's first block), in one scan
     {
         const int chunk = (ndocs + kPlanThreads - 1) / kPlanThreads;
         const int lo = tid * chunk, hi = min(lo + chunk, ndocs);
+        auto tiles_of = [&](int d) { return (cux[d + 1] - cux[d] + kTile - 1) / kTile; };
+        auto blocks_of = [&](int d) -> long {
+            const long nb = (cux[d + 1] - cux[d] + kBlock - 1) / kBlock;
+            return nb * (nb + 1) / 2;
+        };
         int sum = 0;
-        for (int d = lo; d < hi; ++d) sum += (cu[d + 1] - cu[d] + kTile - 1) / kTile;
+        long bsum = 0;
+        for (int d = lo; d < hi; ++d) {
+            sum += tiles_of(d);
+            if (dboff) bsum += blocks_of(d);
+        }
         int all;
-        int run = block_incl_scan(sum, wsum, all) - sum;
+        long total_blocks;
+        int run = sum;
+        long brun = bsum;
+        block_incl_scan2(run, brun, wsum, lwsum, all, total_blocks);
+        run -= sum;
+        brun -= bsum;
+        const bool fits = dboff && ds_blocks > 0 && total_blocks <= ds_blocks;
         for (int d = lo; d < hi; ++d) {
             tiles_prefix[d] = run;
             if (lds_pref) lpref[d] = run;
-            run += (cu[d + 1] - cu[d] + kTile - 1) / kTile;
+            run += tiles_of(d);
+            if (dboff) {
+                dboff[d] = fits ? (int32_t)brun : 0;
+                brun += blocks_of(d);
+            }
         }
         if (tid == 0) {
             tiles_prefix[ndocs] = all;
             if (lds_pref) lpref[ndocs] = all;
+            // 1 if the backward's dS store holds this call's blocks
+            ctrl[1] = fits ? 1 : 0;
         }
-    }
-    // dS store: first causal 32x32 block of each document (nb (nb + 1) / 2
-    // blocks for nb = ceil(L / 32)), and whether the call fits the capacity
-    if (dboff) {
-        const int chunk = (ndocs + kPlanThreads - 1) / kPlanThreads;
-        const int lo = tid * chunk, hi = min(lo + chunk, ndocs);
-        long sum = 0;
-        for (int d = lo; d < hi; ++d) {
-            const long nb = (cu[d + 1] - cu[d] + kBlock - 1) / kBlock;
-            sum += nb * (nb + 1) / 2;
-        }
-        long total_blocks;
-        long run = block_incl_scan(sum, lwsum, total_blocks) - sum;
-        const bool fits = ds_blocks > 0 && total_blocks <= ds_blocks;
-        for (int d = lo; d < hi; ++d) {
-            dboff[d] = fits ? (int32_t)run : 0;
-            const long nb = (cu[d + 1] - cu[d] + kBlock - 1) / kBlock;
-            run += nb * (nb + 1) / 2;
-        }
-        if (tid == 0) ctrl[1] = fits ? 1 : 0;
-    } else if (tid == 0) {
-        ctrl[1] = 0;
     }
     // the prefix table (LDS, or global beyond kPrefixLds documents, which then
     // must have reached L2) is complete for every thread
@@ -216,7 +272,7 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
     auto place = [&](int p, int doc, int pre, int next) {
         const int t = p - pre;
         const int n = next - pre;
-        const int ds = cu[doc], de = cu[doc + 1];
+        const int ds = cux[doc], de = cux[doc + 1];
         const int4 tile = make_int4(ds + kTile * t, ds, de, doc);
         {
             const int cost = t + 1;
