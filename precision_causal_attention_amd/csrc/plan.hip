@@ -1,5 +1,5 @@
-// GPU-built, cost-sorted tile lists (FLAMIA paper, Section 3.6.2 and
-// Appendix B.6): built on the device in one single-workgroup launch, no
+// GPU-built tile lists, expensive items first (FLAMIA paper, Section 3.6.2
+// and Appendix B.6): built on the device in one single-workgroup launch, no
 // host synchronization.
 //
 // A document of L tokens has n = ceil(L/128) tiles of 128 tokens, anchored at
@@ -32,9 +32,10 @@
 // ctrl layout (int32): [0] number of tiles, [1] 1 if the backward's dS store
 // holds this call's blocks (capacity given and not exceeded), else 0, [2] the
 // work-queue counter of the persistent key-major pass at d = 128 (zeroed here,
-// by every call, before that pass runs).  The
-// placement cursors of the cost classes live in LDS.  The dS block offsets of
-// the documents go to dboff.
+// by every call, before that pass runs).  cu_seqlens (up to kPrefixLds
+// documents), the tile prefix of the documents, their document-major slots
+// and the placement cursors live in LDS.  The dS block offsets of the
+// documents go to dboff.
 #include "device.h"
 #include "kernels.h"
 
@@ -44,33 +45,10 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPrefixLds = 4096;          // documents whose tile prefix is kept in LDS
 
-// Inclusive scan of one value per thread over the block: a shuffle scan in
-// each wave, then the wave totals (integer sums: the result does not depend
-// on the order).  Returns this thread's inclusive prefix; `total` gets the
-// block's sum.  Two barriers; wsum is free again on return.
-template <typename V>
-__device__ V block_incl_scan(V v, V* wsum, V& total) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const V t = __shfl_up(v, off);
-        if (lane >= off) v += t;
-    }
-    if (lane == 63) wsum[w] = v;
-    __syncthreads();
-    V before = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < kPlanWaves; ++i) {
-        const V x = wsum[i];
-        if (i < w) before += x;
-        tot += x;
-    }
-    __syncthreads();
-    total = tot;
-    return v + before;
-}
-
-// block_incl_scan of two values at once (the same two barriers).
+// Inclusive scans of two values per thread over the block at once: a shuffle
+// scan in each wave, then the wave totals (integer sums: the result does not
+// depend on the order).  va, vb become this thread's inclusive prefixes, ta,
+// tb the block's sums.  Two barriers; wa and wb are free again on return.
 template <typename A, typename B>
 __device__ void block_incl_scan2(A& va, B& vb, A* wa, B* wb, A& ta, B& tb) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
