@@ -10,7 +10,7 @@ so the parity tests cannot see it; these tests check it directly:
   - the key-major list (dK/dV: tile t meets n - t query tiles) is document-
     major at d = 128 and cost-major (all tiles by non-increasing cost) at
     d = 64;
-  - beyond 4095 documents both lists are cost-major.
+  - from 4096 documents on (no LDS prefix table) both lists are cost-major.
 The workspace offsets follow the layout of the host layer (control block,
 tile prefix, query-major list, key-major list, each 256-byte aligned).
 """
@@ -122,14 +122,21 @@ def test_lists_document_major(d):
         _check_cost_major(tk.tolist(), kcost)
 
 
-def test_lists_cost_major_beyond_lds_prefix():
-    """4500 documents: the work-list kernel keeps no prefix table in LDS and
-    orders both lists by cost alone."""
+@pytest.mark.parametrize("ndocs", [4095, 4096, 4500])
+def test_lists_at_the_lds_prefix_limit(ndocs):
+    """Up to 4095 documents the work-list kernel keeps cu_seqlens and the
+    tile prefix in LDS and builds the document-major lists; from 4096 on it
+    works from global memory and orders both lists by cost alone."""
     rng = np.random.default_rng(12)
-    lens = [int(x) for x in rng.integers(1, 300, size=4500)]
+    lens = [int(x) for x in rng.integers(1, 300, size=ndocs)]
     say(f"[work lists] docs={len(lens)} T={sum(lens)}")
     cu, n_f, q_f, n, tq, tk = _run(lens, 2, 1, 64, 4)
     want = _expected(cu)
-    assert n == len(want) and set(map(tuple, tq.tolist())) == want and set(map(tuple, tk.tolist())) == want
-    _check_cost_major(tq.tolist(), qcost)
+    assert n_f == n == len(want)
+    assert set(q_f) == want and set(map(tuple, tq.tolist())) == want and set(map(tuple, tk.tolist())) == want
+    if ndocs < 4096:
+        _check_document_major(tq.tolist(), qcost)
+        _check_document_major(q_f, qcost)
+    else:
+        _check_cost_major(tq.tolist(), qcost)
     _check_cost_major(tk.tolist(), kcost)
