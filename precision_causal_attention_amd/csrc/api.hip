@@ -391,6 +391,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     ba.lse2 = lse2; ba.dvec = dvec;
     ba.dk = dk; ba.dv = dv;
     ba.tiles = tiles_k; ba.ntiles = ctrl; ba.queue = ctrl + 2;
+    ba.zero = (const uint8_t*)(ctrl + 32);
     ba.ttot = dims->ttot; ba.hq = dims->hq; ba.hkv = dims->hkv;
     ba.scale = scale;
     ba.c1 = scale * 1.4426950408889634f;

@@ -59,15 +59,36 @@ struct BwdStep {
 };
 
 
-// A ring of step buffers, so that a step fills its buffer without waiting:
-// step i writes buffer i % N, last read by the products of step i - N and,
-// with the software pipeline (d = 64, MXFP8, N = 3), by the dV/dK products
-// of that step issued in step i - N + 1; every wave is past both before it
-// reaches the barrier of step i - 1.
-template <int D, int MIX, int N, int EXACT = 0>
-struct BwdSmem {
-    static constexpr int kStride = BwdStep<D, MIX, EXACT>::kStride;
-    BwdStep<D, MIX, EXACT> buf[N];
+// Step buffer of the LDS DMA staging (MXFP8 pipeline without the dS store):
+// the loads write LDS directly, 16 bytes per lane in lane order, so the code
+// tiles have unpadded rows and bank conflicts are avoided by placing 16-byte
+// chunk c of row r at chunk c ^ ((r >> 2) & 3) instead; the scale bytes
+// arrive zero-extended to dwords.
+template <int D>
+struct BwdStepDma {
+    static constexpr int kStride = D;
+    static constexpr int kNStride = 0;
+    uint8_t q[kQStep * D];
+    uint8_t o[kQStep * D];                       // quantized dO
+    alignas(16) float lse[kQStep];
+    alignas(16) float dv[kQStep];                // -D
+    uint32_t eq[kQStep];
+    uint32_t eo[kQStep];
+};
+
+// A ring of step buffers, so that a step fills its buffer without waiting.
+// Register staging: step i is stored into buffer i % N at its start, after
+// the barrier of step i - 1; the buffer was last read by the products of
+// step i - N and, with the software pipeline (N = 3), by the dV/dK products
+// of that step issued in step i - N + 1, and every wave is past both before
+// it reaches that barrier.  LDS DMA staging (N = 6): steps go in pairs with
+// one barrier per pair, at its first step; pair j + 1 is fetched right after
+// the barrier of pair j (two steps ahead) into the buffers of pair j - 2,
+// last read by that pair's products and, pipelined, in the first step of
+// pair j - 1.
+template <class S, int N>
+struct StepRing {
+    S buf[N];
 };
 
 // PROBE = 1: the diagnostics instantiation (probed raw scores, dS-hat zero count).
@@ -80,13 +101,23 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
     static_assert(D == 64, "d = 128 runs in bwd_split.hip");
     static_assert(!EXACT || (!STORE && !MIX), "the exact options run without the store, on MXFP8");
     constexpr bool PIPE = !STORE && !MIX;
-    constexpr int NBUF = PIPE ? 3 : 2;
-    using Step = BwdStep<D, MIX, EXACT>;
+    // Steps staged by LDS DMA two steps ahead with one barrier per two steps
+    // (the MXFP8 pipeline; 2.5% faster than a barrier per step at the same
+    // depth); the other variants load a step into registers one step ahead
+    // and store it.
+    constexpr bool DMA = PIPE && !EXACT;
+    constexpr int NBUF = DMA ? 6 : PIPE ? 3 : 2;
+    using Step = std::conditional_t<DMA, BwdStepDma<D>, BwdStep<D, MIX, EXACT>>;
     constexpr int STR = Step::kStride;
     constexpr int NSTR = Step::kNStride;
     constexpr int NQ = kQStep * D / 16 / 256;     // 16-byte chunks per thread of a 64-row code tile
     constexpr int NQN = MIX ? 2 * NQ : 1;         // same for the bf16 NVFP4 rows
-    __shared__ BwdSmem<D, MIX, NBUF, EXACT> sm;
+    __shared__ StepRing<Step, NBUF> sm;
+    // byte offset of (row, col) in a staged code tile
+    auto toff = [](int row, int col) -> int {
+        if constexpr (DMA) return row * D + ((((col >> 4) ^ (row >> 2)) & 3) << 4) + (col & 15);
+        else return row * STR + col;
+    };
 
     const int ti = (int)blockIdx.x / a.hkv;
     if (ti >= *a.ntiles) return;
@@ -161,7 +192,7 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
             b.eq[tid] = (uint8_t)p_eq;
             b.eo[tid] = (uint8_t)p_eo;
             b.lse[tid] = p_in ? p_lse : INFINITY;   // +inf: row outside the document
-            b.dv[tid] = -p_dv;                       // -D: accumulator input of dP
+            b.dv[tid] = p_dv;                        // -D: accumulator input of dP
         }
         if constexpr (EXACT) {
             // thread tid holds query tid % 64: each half-wave one 32-query block
@@ -173,7 +204,29 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
             }
         }
     };
-    load_step(g * G, kt0);
+    // LDS DMA staging: wave w fetches rows 16w .. 16w + 15 of both code tiles
+    // (lane l: row 16w + l / 4 into physical chunk l % 4, which holds logical
+    // chunk (l % 4) ^ (l / 16)) and one per-query array: lse2 (wave 0), -D (1),
+    // Q's (2) and dO's (3) scale bytes.  Rows past the end of the document read zeros: a zero Q and dO row
+    // with lse2 = D = 0 has S = dP = dS = 0 and P = 1 against a zero dO row,
+    // so it adds nothing to dK or dV.
+    auto issue_step = [&](Step& b, int h, int q0) {
+        if constexpr (DMA) {
+            const int row = 16 * wave_u + (lane >> 2);
+            const int c = (lane & 3) ^ (lane >> 4);
+            const bool in = q0 + row < L;
+            const long off = ((long)(ds + q0 + row) * a.hq + h) * D + 16 * c;
+            dma16(in ? (const void*)(a.qc + off) : (const void*)a.zero, &b.q[kQStep * D / 4 * wave_u]);
+            dma16(in ? (const void*)(a.oc + off) : (const void*)a.zero, &b.o[kQStep * D / 4 * wave_u]);
+            const bool vin = q0 + lane < L;
+            const long vo = (long)h * a.ttot + ds + q0 + lane;
+            if (wave_u == 0) dma4(vin ? (const void*)(a.lse2 + vo) : (const void*)a.zero, b.lse);
+            else if (wave_u == 1) dma4(vin ? (const void*)(a.dvec + vo) : (const void*)a.zero, b.dv);
+            else if (wave_u == 2) dma1(vin ? (const void*)(a.qs + vo) : (const void*)a.zero, b.eq);
+            else dma1(vin ? (const void*)(a.os + vo) : (const void*)a.zero, b.eo);
+        }
+    };
+    if constexpr (!DMA) load_step(g * G, kt0);
 
     // The wave's key rows as B operands of S and dP (column = key, k = channel);
     // mixed path: channels 16 kc + 8 lg .. + 8 of the key's NVFP4 values for S
@@ -202,6 +255,25 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
     }
     const int ek = MIX ? 127 : a.ks[(long)g * a.ttot + key_row];
     const int ev = a.vs[(long)g * a.ttot + key_row];
+    // the first pair of steps (issued after the key rows, so that waiting
+    // for it waits for the key rows too and for nothing younger)
+    int lh = 0, lq0 = kt0;      // next step to fetch
+    bool lmore = true;
+    bool odd = false;           // the current step is the second of its pair
+    auto advance = [&](int& hx, int& qx) {
+        qx += kQStep;
+        if (qx >= L) { qx = kt0; ++hx; }
+    };
+    if constexpr (DMA) {
+        issue_step(sm.buf[0], g * G, kt0);
+        advance(lh, lq0);
+        lmore = lh < G;
+        if (lmore) {
+            issue_step(sm.buf[1], g * G + lh, lq0);
+            advance(lh, lq0);
+            lmore = lh < G;
+        }
+    }
 
     v16f dvt[DT], dkt[DT];
 #pragma unroll
@@ -220,20 +292,26 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
         const v8i db = v8i{dsc[0][0], dsc[0][1], dsc[0][2], dsc[0][3], dsc[1][0], dsc[1][1], dsc[1][2], dsc[1][3]};
         // A scales: dO's and Q's token blocks, or (exact options) dO's block
         // maximum and 1 (Q's exponents are inside dS-hat)
-        const int so = EXACT ? (int)b.eob[lg] : (int)b.eo[32 * lg];
-        const int sq = EXACT ? 127 : (int)b.eq[32 * lg];
+        int so, sq;
+        if constexpr (EXACT) {
+            so = b.eob[lg];
+            sq = 127;
+        } else {
+            so = b.eo[32 * lg];
+            sq = b.eq[32 * lg];
+        }
         const int sd = lg ? es[1] : es[0];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             v2i r[4];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                r[rr] = lds_read_tr8(&b.o[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                r[rr] = lds_read_tr8(&b.o[toff(16 * rr + tr_key, 32 * dt + tr_col)]);
             const v8i oa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
             dvt[dt] = mfma_mx(oa, pb, dvt[dt], so, 127 - 8);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                r[rr] = lds_read_tr8(&b.q[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                r[rr] = lds_read_tr8(&b.q[toff(16 * rr + tr_key, 32 * dt + tr_col)]);
             const v8i qa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
             dkt[dt] = mfma_mx(qa, db, dkt[dt], sq, sd);
         }
@@ -269,19 +347,37 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
     // whether another step follows.
     auto step = [&](auto mask_tag) -> bool {
         constexpr bool MASK = decltype(mask_tag)::value;
-        // ---- publish the prefetched step in LDS, start fetching the next one
         Step& B = sm.buf[cur];
-        store_step(B);
-        __syncthreads();
         const int h = g * G + hh;
         const int qs0 = q0;
-        q0 += kQStep;
-        if (q0 >= L) { q0 = kt0; ++hh; }
+        advance(hh, q0);
         const bool more = hh < G;
-        flush_store();
-        // unconditional (the last step re-fetches a valid step): a conditional
-        // update would keep the prefetch registers in scratch
-        load_step(g * G + min(hh, G - 1), q0);
+        if constexpr (DMA) {
+            // at the first step of a pair: wait for both of its steps' loads
+            // (the only ones outstanding), then fetch the next pair
+            if (!odd) {
+                vm_drain_barrier();
+#pragma unroll
+                for (int k = 2; k < 4; ++k) {
+                    if (lmore) {
+                        int b = cur + k;
+                        if (b >= NBUF) b -= NBUF;
+                        issue_step(sm.buf[b], g * G + lh, lq0);
+                        advance(lh, lq0);
+                        lmore = lh < G;
+                    }
+                }
+            }
+            odd = !odd;
+        } else {
+            // publish the prefetched step in LDS, start fetching the next one
+            store_step(B);
+            __syncthreads();
+            flush_store();
+            // unconditional (the last step re-fetches a valid step): a
+            // conditional update would keep the prefetch registers in scratch
+            load_step(g * G + min(hh, G - 1), q0);
+        }
 
         // In a step that meets the causal boundary, the 32-query block st is
         // block qb = (qs0 - kt0) / 32 + st of the key tile's diagonal: blocks
@@ -317,13 +413,13 @@ __global__ void __launch_bounds__(256, 2) bwd_kernel(const BwdArgs a) {
                         sacc[st] = mfma_bf16(qa, kn[n], sacc[st]);
                     }
                 } else {
-                    const uint4 lo = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 16 * lg]);
-                    const uint4 hi = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 32 + 16 * lg]);
+                    const uint4 lo = *reinterpret_cast<const uint4*>(&B.q[toff(row, 64 * kc + 16 * lg)]);
+                    const uint4 hi = *reinterpret_cast<const uint4*>(&B.q[toff(row, 64 * kc + 32 + 16 * lg)]);
                     const v8i qa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                     sacc[st] = mfma_mx(qa, kb[kc], sacc[st], B.eq[row], ek);
                 }
-                const uint4 lo = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 16 * lg]);
-                const uint4 hi = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 32 + 16 * lg]);
+                const uint4 lo = *reinterpret_cast<const uint4*>(&B.o[toff(row, 64 * kc + 16 * lg)]);
+                const uint4 hi = *reinterpret_cast<const uint4*>(&B.o[toff(row, 64 * kc + 32 + 16 * lg)]);
                 const v8i oa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 pacc[st] = mfma_mx(oa, vb[kc], pacc[st], B.eo[row], ev);
             }

@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
             b.eq[tid] = (uint8_t)p_eq;
             b.eo[tid] = (uint8_t)p_eo;
             b.lse[tid] = p_in ? p_lse : INFINITY;   // +inf: row outside the document
-            b.dv[tid] = -p_dv;                       // -D: accumulator input of dP
+            b.dv[tid] = p_dv;                        // -D: accumulator input of dP
         }
         if constexpr (EXACT) {
             // thread tid holds query tid % 64: each half-wave one 32-query block

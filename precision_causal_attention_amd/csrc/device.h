@@ -49,6 +49,49 @@ __device__ __forceinline__ v2i lds_read_tr8(const uint8_t* lds_addr) {
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(v2i, const_cast<uint8_t*>(lds_addr)));
 }
 
+// Direct global -> LDS loads (global_load_lds_*): lane l of the wave writes
+// its 16 / 4 bytes at lds_base + 16 l / 4 l; the one-byte form writes the
+// byte zero-extended to a dword at lds_base + 4 l (all measured on gfx950).
+// The LDS base must be wave-uniform (it goes through M0, which is saved and
+// restored around the load).  They count in vmcnt like any vector load and
+// bypass the registers.  They are issued from inline assembly on purpose:
+// the compiler would otherwise treat every later LDS read as dependent on
+// them and wait for all outstanding loads before it, which defeats fetching
+// ahead.  Since the compiler does not know of them, its own waits do not
+// cover them (__syncthreads does not wait for them either): the caller waits
+// with vm_drain_barrier before reading the LDS they wrote.  Waits that the
+// compiler inserts for its own loads can only wait longer than needed, never
+// too little (loads complete in issue order).
+__device__ __forceinline__ uint32_t lds_addr_of(void* p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) void*)p);
+}
+#define FLAMIA_DMA_ASM(OP)                                                                     \
+    "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t" OP " %1, off\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+    uint32_t save;
+    asm volatile(FLAMIA_DMA_ASM("global_load_lds_dwordx4") : "=&s"(save) : "v"(src), "s"(lds_addr_of(lds_base))
+                 : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
+    uint32_t save;
+    asm volatile(FLAMIA_DMA_ASM("global_load_lds_dword") : "=&s"(save) : "v"(src), "s"(lds_addr_of(lds_base))
+                 : "memory");
+}
+__device__ __forceinline__ void dma1(const void* src, void* lds_base) {
+    uint32_t save;
+    asm volatile(FLAMIA_DMA_ASM("global_load_lds_ubyte") : "=&s"(save) : "v"(src), "s"(lds_addr_of(lds_base))
+                 : "memory");
+}
+#undef FLAMIA_DMA_ASM
+// Waits for every outstanding vector memory operation of the wave (the
+// direct LDS loads above included), then joins the workgroup barrier.  No
+// LDS access moves across it (opaque memory clobbers on both sides).
+__device__ __forceinline__ void vm_drain_barrier() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Four fp32 -> four E4M3 bytes (byte i = element i), round to nearest even;
 // bit-identical to the format's definition for |x| <= 448.
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {

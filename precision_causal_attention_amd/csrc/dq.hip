@@ -195,12 +195,12 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
         const float dval = ldexpf(tot, e);
         if (q_valid && lg == 0) {
             a.os_w[(long)h * a.ttot + q_row] = (uint8_t)eo;
-            a.dvec_w[(long)h * a.ttot + q_row] = dval;
+            a.dvec_w[(long)h * a.ttot + q_row] = -dval;   // stored as -D
         }
         nD = -dval;
     } else {
         eo = a.os[(long)h * a.ttot + q_row];
-        nD = -a.dvec[(long)h * a.ttot + q_row];
+        nD = a.dvec[(long)h * a.ttot + q_row];
     }
     const float lse_raw = a.lse2[(long)h * a.ttot + q_row];
     const float lse = q_valid ? lse_raw : INFINITY;      // P = 0 on rows outside the document

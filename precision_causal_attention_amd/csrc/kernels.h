@@ -27,7 +27,8 @@ struct QuantArgs {
     QuantTensor t[3];
     int ntensors;
     int per_token;            // 1: one exponent per token instead of per 32-token block
-    // dO variant only (nullptr otherwise; then t[0] is dO): D = dO~ . O
+    // dO variant only (nullptr otherwise; then t[0] is dO): -D with D = dO~ . O
+    // (stored negated: the backward products start their dP accumulators from it)
     const uint16_t* o;
     float* dvec;
 };
@@ -106,7 +107,7 @@ struct FwdArgs {
 struct BwdArgs {
     const uint8_t *qc, *qs, *kc, *ks, *vc, *vs, *oc, *os;   // oc/os: quantized dO
     const float* lse2;
-    const float* dvec;
+    const float* dvec;        // -D per (head, token)
     uint16_t *dk, *dv;
     const int4* tiles;
     const int32_t* ntiles;    // ntiles[1] != 0: store dS-hat blocks
@@ -120,6 +121,7 @@ struct BwdArgs {
     const int32_t* dboff;
     long ds_blocks;
     int exact;                // 1: the exact options (dO's and Q's token exponents folded)
+    const uint8_t* zero;      // 64 zero bytes, 16-byte aligned (the rows past a document's end)
     ProbeArgs probe;
 };
 

@@ -32,7 +32,9 @@
 // ctrl layout (int32): [0] number of tiles, [1] 1 if the backward's dS store
 // holds this call's blocks (capacity given and not exceeded), else 0, [2] the
 // work-queue counter of the persistent key-major pass at d = 128 (zeroed here,
-// by every call, before that pass runs).  cu_seqlens (up to kPrefixLds
+// by every call, before that pass runs), [32 .. 47] 64 zero bytes that the
+// attention kernels' staged loads read for rows past a document's end
+// (written by every call).  cu_seqlens (up to kPrefixLds
 // documents), the tile prefix of the documents, their document-major slots
 // and the placement cursors live in LDS.  The dS block offsets of the
 // documents go to dboff.
@@ -133,6 +135,7 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
     __shared__ int bad_all;
     const int tid = threadIdx.x;
     const bool lds_pref = ndocs < kPrefixLds;
+    if (tid < 16) ctrl[32 + tid] = 0;
     // cu_seqlens is read from global memory once when it fits in LDS
     if (lds_pref)
         for (int d = tid; d <= ndocs; d += kPlanThreads) lcu[d] = cu[d];

@@ -279,7 +279,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const QuantArgs a) {
                     dot = fmaf(hi[1], bf16_to_f32(w[2 * k + 1] >> 16), dot);
                 }
                 dot = ldexpf(token_sum<CPT>(dot), er[r]);
-                if (tok < nt && ch == 0) a.dvec[(long)h * a.ttot + bs + tok] = dot;
+                if (tok < nt && ch == 0) a.dvec[(long)h * a.ttot + bs + tok] = -dot;   // stored as -D
             }
         }
     }
