@@ -59,7 +59,7 @@ __device__ __forceinline__ v2i lds_read_tr8(const uint8_t* lds_addr) {
 // them and wait for all outstanding loads before it, which defeats fetching
 // ahead.  Since the compiler does not know of them, its own waits do not
 // cover them (__syncthreads does not wait for them either): the caller waits
-// with vm_drain_barrier before reading the LDS they wrote.  Waits that the
+// with vm_wait_barrier before reading the LDS they wrote.  Waits that the
 // compiler inserts for its own loads can only wait longer than needed, never
 // too little (loads complete in issue order).
 __device__ __forceinline__ uint32_t lds_addr_of(void* p) {
@@ -83,14 +83,20 @@ __device__ __forceinline__ void dma1(const void* src, void* lds_base) {
                  : "memory");
 }
 #undef FLAMIA_DMA_ASM
-// Waits for every outstanding vector memory operation of the wave (the
-// direct LDS loads above included), then joins the workgroup barrier.  No
-// LDS access moves across it (opaque memory clobbers on both sides).
-__device__ __forceinline__ void vm_drain_barrier() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Waits until at most N vector memory operations of the wave are
+// outstanding (the direct LDS loads above included), then joins the
+// workgroup barrier.  Loads complete in issue order, so with N = the number
+// of loads issued after a given one this waits for that load whatever the
+// stores in between do.  No LDS access moves across it (opaque memory
+// clobbers on both sides).
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
+__device__ __forceinline__ void vm_drain_barrier() { vm_wait_barrier<0>(); }
 
 // Four fp32 -> four E4M3 bytes (byte i = element i), round to nearest even;
 // bit-identical to the format's definition for |x| <= 448.

@@ -56,7 +56,7 @@ struct DqSmem {
 // per SIMD left latencies exposed: 36% longer).
 // PROBE = 1: the diagnostics instantiation (writes the probed raw scores).
 template <int D, int MIX, bool FUSED, int EXACT, int PROBE = 0>
-__global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
+__global__ void __launch_bounds__(256, (D == 64 && !MIX && !PROBE) ? 3 : 2) dq_kernel(const DqArgs a) {
     constexpr int KC = D / 64;
     constexpr int NC = D / 16;                    // 16-channel steps of S on the mixed path
     constexpr int DT = D / 32;
@@ -65,7 +65,16 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
     constexpr int CHUNKS = kTile * D / 16;
     constexpr int NCH = MIX ? 2 * CHUNKS / 256 : 1;   // 16-byte chunks per thread of a bf16 K tile
     static_assert(!EXACT || (FUSED && !MIX), "the exact options run the fused MXFP8 pass");
-    __shared__ DqSmem<D, MIX, EXACT> sm;
+    // d = 64: two tile buffers.  Tile t is stored into buffer t % 2, last
+    // read by the products of tile t - 2, which every wave finished before
+    // the barrier of tile t - 1, so one barrier per tile suffices (1% faster
+    // than one buffer and two barriers).  The second buffer raises the
+    // registers the compiler plans for; the MXFP8 variants are held to three
+    // waves per SIMD (168 VGPRs, two spilled outside the tile loop).  d = 128
+    // keeps one buffer and a barrier before the store (two buffers spill
+    // there).
+    constexpr int NB = D == 64 ? 2 : 1;
+    __shared__ DqSmem<D, MIX, EXACT> smr[NB];
 
     if (a.ntiles[1] != 0) return;                    // the dS store is in use: dq_store.hip runs
     const int ti = (int)blockIdx.x / a.hq;
@@ -238,9 +247,11 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
 
     // One 128-key tile; DIAG marks the last (diagonal) tile, the only one that
     // needs the causal mask and the only one with nothing left to prefetch.
+    int cur = 0;                                     // buffer of the current tile
     auto tile = [&](const int t, auto diag_tag) {
         constexpr bool DIAG = decltype(diag_tag)::value;
-        __syncthreads();
+        auto& sm = smr[cur];
+        if constexpr (NB == 1) __syncthreads();   // every wave is past the previous tile
 #pragma unroll
         for (int r = 0; r < CHUNKS / 256; ++r) {
             const int c = tid + 256 * r;
@@ -378,6 +389,7 @@ __global__ void __launch_bounds__(256, 2) dq_kernel(const DqArgs a) {
                 dq_chunk(c, dsc[2 * c], dsc[2 * c + 1], es[2 * c], es[2 * c + 1]);
             }
         }
+        if constexpr (NB == 2) cur ^= 1;
     };
     for (int t = 0; t + 1 < ntiles; ++t) tile(t, std::false_type{});
     tile(ntiles - 1, std::true_type{});
