@@ -70,6 +70,41 @@ struct SplitSmem {
     };
 };
 
+// Step buffer of the direct-LDS staging (the MXFP8 variants): the loads
+// write LDS 16 bytes per lane in lane order, so rows are unpadded and
+// 16-byte chunk c of row r sits at chunk c ^ ((r ^ (r >> 1)) & 7) (no bank
+// conflicts for the row and transposed reads); scale bytes arrive
+// zero-extended to dwords.
+struct SplitStepDma {
+    static constexpr int kStride = kSD;
+    static constexpr int kNStride = 0;
+    alignas(16) uint8_t q[kSStep * kSD];
+    alignas(16) uint8_t o[kSStep * kSD];            // quantized dO
+    alignas(16) float lse[kSStep];
+    alignas(16) float dv[kSStep];                   // -D
+    uint32_t eq[kSStep];
+    uint32_t eo[kSStep];
+};
+
+// Ring of three steps and two exchange buffers, one barrier per step (after
+// the exchange writes).  Step k is fetched right after the barrier of step
+// k - 2 into the buffer of step k - 3, whose last reads (its dV/dK products,
+// after the barrier of step k - 3) every wave finished before the barrier of
+// step k - 2; each wave waits for its own loads of step k before the barrier
+// of step k - 1, after which step k's products start.  Step i writes its
+// codes into exchange buffer i % 2, read by the partner after the barrier of
+// step i; the next write to it (step i + 2) comes after the barrier of step
+// i + 1.
+struct SplitSmemDma {
+    union {
+        struct {
+            SplitStepDma buf[3];
+            SplitXchg x[2];
+        } loop;
+        float rot[4][2][16][64];
+    };
+};
+
 }  // namespace
 
 // PROBE = 1: the diagnostics instantiation (probed raw scores, dS-hat zero count).
@@ -79,13 +114,22 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     constexpr int KC = D / 64;
     constexpr int NC = D / 16;
     constexpr int DTH = 2;                        // 32-channel tiles of dK / dV per wave
-    using Step = SplitStep<MIX, EXACT>;
+    using Step = std::conditional_t<!MIX && !EXACT, SplitStepDma, SplitStep<MIX, EXACT>>;
     constexpr int STR = Step::kStride;
     constexpr int NSTR = Step::kNStride;
     static_assert(!EXACT || (!STORE && !MIX), "the exact options run without the store, on MXFP8");
     constexpr int NQ = kSStep * D / 16 / 512;     // 16-byte chunks per thread of a 64-row code tile
     constexpr int NQN = MIX ? 2 * NQ : 1;
-    __shared__ SplitSmem<MIX, EXACT> sm;
+    // Steps staged by direct LDS loads one step ahead with one barrier per
+    // step (MXFP8); the mixed path and the exact options load a step into
+    // registers and store it behind a second barrier.
+    constexpr bool DMA = !MIX && !EXACT;
+    __shared__ std::conditional_t<DMA, SplitSmemDma, SplitSmem<MIX, EXACT>> sm;
+    // byte offset of (row, col) in a staged code tile
+    auto toff = [](int row, int col) -> int {
+        if constexpr (DMA) return row * D + ((((col >> 4) ^ row ^ (row >> 1)) & 7) << 4) + (col & 15);
+        else return row * STR + col;
+    };
 
     // Persistent workgroups: one per CU (an eight-wave workgroup fills a CU's
     // registers).  Workgroup b takes item b of the cost-ordered list first,
@@ -188,7 +232,30 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
             }
         }
     };
-    load_step(g * G, kt0);
+    // Direct staging: wave w fetches rows 8w .. 8w + 7 of both code tiles
+    // (lane l: row 8w + l / 8 into physical chunk l % 8) and waves 0 .. 3 one
+    // per-query array each: lse2, -D, Q's and dO's scale bytes.  Rows past
+    // the end of the document read zeros: a zero Q and dO row with lse2 =
+    // D = 0 has S = dP = dS = 0 and P = 1 against a zero dO row, so it adds
+    // nothing to dK or dV.
+    auto issue_step = [&](auto& b, int h, int q0) {
+        const int row = 8 * wave_u + (lane >> 3);
+        const int c = (lane & 7) ^ ((row ^ (row >> 1)) & 7);
+        const bool in = q0 + row < L;
+        const long off = ((long)(ds + q0 + row) * a.hq + h) * D + 16 * c;
+        dma16(in ? (const void*)(a.qc + off) : (const void*)a.zero, &b.q[8 * D * wave_u]);
+        dma16(in ? (const void*)(a.oc + off) : (const void*)a.zero, &b.o[8 * D * wave_u]);
+        if (wave_u < 4) {
+            const bool vin = q0 + lane < L;
+            const long vo = (long)h * a.ttot + ds + q0 + lane;
+            if (wave_u == 0) dma4(vin ? (const void*)(a.lse2 + vo) : (const void*)a.zero, b.lse);
+            else if (wave_u == 1) dma4(vin ? (const void*)(a.dvec + vo) : (const void*)a.zero, b.dv);
+            else if (wave_u == 2) dma1(vin ? (const void*)(a.qs + vo) : (const void*)a.zero, b.eq);
+            else dma1(vin ? (const void*)(a.os + vo) : (const void*)a.zero, b.eo);
+        }
+    };
+    if constexpr (DMA) issue_step(sm.loop.buf[0], g * G, kt0);
+    else load_step(g * G, kt0);
 
     // The pair's key rows as B operands of S and dP (column = key, k = channel)
     v8i kb[MIX ? 1 : KC], vb[KC];
@@ -227,7 +294,31 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     const float inv256 = 1.f / 256.f;
 
     int cur = 0;
+    int xi = 0;                   // exchange buffer of the current step (direct staging)
     int hh = 0, q0 = kt0;
+    int lh = 0, lq0 = kt0;        // next step to fetch (direct staging)
+    bool lmore = true;
+    auto advance = [&](int& hx, int& qx) {
+        qx += kSStep;
+        if (qx >= L) { qx = kt0; ++hx; }
+    };
+    if constexpr (DMA) {
+        // the key rows and scales are consumed here, before the next loads:
+        // the compiler's own wait for them, at a later first use, would wait
+        // for every load issued before that use
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) asm volatile("" ::"v"(kb[kc]), "v"(vb[kc]));
+        asm volatile("" ::"v"(ek), "v"(ev));
+        // the first step's loads, then the second step's
+        vm_drain_barrier();
+        advance(lh, lq0);
+        lmore = lh < G;
+        if (lmore) {
+            issue_step(sm.loop.buf[1], g * G + lh, lq0);
+            advance(lh, lq0);
+            lmore = lh < G;
+        }
+    }
     // this wave's dS block of the previous step, stored at the start of the next one
     u32x4 pend_w = u32x4{0, 0, 0, 0};
     long pend_blk = 0;
@@ -244,16 +335,17 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
     auto step = [&](auto mask_tag) -> bool {
         constexpr bool MASK = decltype(mask_tag)::value;
         Step& B = sm.loop.buf[cur];
-        store_step(B);
-        __syncthreads();
+        if constexpr (!DMA) {
+            store_step(B);
+            __syncthreads();
+        }
         const int h = g * G + hh;
         const int qs0 = q0;
-        q0 += kSStep;
-        if (q0 >= L) { q0 = kt0; ++hh; }
+        advance(hh, q0);
         const bool more = hh < G;
         if (PERSIST && !more && threadIdx.x == 0) claim = (int)gridDim.x + atomicAdd(a.queue, 1);
         flush_store();
-        load_step(g * G + min(hh, G - 1), q0);
+        if constexpr (!DMA) load_step(g * G + min(hh, G - 1), q0);
 
         // the step's 32-query blocks are blocks qb0 and qb0 + 1 of the key
         // tile's diagonal: a block before the pair's keys is skipped (P = 0),
@@ -284,13 +376,13 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
                         sacc = mfma_bf16(qa, kn[n], sacc);
                     }
                 } else {
-                    const uint4 lo = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 16 * lg]);
-                    const uint4 hi = *reinterpret_cast<const uint4*>(&B.q[row * STR + 64 * kc + 32 + 16 * lg]);
+                    const uint4 lo = *reinterpret_cast<const uint4*>(&B.q[toff(row, 64 * kc + 16 * lg)]);
+                    const uint4 hi = *reinterpret_cast<const uint4*>(&B.q[toff(row, 64 * kc + 32 + 16 * lg)]);
                     const v8i qa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                     sacc = mfma_mx(qa, kb[kc], sacc, B.eq[row], ek);
                 }
-                const uint4 lo = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 16 * lg]);
-                const uint4 hi = *reinterpret_cast<const uint4*>(&B.o[row * STR + 64 * kc + 32 + 16 * lg]);
+                const uint4 lo = *reinterpret_cast<const uint4*>(&B.o[toff(row, 64 * kc + 16 * lg)]);
+                const uint4 hi = *reinterpret_cast<const uint4*>(&B.o[toff(row, 64 * kc + 32 + 16 * lg)]);
                 const v8i oa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 pacc = mfma_mx(oa, vb[kc], pacc, B.eo[row], ev);
             }
@@ -359,14 +451,29 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
         }
         // ---- exchange with the partner wave, then dV^T += dO^T P-hat_b and
         // dK^T += Q^T dS-hat for the wave's channel half over the 64 queries
-        sm.loop.x.pb[wave_u][lane] = u32x4{(uint32_t)pbc[0], (uint32_t)pbc[1], (uint32_t)pbc[2], (uint32_t)pbc[3]};
-        sm.loop.x.db[wave_u][lane] = u32x4{(uint32_t)dsc[0], (uint32_t)dsc[1], (uint32_t)dsc[2], (uint32_t)dsc[3]};
-        if (lane == 0) sm.loop.x.es[wave_u] = es;
-        __syncthreads();
+        SplitXchg& X = [&]() -> SplitXchg& {
+            if constexpr (DMA) return sm.loop.x[xi];
+            else return sm.loop.x;
+        }();
+        X.pb[wave_u][lane] = u32x4{(uint32_t)pbc[0], (uint32_t)pbc[1], (uint32_t)pbc[2], (uint32_t)pbc[3]};
+        X.db[wave_u][lane] = u32x4{(uint32_t)dsc[0], (uint32_t)dsc[1], (uint32_t)dsc[2], (uint32_t)dsc[3]};
+        if (lane == 0) X.es[wave_u] = es;
+        if constexpr (DMA) {
+            // the exchange, and this wave's loads of the next step; then fetch
+            // the step after it
+            vm_drain_barrier();
+            if (lmore) {
+                issue_step(sm.loop.buf[cur == 0 ? 2 : cur - 1], g * G + lh, lq0);
+                advance(lh, lq0);
+                lmore = lh < G;
+            }
+        } else {
+            __syncthreads();
+        }
         if (!skip1) {
             const int pw = wave_u ^ 4;
-            const u32x4 ppb = sm.loop.x.pb[pw][lane], pdb = sm.loop.x.db[pw][lane];
-            const int pes = sm.loop.x.es[pw];
+            const u32x4 ppb = X.pb[pw][lane], pdb = X.db[pw][lane];
+            const int pes = X.es[pw];
             // block 0 of the contraction is wave half 0's, block 1 wave half 1's
             const u32x4 b0 = hf ? ppb : u32x4{(uint32_t)pbc[0], (uint32_t)pbc[1], (uint32_t)pbc[2], (uint32_t)pbc[3]};
             const u32x4 b1 = hf ? u32x4{(uint32_t)pbc[0], (uint32_t)pbc[1], (uint32_t)pbc[2], (uint32_t)pbc[3]} : ppb;
@@ -377,8 +484,14 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
             const int e0 = hf ? pes : es, e1 = hf ? es : pes;
             // A scales: dO's and Q's token blocks, or (exact options) dO's
             // block maximum and 1 (Q's exponents are inside dS-hat)
-            const int so = EXACT ? (int)B.eob[lg] : (int)B.eo[32 * lg];
-            const int sq = EXACT ? 127 : (int)B.eq[32 * lg];
+            int so, sq;
+            if constexpr (EXACT) {
+                so = B.eob[lg];
+                sq = 127;
+            } else {
+                so = B.eo[32 * lg];
+                sq = B.eq[32 * lg];
+            }
             const int sd = lg ? e1 : e0;
 #pragma unroll
             for (int t = 0; t < DTH; ++t) {
@@ -386,17 +499,22 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
                 v2i r[4];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr)
-                    r[rr] = lds_read_tr8(&B.o[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                    r[rr] = lds_read_tr8(&B.o[toff(16 * rr + tr_key, 32 * dt + tr_col)]);
                 const v8i oa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
                 dvt[t] = mfma_mx(oa, pb, dvt[t], so, 127 - 8);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr)
-                    r[rr] = lds_read_tr8(&B.q[(16 * rr + tr_key) * STR + 32 * dt + tr_col]);
+                    r[rr] = lds_read_tr8(&B.q[toff(16 * rr + tr_key, 32 * dt + tr_col)]);
                 const v8i qa = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
                 dkt[t] = mfma_mx(qa, db, dkt[t], sq, sd);
             }
         }
-        cur ^= 1;
+        if constexpr (DMA) {
+            cur = cur == 2 ? 0 : cur + 1;
+            xi ^= 1;
+        } else {
+            cur ^= 1;
+        }
         return more;
     };
     bool more = true;
