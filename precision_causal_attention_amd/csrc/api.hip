@@ -381,7 +381,7 @@ flamia_status_t flamia_bwd(const flamia_dims_t* dims, const flamia_opts_t* opts_
     uint8_t* ds_codes = base + w.ds_codes;
     uint8_t* ds_scales = base + w.ds_scales;
     PlanArgs pa{cu_seqlens, dims->ndocs, dims->ttot, opts.cu_status, w.max_cost, (int32_t*)(base + w.prefix),
-                ctrl, w.max_tiles, tiles_q, tiles_k, d == 128 ? 1 : 0, dboff, ds_blocks};
+                ctrl, w.max_tiles, tiles_q, tiles_k, 1, dboff, ds_blocks};
     const float scale = scale_of(opts, d);
     BwdArgs ba;
     ba.qc = q_mx.codes; ba.qs = q_mx.scales;

@@ -303,12 +303,14 @@ __global__ void __launch_bounds__(512, 1) bwd_split_kernel(const BwdArgs a) {
         if (qx >= L) { qx = kt0; ++hx; }
     };
     if constexpr (DMA) {
-        // the key rows and scales are consumed here, before the next loads:
-        // the compiler's own wait for them, at a later first use, would wait
-        // for every load issued before that use
+        // the key rows and scales are in registers before the next loads go out
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) asm volatile("" ::"v"(kb[kc]), "v"(vb[kc]));
-        asm volatile("" ::"v"(ek), "v"(ev));
+        for (int kc = 0; kc < KC; ++kc) {
+            keep_loaded(kb[kc]);
+            keep_loaded(vb[kc]);
+        }
+        keep_loaded(ek);
+        keep_loaded(ev);
         // the first step's loads, then the second step's
         vm_drain_barrier();
         advance(lh, lq0);

@@ -97,6 +97,19 @@ __device__ __forceinline__ void vm_wait_barrier() {
     asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ void vm_drain_barrier() { vm_wait_barrier<0>(); }
+// Makes the compiler have x in registers here, so that its wait for the load
+// of x is placed here and not at a later first use, where it would also wait
+// for the direct LDS loads issued in between (the compiler cannot tell them
+// apart).  Device pass only: the host pass has no VGPR constraint, and the
+// failed substitution would silently drop the kernel's host stub.
+template <class T>
+__device__ __forceinline__ void keep_loaded(const T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" ::"v"(x));
+#else
+    (void)x;
+#endif
+}
 
 // Four fp32 -> four E4M3 bytes (byte i = element i), round to nearest even;
 // bit-identical to the format's definition for |x| <= 448.

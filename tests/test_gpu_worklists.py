@@ -8,9 +8,10 @@ so the parity tests cannot see it; these tests check it directly:
     non-increasing tile count, each document's tiles contiguous and by
     decreasing cost (tile t of a document costs t + 1 key tiles);
   - the key-major list (dK/dV: tile t meets n - t query tiles) is document-
-    major at d = 128 and cost-major (all tiles by non-increasing cost) at
-    d = 64;
-  - from 4096 documents on (no LDS prefix table) both lists are cost-major.
+    major too (the key tiles of a document then run together and share its
+    query rows in L2);
+  - from 4096 documents on (no LDS prefix table) both lists are cost-major
+    (all tiles by non-increasing cost).
 The workspace offsets follow the layout of the host layer (control block,
 tile prefix, query-major list, key-major list, each 256-byte aligned).
 """
@@ -116,10 +117,7 @@ def test_lists_document_major(d):
     assert set(map(tuple, tk.tolist())) == want
     _check_document_major(q_f, qcost)
     _check_document_major(tq.tolist(), qcost)
-    if d == 128:
-        _check_document_major(tk.tolist(), kcost)
-    else:
-        _check_cost_major(tk.tolist(), kcost)
+    _check_document_major(tk.tolist(), kcost)
 
 
 @pytest.mark.parametrize("ndocs", [4095, 4096, 4500])
@@ -137,6 +135,7 @@ def test_lists_at_the_lds_prefix_limit(ndocs):
     if ndocs < 4096:
         _check_document_major(tq.tolist(), qcost)
         _check_document_major(q_f, qcost)
+        _check_document_major(tk.tolist(), kcost)
     else:
         _check_cost_major(tq.tolist(), qcost)
-    _check_cost_major(tk.tolist(), kcost)
+        _check_cost_major(tk.tolist(), kcost)
