@@ -15,9 +15,10 @@
 //   major) or Q/dO rows (key major) in that XCD's L2;
 //   cost-major: all tiles by decreasing cost, documents interleaved.
 // The query-major list is document-major; the key-major one is document-major
-// when the caller asks for it (the d = 128 pass: 2-5% faster; the d = 64 pass
-// ran 2% slower so), else cost-major.  Beyond kPrefixLds documents both lists
-// are cost-major.  Sorting is a counting sort on the small integer tile count
+// when the caller asks for it (the attention library does at both head
+// dimensions), else cost-major, and then ends with every document's last tile
+// (cost 1), which fills the tail as in the cost-major order.  Beyond
+// kPrefixLds documents both lists are cost-major.  Sorting is a counting sort on the small integer tile count
 // or cost instead of a comparison sort.  Within one class the order is
 // whatever the atomics give; it does not change any result.
 // Work item (tile, head) is decoded by the attention kernels from the
@@ -263,8 +264,24 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
         }
         if (tiles_k) {
             const int cost = n - t;
-            const int slot = kdoc ? ldbase[doc] + (n - cost)
-                                  : (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&curk[cost], 1);
+            int slot;
+            if (kdoc) {
+                // document-major over the tiles of cost >= 2, then every
+                // document's last tile (cost 1) at the end of the list, in
+                // document order: those few-step items fill in the tail.
+                // rank = documents before this one = those with more tiles
+                // (A[n + 1] = (above[n + 1] - hist[n + 1]) / n, from
+                // hist[c] = above[c] - (c - 1) A[c]) plus its place in its
+                // class (cursor offset / n).
+                const int c = min(n, max_cost);
+                const int ab = c + 1 < C1 ? above[c + 1] : 0;
+                const int more = c + 1 < C1 ? (ab - hist[c + 1]) / c : 0;
+                const int rank = more + (ldbase[doc] - ab) / n;
+                const int ndocs_ne = hist[1] - (C1 > 2 ? hist[2] : 0);   // documents with a tile
+                slot = cost >= 2 ? ldbase[doc] - rank + t : total - ndocs_ne + rank;
+            } else {
+                slot = (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&curk[cost], 1);
+            }
             if (slot < max_tiles) tiles_k[slot] = tile;
         }
     };

@@ -8,8 +8,9 @@ so the parity tests cannot see it; these tests check it directly:
     non-increasing tile count, each document's tiles contiguous and by
     decreasing cost (tile t of a document costs t + 1 key tiles);
   - the key-major list (dK/dV: tile t meets n - t query tiles) is document-
-    major too (the key tiles of a document then run together and share its
-    query rows in L2);
+    major too over the tiles of cost >= 2 (the key tiles of a document then
+    run together and share its query rows in L2), followed by every
+    document's last tile (cost 1) in the same document order;
   - from 4096 documents on (no LDS prefix table) both lists are cost-major
     (all tiles by non-increasing cost).
 The workspace offsets follow the layout of the host layer (control block,
@@ -76,6 +77,24 @@ def _check_document_major(lst, cost):
     assert all(a >= b for a, b in zip(counts, counts[1:])), counts[:20]
 
 
+def _check_key_list(lst):
+    """Document-major over the tiles of cost >= 2, then the cost-1 tiles in
+    the same document order."""
+    ones = [i for i, row in enumerate(lst) if kcost(row) == 1]
+    m = len(ones)
+    assert ones == list(range(len(lst) - m, len(lst))), "cost-1 tiles are not the tail"
+    head, tail = lst[:len(lst) - m], lst[len(lst) - m:]
+    _check_document_major(head, kcost)
+    for i, row in enumerate(head):
+        if i == 0 or row[3] != head[i - 1][3]:
+            assert kcost(row) == _ntiles(row), ("a document does not start with its costliest tile", row)
+    head_docs = [int(r[3]) for i, r in enumerate(head) if i == 0 or r[3] != head[i - 1][3]]
+    tail_docs = [int(r[3]) for r in tail]
+    assert tail_docs[:len(head_docs)] == head_docs, "tail order differs from the documents' order"
+    counts = [_ntiles(r) for r in tail]
+    assert all(a >= b for a, b in zip(counts, counts[1:])), counts[:20]
+
+
 def _check_cost_major(lst, cost):
     c = [cost(row) for row in lst]
     assert all(a >= b for a, b in zip(c, c[1:])), c[:40]
@@ -117,7 +136,7 @@ def test_lists_document_major(d):
     assert set(map(tuple, tk.tolist())) == want
     _check_document_major(q_f, qcost)
     _check_document_major(tq.tolist(), qcost)
-    _check_document_major(tk.tolist(), kcost)
+    _check_key_list(tk.tolist())
 
 
 @pytest.mark.parametrize("ndocs", [4095, 4096, 4500])
@@ -135,7 +154,7 @@ def test_lists_at_the_lds_prefix_limit(ndocs):
     if ndocs < 4096:
         _check_document_major(tq.tolist(), qcost)
         _check_document_major(q_f, qcost)
-        _check_document_major(tk.tolist(), kcost)
+        _check_key_list(tk.tolist())
     else:
         _check_cost_major(tq.tolist(), qcost)
         _check_cost_major(tk.tolist(), kcost)
