@@ -16,8 +16,9 @@
 //   cost-major: all tiles by decreasing cost, documents interleaved.
 // The query-major list is document-major; the key-major one is document-major
 // when the caller asks for it (the attention library does at both head
-// dimensions), else cost-major, and then ends with every document's last tile
-// (cost 1), which fills the tail as in the cost-major order.  Beyond
+// dimensions), else cost-major.  A document-major list ends with every
+// document's cost-1 tile (query-major: the first, key-major: the last), which
+// fill in the tail as in the cost-major order.  Beyond
 // kPrefixLds documents both lists are cost-major.  Sorting is a counting sort on the small integer tile count
 // or cost instead of a comparison sort.  Within one class the order is
 // whatever the atomics give; it does not change any result.
@@ -41,6 +42,16 @@
 // documents go to dboff.
 #include "device.h"
 #include "kernels.h"
+
+namespace {
+// Tiles of cost <= kTail* go to the end of the document-major lists, where
+// they fill in the tail (16 x 1024-token documents: forward 73.6 -> 68.3 us,
+// dQ pass 110.8 -> 104.4 us with 1 for the query-major list; 2 was no
+// better there and 0.4% slower on the 4 x 8192 GQA call; the key-major list
+// with 1: dK/dV 2-3% faster).
+constexpr int kTailQ = 1;
+constexpr int kTailK = 1;
+}  // namespace
 
 namespace flamia {
 
@@ -249,6 +260,27 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
         for (int c = tid; c < C1; c += kPlanThreads) curk[c] = 0;
         __syncthreads();
     }
+    // Document-major slot of the tile of cost `cost` (1..n) of document doc
+    // (n tiles) when the tiles of cost <= T go to the end of the list: the
+    // list is document-major over the tiles of cost > T, then the tiles of
+    // cost T, T - 1, ..., 1, each class in document order; those short
+    // items fill in the tail, as in the cost-major order.  A[j] (documents
+    // with at least j tiles) follows from hist[j] = above[j] - (j - 1) A[j];
+    // a document's rank (documents placed before it) is A[n + 1] plus its
+    // place in its class (cursor offset / n); the documents before it have
+    // at least n > T tiles, so its first main slot is ldbase - T rank.
+    auto docs_with = [&](int j) -> int {
+        if (j == 1) return hist[1] - (C1 > 2 ? hist[2] : 0);
+        return j < C1 ? (above[j] - hist[j]) / (j - 1) : 0;
+    };
+    auto dm_slot = [&](int doc, int n, int cost, int T) -> int {
+        const int c = min(n, max_cost);
+        const int rank = docs_with(c + 1) + (ldbase[doc] - (c + 1 < C1 ? above[c + 1] : 0)) / n;
+        if (cost > T) return ldbase[doc] - T * rank + (n - cost);
+        int start = total;
+        for (int j = 1; j <= cost; ++j) start -= docs_with(j);
+        return start + rank;
+    };
     // tile p, the t-th of the n tiles of document doc, whose first tile is pre
     const bool kdoc = lds_pref && key_docmajor;
     auto place = [&](int p, int doc, int pre, int next) {
@@ -258,30 +290,14 @@ plan_kernel(const int32_t* __restrict__ cu, int ndocs, int ttot, int32_t* __rest
         const int4 tile = make_int4(ds + kTile * t, ds, de, doc);
         {
             const int cost = t + 1;
-            const int slot = lds_pref ? ldbase[doc] + (n - cost)
+            const int slot = lds_pref ? dm_slot(doc, n, cost, kTailQ)
                                       : (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&curq[cost], 1);
             if (slot < max_tiles) tiles_q[slot] = tile;
         }
         if (tiles_k) {
             const int cost = n - t;
-            int slot;
-            if (kdoc) {
-                // document-major over the tiles of cost >= 2, then every
-                // document's last tile (cost 1) at the end of the list, in
-                // document order: those few-step items fill in the tail.
-                // rank = documents before this one = those with more tiles
-                // (A[n + 1] = (above[n + 1] - hist[n + 1]) / n, from
-                // hist[c] = above[c] - (c - 1) A[c]) plus its place in its
-                // class (cursor offset / n).
-                const int c = min(n, max_cost);
-                const int ab = c + 1 < C1 ? above[c + 1] : 0;
-                const int more = c + 1 < C1 ? (ab - hist[c + 1]) / c : 0;
-                const int rank = more + (ldbase[doc] - ab) / n;
-                const int ndocs_ne = hist[1] - (C1 > 2 ? hist[2] : 0);   // documents with a tile
-                slot = cost >= 2 ? ldbase[doc] - rank + t : total - ndocs_ne + rank;
-            } else {
-                slot = (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&curk[cost], 1);
-            }
+            const int slot = kdoc ? dm_slot(doc, n, cost, kTailK)
+                                  : (cost + 1 < C1 ? hist[cost + 1] : 0) + atomicAdd(&curk[cost], 1);
             if (slot < max_tiles) tiles_k[slot] = tile;
         }
     };

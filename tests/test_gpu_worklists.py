@@ -4,9 +4,11 @@ first), read back from the workspace after a call.
 The order of the items changes no output (every item writes its own rows),
 so the parity tests cannot see it; these tests check it directly:
   - every (document, 128-token tile) item appears exactly once in each list;
-  - the query-major list (forward, dQ) is document-major: documents by
-    non-increasing tile count, each document's tiles contiguous and by
-    decreasing cost (tile t of a document costs t + 1 key tiles);
+  - the query-major list (forward, dQ) is document-major over the tiles of
+    cost >= 2: documents by non-increasing tile count, each document's tiles
+    contiguous and by decreasing cost (tile t of a document costs t + 1 key
+    tiles), followed by every document's first tile (cost 1) in the same
+    document order;
   - the key-major list (dK/dV: tile t meets n - t query tiles) is document-
     major too over the tiles of cost >= 2 (the key tiles of a document then
     run together and share its query rows in L2), followed by every
@@ -77,22 +79,25 @@ def _check_document_major(lst, cost):
     assert all(a >= b for a, b in zip(counts, counts[1:])), counts[:20]
 
 
-def _check_key_list(lst):
-    """Document-major over the tiles of cost >= 2, then the cost-1 tiles in
-    the same document order."""
-    ones = [i for i, row in enumerate(lst) if kcost(row) == 1]
-    m = len(ones)
-    assert ones == list(range(len(lst) - m, len(lst))), "cost-1 tiles are not the tail"
+def _check_tail_list(lst, cost, T):
+    """Document-major over the tiles of cost > T, then the tiles of cost T,
+    T - 1, ..., 1, each class in the documents' order (by non-increasing
+    tile count)."""
+    m = sum(1 for row in lst if cost(row) <= T)
     head, tail = lst[:len(lst) - m], lst[len(lst) - m:]
-    _check_document_major(head, kcost)
+    assert all(cost(r) > T for r in head) and all(cost(r) <= T for r in tail), "cheap tiles are not the tail"
+    _check_document_major(head, cost)
     for i, row in enumerate(head):
         if i == 0 or row[3] != head[i - 1][3]:
-            assert kcost(row) == _ntiles(row), ("a document does not start with its costliest tile", row)
+            assert cost(row) == _ntiles(row), ("a document does not start with its costliest tile", row)
+    tc = [cost(r) for r in tail]
+    assert all(a >= b for a, b in zip(tc, tc[1:])), tc[:40]
     head_docs = [int(r[3]) for i, r in enumerate(head) if i == 0 or r[3] != head[i - 1][3]]
-    tail_docs = [int(r[3]) for r in tail]
-    assert tail_docs[:len(head_docs)] == head_docs, "tail order differs from the documents' order"
-    counts = [_ntiles(r) for r in tail]
-    assert all(a >= b for a, b in zip(counts, counts[1:])), counts[:20]
+    for k in range(1, T + 1):
+        docs = [int(r[3]) for r in tail if cost(r) == k]
+        counts = [_ntiles(r) for r in tail if cost(r) == k]
+        assert all(a >= b for a, b in zip(counts, counts[1:])), (k, counts[:20])
+        assert docs[:len(head_docs)] == head_docs, (k, "tail order differs from the documents' order")
 
 
 def _check_cost_major(lst, cost):
@@ -134,9 +139,9 @@ def test_lists_document_major(d):
     assert set(q_f) == want and len(q_f) == n
     assert set(map(tuple, tq.tolist())) == want
     assert set(map(tuple, tk.tolist())) == want
-    _check_document_major(q_f, qcost)
-    _check_document_major(tq.tolist(), qcost)
-    _check_key_list(tk.tolist())
+    _check_tail_list(q_f, qcost, 1)
+    _check_tail_list(tq.tolist(), qcost, 1)
+    _check_tail_list(tk.tolist(), kcost, 1)
 
 
 @pytest.mark.parametrize("ndocs", [4095, 4096, 4500])
@@ -152,9 +157,9 @@ def test_lists_at_the_lds_prefix_limit(ndocs):
     assert n_f == n == len(want)
     assert set(q_f) == want and set(map(tuple, tq.tolist())) == want and set(map(tuple, tk.tolist())) == want
     if ndocs < 4096:
-        _check_document_major(tq.tolist(), qcost)
-        _check_document_major(q_f, qcost)
-        _check_key_list(tk.tolist())
+        _check_tail_list(tq.tolist(), qcost, 1)
+        _check_tail_list(q_f, qcost, 1)
+        _check_tail_list(tk.tolist(), kcost, 1)
     else:
         _check_cost_major(tq.tolist(), qcost)
         _check_cost_major(tk.tolist(), kcost)
