@@ -11,8 +11,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libflamia.so")
-# the benchmark's matrix-core issue-rate probe (not part of the library's ABI)
-PROBE_SRC = os.path.join(PKG, "probe", "mfma_peak.hip")
+# the issue-rate probes of the matrix core (the benchmark's achievable peak)
+# and of the softmax's vector instructions (not part of the library's ABI)
+PROBE_SRCS = [os.path.join(PKG, "probe", "mfma_peak.hip"), os.path.join(PKG, "probe", "valu_rates.hip")]
 PROBE_LIB = os.path.join(PKG, "libflamia_probe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
@@ -57,9 +58,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
     tmp = PROBE_LIB + ".tmp"
-    r = subprocess.run([cc, *FLAGS, "-shared", PROBE_SRC, "-o", tmp], capture_output=True, text=True)
+    r = subprocess.run([cc, *FLAGS, "-shared", *PROBE_SRCS, "-o", tmp], capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed on {PROBE_SRCS}:\n{r.stderr}")
     os.replace(tmp, PROBE_LIB)
     return LIB
 

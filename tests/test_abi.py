@@ -178,3 +178,24 @@ def test_noalloc_forward_refuses_capacities_beyond_its_scratch():
     rc = L.flamia_fwd_noalloc(ctypes.byref(big), None, None, P(FAKE), P(FAKE), P(FAKE), mx, mx, mx,
                               P(FAKE), P(FAKE), None)
     assert rc == 1                                           # FLAMIA_ERR_NULL
+
+
+def test_probe_library_exports_and_refuses_bad_arguments():
+    """The issue-rate probes (matrix core and vector instructions) load from
+    their own library; invalid arguments come back as an error before any
+    launch."""
+    import os
+    path = os.path.join(os.path.dirname(F.LIB_PATH), "libflamia_probe.so")
+    P = ctypes.CDLL(path)
+    for n in ("flamia_probe_mfma_peak", "flamia_probe_valu_count", "flamia_probe_valu_name",
+              "flamia_probe_valu_rate"):
+        assert hasattr(P, n)
+    P.flamia_probe_valu_name.restype = ctypes.c_char_p
+    n = P.flamia_probe_valu_count()
+    assert n == 16
+    assert P.flamia_probe_valu_name(0) == b"v_fma_f32"
+    assert P.flamia_probe_valu_name(n) == b""
+    P.flamia_probe_valu_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert P.flamia_probe_valu_rate(n, 1, 1, ctypes.c_void_p(16), None) != 0
+    assert P.flamia_probe_valu_rate(0, 1, 1, None, None) != 0
+    assert P.flamia_probe_valu_rate(0, 0, 1, ctypes.c_void_p(16), None) != 0
