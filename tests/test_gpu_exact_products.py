@@ -21,6 +21,7 @@ import pytest
 from precision_causal_attention_amd import flamia as F
 from precision_causal_attention_amd import workloads as W
 
+import parity_rules as R
 from gpu_util import check_outputs, run_hip, say
 
 pytestmark = pytest.mark.gpu
@@ -121,3 +122,19 @@ def test_exact_products_exact_options(orc, case, attn):
     _codes_exact(orc, inst, g, exact=1)
     r = _oracle(orc, inst, scale, exact=1)
     check_outputs(g, r, "exact" if attn == "broad" else "exact-forward")
+
+
+@pytest.mark.parametrize("other", [{"tau": 3}, {"c_log2": 3}])
+def test_exact_products_tell_c_and_tau_apart(orc, other):
+    """The pages fix (c, tau) = (4, 4) (Appendix B.1).  The HIP path run with
+    a neighbouring choice matches the oracle run with that choice, and its O
+    fails the exact-product rule against the oracle at (4, 4): on hardware
+    outputs the rule tells the parameters apart, not only on the oracle's
+    own (the CPU power pins)."""
+    inst = CASES["gqa-d64"]()
+    say(f"[exact products, other parameters] gqa-d64 peaked {other}")
+    g = run_hip(inst, _opts(0.0, **other), doclen_cap=0)
+    check_outputs(g, _oracle(orc, inst, 0.0, **other), "exact-forward")
+    r44 = _oracle(orc, inst, 0.0)
+    with pytest.raises(AssertionError):
+        R.check_exact("O against (c, tau) = (4, 4)", g["o"], r44["o64"], say=say)
