@@ -17,8 +17,8 @@
 // The query-major list is document-major; the key-major one is document-major
 // when the caller asks for it (the attention library does at both head
 // dimensions), else cost-major.  A document-major list ends with every
-// document's cost-1 tile (query-major: the first, key-major: the last), which
-// fill in the tail as in the cost-major order.  Beyond
+// document's cheapest tiles (query-major: the first, key-major: the last
+// two), by decreasing cost, which fill in the tail as in the cost-major order.  Beyond
 // kPrefixLds documents both lists are cost-major.  Sorting is a counting sort on the small integer tile count
 // or cost instead of a comparison sort.  Within one class the order is
 // whatever the atomics give; it does not change any result.
@@ -47,10 +47,13 @@ namespace {
 // Tiles of cost <= kTail* go to the end of the document-major lists, where
 // they fill in the tail (16 x 1024-token documents: forward 73.6 -> 68.3 us,
 // dQ pass 110.8 -> 104.4 us with 1 for the query-major list; 2 was no
-// better there and 0.4% slower on the 4 x 8192 GQA call; the key-major list
-// with 1: dK/dV 2-3% faster).
+// better there and 0.4% slower on the 4 x 8192 GQA call).  The key-major
+// list moves the last two key tiles of every document (with 1, on the
+// 4 x 8192 GQA call, the first tiles of the shortest documents started last
+// and ended the launch, per-workgroup timestamps showed): dK/dV 407 -> 397
+// us against 1 (3 and 5: 399-402 us), no change on the d = 128 workloads.
 constexpr int kTailQ = 1;
-constexpr int kTailK = 1;
+constexpr int kTailK = 2;
 }  // namespace
 
 namespace flamia {

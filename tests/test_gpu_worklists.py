@@ -141,7 +141,7 @@ def test_lists_document_major(d):
     assert set(map(tuple, tk.tolist())) == want
     _check_tail_list(q_f, qcost, 1)
     _check_tail_list(tq.tolist(), qcost, 1)
-    _check_tail_list(tk.tolist(), kcost, 1)
+    _check_tail_list(tk.tolist(), kcost, 2)
 
 
 @pytest.mark.parametrize("ndocs", [4095, 4096, 4500])
@@ -159,7 +159,7 @@ def test_lists_at_the_lds_prefix_limit(ndocs):
     if ndocs < 4096:
         _check_tail_list(tq.tolist(), qcost, 1)
         _check_tail_list(q_f, qcost, 1)
-        _check_tail_list(tk.tolist(), kcost, 1)
+        _check_tail_list(tk.tolist(), kcost, 2)
     else:
         _check_cost_major(tq.tolist(), qcost)
         _check_cost_major(tk.tolist(), kcost)
