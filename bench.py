@@ -75,10 +75,11 @@ FWD_PHASES = ["quantize_qkv", "worklist_fwd", "fwd_kernel"]
 BWD_PHASES_STORE = ["quantize_do", "worklist_bwd", "dkv_kernel", "dq_kernel"]
 BWD_PHASES_FUSED = ["worklist_bwd", "dq_kernel", "dkv_kernel"]
 CSRC = os.path.join(ROOT, "precision_causal_attention_amd", "csrc")
-# sources whose text decides each attention kernel's memory traffic
+# sources whose text decides each attention kernel's memory traffic (the
+# work-list kernel's order decides which items run together and share L2)
 KERNEL_SOURCES = {"fwd_kernel": ["fwd.hip"], "dkv_kernel": ["bwd.hip", "bwd_split.hip"],
                   "dq_kernel": ["dq.hip", "dq_store.hip"]}
-COMMON_SOURCES = ["device.h", "kernels.h"]
+COMMON_SOURCES = ["device.h", "kernels.h", "plan.hip"]
 
 
 def log(*a):
