@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(256, (D == 64 && !MIX && !PROBE) ? 3 : 2) dq_k
     if (ti >= *a.ntiles) return;
     const int4 it = a.tiles[ti];
     const int q0 = it.x, ds = it.y, de = it.z;
-    const int h = xcd_head((int)blockIdx.x - ti * a.hq, a.hq);
+    const int h = xcd_head((int)blockIdx.x - ti * a.hq, a.hq, it.w);
     const int g = h / (a.hq / a.hkv);
     const int L = de - ds;
     const int lq0 = q0 - ds;

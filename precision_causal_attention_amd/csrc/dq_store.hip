@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 3 : 2) dq_store_kernel(const Dq
     if (ti >= a.ntiles[0]) return;
     const int4 it = a.tiles[ti];
     const int q0 = it.x, ds = it.y, de = it.z, doc = it.w;
-    const int h = xcd_head((int)blockIdx.x - ti * a.hq, a.hq);
+    const int h = xcd_head((int)blockIdx.x - ti * a.hq, a.hq, it.w);
     const int g = h / (a.hq / a.hkv);
     const int L = de - ds;
     const int lq0 = q0 - ds;
